@@ -1,0 +1,229 @@
+"""Benchmark of the MatMul-family hot path on one MI355X.
+
+One step = one call of each of the five workloads through the C ABI, in order,
+on one stream (all inputs resident in HBM before timing starts):
+  1. Gemm fp32   transA=transB=1, A[48,64] B[32,48] C[1,32], alpha .75 beta 1.5
+  2. MatMul bf16 A[8,1,512,1024] x B[1,16,1024,768]
+  3. Gemm bf16   8192^3, transB=1, C[8192]
+  4. QLinearMatMul int8 4096^3, per-row a / per-column b parameters
+  5. GroupedMatMul bf16, M=16384 K=4096 N=2048 G=64 S=8
+`value` is the step's algorithmic operations (2*M*N*K per product; int8
+multiply-adds counted like flops) divided by the step time.  Each workload is
+also timed on its own (median of HIP-event intervals around its call) and
+reported against the MI355X dense MFMA peak of its type under `per_config`.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--only NAME]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s (int8: TOPS) per config and % of MI355X dense MFMA peak, 1 GPU"
+UNIT = "TFLOP/s (int8: TOPS)"
+# MI355X datasheet dense peaks (TFLOP/s or TOPS) and HBM bandwidth (GB/s)
+PEAK = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "int8": 5033.2}
+HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_workloads(torch, synth, dev, only=None):
+    """Host draws -> device tensors.  Returns name -> dict(run=callable, ops, dtype, bytes, ...)."""
+    W = {}
+
+    def want(n):
+        return only is None or n in only
+
+    if want("gemm_f32_64x32x48"):
+        c = synth.gemm_f32_64x32x48()
+        d = dict(A=dev(c["A"]), B=dev(c["B"]), C=dev(c["C"]))
+        d["Y"] = torch.empty((64, 32), dtype=torch.float32, device="cuda")
+        W["gemm_f32_64x32x48"] = dict(host=c, dev=d, ops=2 * 64 * 32 * 48, dtype="f32",
+                                      bytes=(48 * 64 + 32 * 48 + 32 + 64 * 32) * 4)
+    if want("matmul_bf16_bcast"):
+        c = synth.matmul_bf16_bcast()
+        d = dict(A=dev(c["A"], "bf16"), B=dev(c["B"], "bf16"))
+        d["Y"] = torch.empty((8, 16, 512, 768), dtype=torch.bfloat16, device="cuda")
+        W["matmul_bf16_bcast"] = dict(host=c, dev=d, ops=2 * 128 * 512 * 768 * 1024, dtype="bf16",
+                                      bytes=(8 * 512 * 1024 + 16 * 1024 * 768 + 128 * 512 * 768) * 2)
+    if want("gemm_bf16_8192"):
+        c = synth.gemm_bf16_8192()
+        d = dict(A=dev(c["A"], "bf16"), B=dev(c["B"], "bf16"), C=dev(c["C"], "bf16"))
+        d["Y"] = torch.empty((8192, 8192), dtype=torch.bfloat16, device="cuda")
+        W["gemm_bf16_8192"] = dict(host=c, dev=d, ops=2 * 8192 ** 3, dtype="bf16",
+                                   bytes=(3 * 8192 * 8192 + 8192) * 2)
+    if want("qlinear_i8_4096"):
+        c = synth.qlinear_i8_4096()
+        d = {k: dev(c[k]) for k in ("a", "a_scale", "a_zero_point", "b", "b_scale", "b_zero_point", "y_scale",
+                                    "y_zero_point")}
+        d["y"] = torch.empty((4096, 4096), dtype=torch.int8, device="cuda")
+        W["qlinear_i8_4096"] = dict(host=c, dev=d, ops=2 * 4096 ** 3, dtype="int8",
+                                    bytes=3 * 4096 * 4096 + 4096 * 10)
+    if want("grouped_bf16_moe"):
+        c = synth.grouped_bf16_moe()
+        d = dict(input=dev(c["input"], "bf16"), weights=dev(c["weights"], "bf16"), idx=dev(c["group_indices"]),
+                 bias=dev(c["bias"], "bf16"))
+        d["out"] = torch.empty((16384, 8, 2048), dtype=torch.bfloat16, device="cuda")
+        W["grouped_bf16_moe"] = dict(host=c, dev=d, ops=2 * 16384 * 8 * 4096 * 2048, dtype="bf16",
+                                     bytes=(16384 * 4096 + 64 * 4096 * 2048 + 64 * 2048 + 16384 * 8 * 2048) * 2
+                                     + 16384 * 8 * 4)
+    return W
+
+
+def make_runner(om, name, w, torch):
+    d, c = w["dev"], w["host"]
+    if name == "gemm_f32_64x32x48":
+        return lambda: om.gemm(d["A"], d["B"], d["C"], c["alpha"], c["beta"], 1, 1, d["Y"])
+    if name == "matmul_bf16_bcast":
+        return lambda: om.matmul(d["A"], d["B"], d["Y"])
+    if name == "gemm_bf16_8192":
+        return lambda: om.gemm(d["A"], d["B"], d["C"], 1.0, 1.0, 0, 1, d["Y"])
+    if name == "qlinear_i8_4096":
+        return lambda: om.qlinear_matmul(d["a"], d["a_scale"], d["a_zero_point"], d["b"], d["b_scale"],
+                                         d["b_zero_point"], d["y_scale"], d["y_zero_point"], d["y"])
+    if name == "grouped_bf16_moe":
+        ws = torch.empty(om.grouped_matmul_workspace_size(16384, 8, 64), dtype=torch.uint8, device="cuda")
+        return lambda: om.grouped_matmul(d["input"], d["weights"], d["idx"], d["bias"], d["out"], ws)
+    raise KeyError(name)
+
+
+def time_each(torch, fn, reps):
+    """Median of HIP-event intervals around single calls, on torch's current stream (the call's stream)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for s, e in evs:
+        s.record()
+        fn()
+        e.record()
+    torch.cuda.synchronize()
+    ms = sorted(s.elapsed_time(e) for s, e in evs)
+    return ms[len(ms) // 2], ms
+
+
+def cpu_baseline(W, budget_s):
+    """The oracle as it stands, timed on a bounded sample of each workload's outputs."""
+    import oracle
+    nth = oracle.threads()
+    total_ops, total_t, parts = 0.0, 0.0, []
+    per = budget_s / max(1, len(W))
+    for name, w in W.items():
+        c = w["host"]
+        K = {"gemm_f32_64x32x48": 48, "matmul_bf16_bcast": 1024, "gemm_bf16_8192": 8192,
+             "qlinear_i8_4096": 4096, "grouped_bf16_moe": 4096}[name]
+        nout = w["ops"] // (2 * K)
+
+        def call(sel):
+            if name == "gemm_f32_64x32x48":
+                return oracle.gemm(c["A"], c["B"], c["C"], c["alpha"], c["beta"], 1, 1, sel=sel)
+            if name == "matmul_bf16_bcast":
+                return oracle.matmul(c["A"], c["B"], dt="bf16", sel=sel)
+            if name == "gemm_bf16_8192":
+                return oracle.gemm(c["A"], c["B"], c["C"], 1.0, 1.0, 0, 1, dt="bf16", sel=sel)
+            if name == "qlinear_i8_4096":
+                return oracle.qlinear_matmul(*(c[k] for k in ("a", "a_scale", "a_zero_point", "b", "b_scale",
+                                                              "b_zero_point", "y_scale", "y_zero_point")), sel=sel)
+            return oracle.grouped_matmul(c["input"], c["weights"], c["group_indices"], c["bias"], dt="bf16",
+                                         sel=sel)
+
+        rng = np.random.default_rng(0)
+        n = min(nout, 256)
+        while True:
+            sel = rng.integers(0, nout, n).astype(np.int64)
+            t0 = time.perf_counter()
+            call(sel)
+            dt = time.perf_counter() - t0
+            if dt >= per * 0.3 or n >= nout:
+                break
+            n = int(min(nout, max(n * 2, n * per * 0.5 / max(dt, 1e-4))))
+        total_ops += 2.0 * K * n
+        total_t += dt
+        parts.append("%s: %d outputs (%.2fs)" % (name, n, dt))
+    return dict(value=total_ops / total_t / 1e12, unit=UNIT, cores=nth, kind="oracle",
+                sample="random output elements of each workload, computed one by one: " + "; ".join(parts))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--reps", type=int, default=30, help="timed calls per workload for the per-config medians")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the baseline")
+    ap.add_argument("--only", default=None, help="comma-separated workload names")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from onnx_matmul_family_amd import _omm as om
+    from onnx_matmul_family_amd import synth
+    from tests.gpu_util import dev
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    om.lib()
+    only = set(args.only.split(",")) if args.only else None
+    t0 = time.time()
+    W = build_workloads(torch, synth, dev, only)
+    torch.cuda.synchronize()
+    log("inputs ready in %.1fs" % (time.time() - t0))
+    runs = {n: make_runner(om, n, w, torch) for n, w in W.items()}
+
+    def step():
+        for fn in runs.values():
+            fn()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / args.steps
+    total_ops = sum(w["ops"] for w in W.values())
+    log("step %.3f ms" % (step_s * 1e3))
+
+    per = []
+    for n, fn in runs.items():
+        med, _ = time_each(torch, fn, args.reps)
+        w = W[n]
+        rate = w["ops"] / (med * 1e-3) / 1e12
+        per.append(dict(workload=n, dtype=w["dtype"], ms=round(med, 4), tflops=round(rate, 2),
+                        frac_peak=round(rate / PEAK[w["dtype"]], 4),
+                        hbm_gbs=round(w["bytes"] / (med * 1e-3) / 1e9, 1)))
+        log("%-20s %9.4f ms  %8.1f T/s  %5.1f%% of %s peak" % (n, med, rate, 100 * rate / PEAK[w["dtype"]],
+                                                               w["dtype"]))
+
+    dom = max(per, key=lambda p: p["ms"])
+    wd = W[dom["workload"]]
+    ach = wd["ops"] / (dom["ms"] * 1e-3) / 1e12
+    roof = dict(bound="mfma", achieved=round(ach, 2), peak=PEAK[wd["dtype"]], unit="TFLOP/s",
+                frac=round(ach / PEAK[wd["dtype"]], 4), traffic=None, kernel=dom["workload"])
+
+    out = {
+        "metric": METRIC, "value": round(total_ops / step_s / 1e12, 2), "unit": UNIT, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16/int8/f32",
+        "data": "synthetic (seeded numpy draws with the specified shapes and distributions)",
+        "config": {"workload": "onnx_matmul_family five-workload step: " + ", ".join(W.keys()),
+                   "ops_per_step": total_ops},
+        "roofline": roof, "per_config": per,
+    }
+    if not args.no_cpu:
+        log("timing the CPU oracle baseline ...")
+        out["cpu_baseline"] = cpu_baseline(W, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

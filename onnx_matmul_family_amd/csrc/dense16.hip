@@ -1,0 +1,137 @@
+// bf16 / fp16 batched GEMM on gfx950 MFMA (v_mfma_f32_32x32x16_{bf16,f16}).
+//
+// Computes Y = alpha * A' B' + beta * C (Gemm, since version 13) and the
+// numpy.matmul product with broadcast batch dims (MatMul, since version 13):
+// fp32 accumulation, one round-to-nearest-even conversion to the output type.
+// The K loop is the shared MFMA core; this file adds the batch / tile mapping
+// and the alpha-beta-C epilogue, which stores 4 consecutive outputs per lane.
+#include "gemm16_core.hpp"
+#include "kernels.hpp"
+
+namespace omm {
+
+namespace {
+
+using namespace core16;
+
+template <int BM, int BN, int DT, bool AK, bool BKM, bool VEC>
+__global__ __launch_bounds__(NT) void dense16_kernel(DenseArgs p, int tiles_m, int tiles_n) {
+    constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+    constexpr int STAGE = (BM + BN) * KSTEP * 2;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    const int T = tiles_m * tiles_n;
+    const int w = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+    const int z = w / T;
+    int tm, tn;
+    grouped_order(w - z * T, tiles_m, tiles_n, 4, tm, tn);
+    const int64_t z0 = z / p.nb1, z1 = z - z0 * p.nb1;
+    const uint16_t* __restrict__ A = (const uint16_t*)p.A + z0 * p.a_bs0 + z1 * p.a_bs1;
+    const uint16_t* __restrict__ B = (const uint16_t*)p.B + z0 * p.b_bs0 + z1 * p.b_bs1;
+    uint16_t* __restrict__ Y = (uint16_t*)p.Y + z0 * p.y_bs0 + z1 * p.y_bs1;
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    const int64_t M = p.M, N = p.N, K = p.K;
+
+    f32x16_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int nk = (int)((K + KSTEP - 1) / KSTEP);
+    TileSrc<BM, AK> srcA;
+    TileSrc<BN, BKM> srcB;
+    srcA.init(A, p.lda, m0, M, K, t);
+    srcB.init(B, p.ldb, n0, N, K, t);
+    if (!VEC)
+        mainloop<BM, BN, DT, AK, BKM, 2>(acc, smem, srcA, srcB, nk, t, lane, wm, wn);
+    else if ((m0 + BM <= M) && (n0 + BN <= N) && (K % KSTEP == 0))
+        mainloop<BM, BN, DT, AK, BKM, 0>(acc, smem, srcA, srcB, nk, t, lane, wm, wn);
+    else
+        mainloop<BM, BN, DT, AK, BKM, 1>(acc, smem, srcA, srcB, nk, t, lane, wm, wn);
+
+    // epilogue: lane holds, for each (i, j, q), row m and the 4 columns n..n+3
+    const float alpha = p.alpha, beta = p.beta;
+    const uint16_t* __restrict__ Cp = (const uint16_t*)p.C;
+    const bool vec_store = VEC && (N % 4 == 0) && (p.ldy % 4 == 0);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int64_t m = m0 + wm * WM + 32 * i + (lane & 31);
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t n = n0 + wn * WN + 32 * j + 8 * q + 4 * (lane >> 5);
+                if (n >= N) continue;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float x = alpha * acc[i][j][4 * q + e];
+                    if (Cp && n + e < N) x += beta * from_bits<DT>(Cp[m * p.c_sm + (n + e) * p.c_sn]);
+                    v[e] = x;
+                }
+                uint16_t* yr = Y + m * p.ldy + n;
+                if (vec_store) {
+                    u32x2_t o;
+                    o.x = (uint32_t)to_bits<DT>(v[0]) | ((uint32_t)to_bits<DT>(v[1]) << 16);
+                    o.y = (uint32_t)to_bits<DT>(v[2]) | ((uint32_t)to_bits<DT>(v[3]) << 16);
+                    *(u32x2_t*)yr = o;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) yr[e] = to_bits<DT>(v[e]);
+                }
+            }
+        }
+    }
+}
+
+template <int BM, int BN, int DT, bool AK, bool BKM, bool VEC>
+hipError_t launch_cfg(const DenseArgs& a, hipStream_t s) {
+    const int64_t tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
+    const int64_t total = tiles_m * tiles_n * a.nb0 * a.nb1;
+    if (total <= 0) return hipSuccess;
+    if (total > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((dense16_kernel<BM, BN, DT, AK, BKM, VEC>), dim3((unsigned)total), dim3(NT), 0, s, a,
+                       (int)tiles_m, (int)tiles_n);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int DT, bool VEC>
+hipError_t launch_layout(const DenseArgs& a, hipStream_t s) {
+    if (a.a_kmajor && a.b_kmajor) return launch_cfg<BM, BN, DT, true, true, VEC>(a, s);
+    if (a.a_kmajor && !a.b_kmajor) return launch_cfg<BM, BN, DT, true, false, VEC>(a, s);
+    if (!a.a_kmajor && a.b_kmajor) return launch_cfg<BM, BN, DT, false, true, VEC>(a, s);
+    return launch_cfg<BM, BN, DT, false, false, VEC>(a, s);
+}
+
+template <int DT>
+hipError_t launch_dt(const DenseArgs& a, hipStream_t s) {
+    // 16-byte loads need 16-byte aligned bases, row strides that are multiples
+    // of 8 elements and a contiguous extent (K, M or N) that is a multiple of 8.
+    auto al16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
+    const bool a_ok = al16(a.A) && a.lda % 8 == 0 && (a.a_kmajor ? a.K % 8 == 0 : a.M % 8 == 0) &&
+                      a.a_bs0 % 8 == 0 && a.a_bs1 % 8 == 0;
+    const bool b_ok = al16(a.B) && a.ldb % 8 == 0 && (a.b_kmajor ? a.K % 8 == 0 : a.N % 8 == 0) &&
+                      a.b_bs0 % 8 == 0 && a.b_bs1 % 8 == 0;
+    const bool y_ok = ((uintptr_t)a.Y & 7) == 0 && a.y_bs0 % 4 == 0 && a.y_bs1 % 4 == 0;
+    const bool vec = a_ok && b_ok && y_ok;
+    const int64_t big_tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256) * a.nb0 * a.nb1;
+    if (vec && big_tiles >= 256) return launch_layout<256, 256, DT, true>(a, s);
+    if (vec) return launch_layout<128, 128, DT, true>(a, s);
+    return launch_layout<128, 128, DT, false>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_dense16(const DenseArgs& a, int dt, hipStream_t s) {
+    return dt == 0 ? launch_dt<0>(a, s) : launch_dt<1>(a, s);
+}
+
+}  // namespace omm

@@ -1,0 +1,283 @@
+// GroupedMatMul (version 29) on gfx950.
+//
+//   output[m, i, :] = input[m, :] @ weights[g] (+ bias[g, :]),  g = group_indices[m, i]
+//
+// The page defines the result through Gather + Expand + MatMul and asks
+// runtimes for a fused grouped product that never forms the gathered
+// (M*S, K, N) weights.  Here the (m, i) pairs are counting-sorted by group on
+// the device and every group's pairs run as the rows of one GEMM against
+// weights[g]:
+//   1. route_kernel (one workgroup): histogram of the M*S indices over the G
+//      groups (invalid indices are counted, not routed), exclusive scans of
+//      the counts and of the per-group tile counts, the tile table
+//      (group, first sorted pair, rows) and the scatter of pair ids
+//      p = m*S + i into group order;
+//   2. grouped16_kernel: one 256x256 output tile per workgroup, rows gathered
+//      from input[p / S], B = weights[g] (n contiguous, read through the
+//      transposing LDS path), epilogue adds bias[g] in fp32, rounds once and
+//      writes each row to output[p].  The grid is the upper bound
+//      (M*S/BM + G) x (N/BN); workgroups past the routed tile count exit.
+// No host synchronisation between the two.  Each output row depends only on
+// its own pair, so the order of pairs inside a group never changes a value.
+#include "gemm16_core.hpp"
+#include "kernels.hpp"
+
+namespace omm {
+
+namespace {
+
+constexpr int ROUTE_THREADS = 1024;
+constexpr int GBM = 256, GBN = 256;  // grouped tile
+constexpr int MAX_G = 8192;          // groups handled by the single-workgroup router
+
+// workspace layout (bytes, from a 256-byte aligned base)
+//   [0, 64)           header: int32 num_tiles, int32 invalid_count
+//   [64, 64+16*TT)    tile table: int4 (group, first sorted pair, rows, 0), TT = P/BM_MIN + G + 1
+//   [.., + 4*P)       sorted pair ids
+constexpr int BM_MIN = 128;
+__host__ __device__ inline int64_t tiles_cap(int64_t P, int64_t G) { return P / BM_MIN + G + 1; }
+__host__ __device__ inline int64_t off_tiles() { return 64; }
+__host__ __device__ inline int64_t off_sorted(int64_t P, int64_t G) {
+    return (off_tiles() + 16 * tiles_cap(P, G) + 255) / 256 * 256;
+}
+
+__device__ __forceinline__ int64_t load_idx(const void* idx, int64_t p, int idx64) {
+    return idx64 ? ((const int64_t*)idx)[p] : (int64_t)((const int32_t*)idx)[p];
+}
+
+// exclusive scan of v[0..n) in LDS by one workgroup; returns the total
+__device__ int block_exclusive_scan(int* v, int n, int* part) {
+    const int t = threadIdx.x, nt = blockDim.x;
+    const int per = (n + nt - 1) / nt;
+    const int lo = min(n, t * per), hi = min(n, lo + per);
+    int s = 0;
+    for (int i = lo; i < hi; ++i) s += v[i];
+    part[t] = s;
+    __syncthreads();
+    for (int d = 1; d < nt; d <<= 1) {
+        const int x = t >= d ? part[t - d] : 0;
+        __syncthreads();
+        part[t] += x;
+        __syncthreads();
+    }
+    int run = part[t] - s;  // exclusive prefix of this thread's range
+    for (int i = lo; i < hi; ++i) {
+        const int c = v[i];
+        v[i] = run;
+        run += c;
+    }
+    const int total = part[nt - 1];
+    __syncthreads();
+    return total;
+}
+
+__global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(const void* idx, int idx64, int64_t P, int G, int BM,
+                                                              char* ws) {
+    __shared__ int cnt[MAX_G];    // pairs per group
+    __shared__ int tile0[MAX_G];  // first tile of each group
+    __shared__ int row0[MAX_G];   // first sorted position of each group, then the scatter cursor
+    __shared__ int part[ROUTE_THREADS];
+    __shared__ int bad;
+    const int t = threadIdx.x;
+    for (int g = t; g < G; g += ROUTE_THREADS) cnt[g] = 0;
+    if (t == 0) bad = 0;
+    __syncthreads();
+    for (int64_t p = t; p < P; p += ROUTE_THREADS) {
+        const int64_t g = load_idx(idx, p, idx64);
+        if (g >= 0 && g < G) atomicAdd(&cnt[g], 1);
+        else atomicAdd(&bad, 1);
+    }
+    __syncthreads();
+    for (int g = t; g < G; g += ROUTE_THREADS) {
+        tile0[g] = (cnt[g] + BM - 1) / BM;
+        row0[g] = cnt[g];
+    }
+    __syncthreads();
+    const int ntiles = block_exclusive_scan(tile0, G, part);
+    block_exclusive_scan(row0, G, part);
+    int4* tiles = (int4*)(ws + off_tiles());
+    for (int g = t; g < G; g += ROUTE_THREADS) {
+        const int c = cnt[g], nt = (c + BM - 1) / BM;
+        for (int tt = 0; tt < nt; ++tt) tiles[tile0[g] + tt] = make_int4(g, row0[g] + tt * BM, min(BM, c - tt * BM), 0);
+    }
+    __syncthreads();
+    int* sorted = (int*)(ws + off_sorted(P, G));
+    for (int64_t p = t; p < P; p += ROUTE_THREADS) {
+        const int64_t g = load_idx(idx, p, idx64);
+        if (g >= 0 && g < G) sorted[atomicAdd(&row0[g], 1)] = (int)p;
+    }
+    if (t == 0) {
+        ((int*)ws)[0] = ntiles;
+        ((int*)ws)[1] = bad;
+    }
+}
+
+template <int DT, int MODE>
+__device__ __forceinline__ void grouped_body(const GroupedArgs& a, const char* ws, int tile, int tn, char* smem) {
+    const int4 te = ((const int4*)(ws + off_tiles()))[tile];
+    const int g = te.x, start = te.y, rows = te.z;
+    const int* sorted = (const int*)(ws + off_sorted(a.M * a.S, a.G));
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t K = a.K, N = a.N, S = a.S;
+    const int64_t n0 = (int64_t)tn * GBN;
+
+    using namespace core16;
+    GatherSrc<GBM> srcA;
+    srcA.base = (const uint16_t*)a.input;
+    srcA.K = K;
+    int r0, lk;
+    Chunks<GBM, true>::coords(t, 0, r0, lk);
+    srcA.lk = lk;
+    srcA.valid = 0;
+#pragma unroll
+    for (int i = 0; i < GatherSrc<GBM>::NC; ++i) {
+        const int r = r0 + 32 * i;
+        int64_t off = 0;
+        if (r < rows) {
+            srcA.valid |= 1u << i;
+            off = (int64_t)(sorted[start + r] / S) * K;
+        }
+        srcA.roff[i] = off + srcA.lk;
+    }
+    TileSrc<GBN, false> srcB;
+    srcB.init((const uint16_t*)a.weights + (int64_t)g * K * N, N, n0, N, K, t);
+
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    const int nk = (int)((K + KSTEP - 1) / KSTEP);
+    mainloop<GBM, GBN, DT, true, false, MODE>(acc, smem, srcA, srcB, nk, t, lane, wm, wn);
+
+    const uint16_t* bias = a.bias ? (const uint16_t*)a.bias + (int64_t)g * N : nullptr;
+    uint16_t* out = (uint16_t*)a.output;
+    const bool vec_store = (MODE != 2) && (N % 4 == 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = wm * 128 + 32 * i + (lane & 31);
+        if (r >= rows) continue;
+        uint16_t* orow = out + (int64_t)sorted[start + r] * N;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t n = n0 + wn * 128 + 32 * j + 8 * q + 4 * (lane >> 5);
+                if (n >= N) continue;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float x = acc[i][j][4 * q + e];
+                    if (bias && n + e < N) x += from_bits<DT>(bias[n + e]);
+                    v[e] = x;
+                }
+                if (vec_store) {
+                    u32x2_t o;
+                    o.x = (uint32_t)to_bits<DT>(v[0]) | ((uint32_t)to_bits<DT>(v[1]) << 16);
+                    o.y = (uint32_t)to_bits<DT>(v[2]) | ((uint32_t)to_bits<DT>(v[3]) << 16);
+                    *(u32x2_t*)(orow + n) = o;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) orow[n + e] = to_bits<DT>(v[e]);
+                }
+            }
+        }
+    }
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(256) void grouped16_kernel(GroupedArgs a, const char* ws, int max_mtiles, int tiles_n) {
+    __shared__ __attribute__((aligned(1024))) char smem[2 * (GBM + GBN) * core16::KSTEP * 2];
+    const int total = max_mtiles * tiles_n;
+    const int w = xcd_remap((int)blockIdx.x, total);
+    int tm, tn;
+    grouped_order(w, max_mtiles, tiles_n, 4, tm, tn);
+    const int ntiles = ((const int*)ws)[0];
+    if (tm >= ntiles) return;
+    const int rows = ((const int4*)(ws + off_tiles()))[tm].z;
+    if (!VEC)
+        grouped_body<DT, 2>(a, ws, tm, tn, smem);
+    else if (rows == GBM && (int64_t)(tn + 1) * GBN <= a.N && a.K % core16::KSTEP == 0)
+        grouped_body<DT, 0>(a, ws, tm, tn, smem);
+    else
+        grouped_body<DT, 1>(a, ws, tm, tn, smem);
+}
+
+// fp32: one workgroup per (pair, 256 columns); plain fp32 dot products.
+__global__ __launch_bounds__(256) void grouped_f32_kernel(GroupedArgs a) {
+    __shared__ float row[1024];
+    const int64_t p = blockIdx.x;
+    const int64_t n = (int64_t)blockIdx.y * 256 + threadIdx.x;
+    const int64_t g = load_idx(a.idx, p, a.idx64);
+    if (g < 0 || g >= a.G) return;
+    const float* in = (const float*)a.input + (p / a.S) * a.K;
+    const float* wg = (const float*)a.weights + g * a.K * a.N;
+    float acc = 0.0f;
+    for (int64_t k0 = 0; k0 < a.K; k0 += 1024) {
+        __syncthreads();
+        for (int k = threadIdx.x; k < 1024; k += 256) row[k] = (k0 + k < a.K) ? in[k0 + k] : 0.0f;
+        __syncthreads();
+        if (n < a.N) {
+            const int64_t kend = min((int64_t)1024, a.K - k0);
+            for (int64_t k = 0; k < kend; ++k) acc += row[k] * wg[(k0 + k) * a.N + n];
+        }
+    }
+    if (n < a.N) {
+        if (a.bias) acc += ((const float*)a.bias)[g * a.N + n];
+        ((float*)a.output)[p * a.N + n] = acc;
+    }
+}
+
+}  // namespace
+
+size_t grouped_workspace_bytes(int64_t M, int64_t S, int64_t G) {
+    const int64_t P = M * S;
+    return (size_t)(off_sorted(P, G) + 4 * P + 255) / 256 * 256;
+}
+
+hipError_t launch_grouped(const GroupedArgs& a, int dt, void* ws, hipStream_t s) {
+    const int64_t P = a.M * a.S;
+    if (a.G > MAX_G || P > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(route_kernel, dim3(1), dim3(ROUTE_THREADS), 0, s, a.idx, a.idx64, P, (int)a.G, GBM, (char*)ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (P == 0 || a.N == 0) return hipSuccess;
+    if (dt == 2) {
+        const int64_t nb = (a.N + 255) / 256;
+        if (nb > 65535) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(grouped_f32_kernel, dim3((unsigned)P, (unsigned)nb), dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
+    const int64_t max_mtiles = P / GBM + a.G;
+    const int64_t tiles_n = (a.N + GBN - 1) / GBN;
+    if (max_mtiles * tiles_n > 0x7fffffff) return hipErrorInvalidValue;
+    auto al16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
+    const bool vec = al16(a.input) && al16(a.weights) && ((uintptr_t)a.output & 7) == 0 && a.K % 8 == 0 &&
+                     a.N % 8 == 0;
+    dim3 grid((unsigned)(max_mtiles * tiles_n));
+    const char* wsc = (const char*)ws;
+    if (dt == 0) {
+        if (vec) hipLaunchKernelGGL((grouped16_kernel<0, true>), grid, dim3(256), 0, s, a, wsc, (int)max_mtiles, (int)tiles_n);
+        else hipLaunchKernelGGL((grouped16_kernel<0, false>), grid, dim3(256), 0, s, a, wsc, (int)max_mtiles, (int)tiles_n);
+    } else {
+        if (vec) hipLaunchKernelGGL((grouped16_kernel<1, true>), grid, dim3(256), 0, s, a, wsc, (int)max_mtiles, (int)tiles_n);
+        else hipLaunchKernelGGL((grouped16_kernel<1, false>), grid, dim3(256), 0, s, a, wsc, (int)max_mtiles, (int)tiles_n);
+    }
+    return hipGetLastError();
+}
+
+hipError_t grouped_invalid_count(const void* ws, hipStream_t s, int64_t* count) {
+    int hdr[2] = {0, 0};
+    hipError_t e = hipMemcpyAsync(hdr, ws, sizeof hdr, hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return e;
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return e;
+    *count = hdr[1];
+    return hipSuccess;
+}
+
+}  // namespace omm

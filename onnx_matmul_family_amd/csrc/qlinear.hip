@@ -1,0 +1,331 @@
+// QLinearMatMul (version 10) on gfx950: int8 MFMA (v_mfma_i32_32x32x32_i8)
+// with an exact int32 accumulator and the fused requantisation.
+//
+// Per output element the operator asks for
+//   acc = sum_k (a - za)(b - zb)                      (int32, wraps mod 2^32)
+//   y   = saturate(rint(fp32(acc) * fp32(fp32(sa * sb) / sy)) + zy)
+// a - za does not fit in int8, so the product runs on the raw bytes and the
+// zero points enter through the expansion (exact mod 2^32)
+//   acc = sum ab - zb * sum_k a[m,k] - za * sum_k b[k,n] + K * za * zb.
+// The row sums of a and column sums of b come from the MFMA operand fragments
+// already in registers (v_dot4_i32_i8 against 0x01010101), so no extra pass
+// over memory.  uint8 operands are mapped to int8 by flipping the top bit
+// (a - 128) and their zero points shifted by 128, which leaves every a - za
+// unchanged.  The requantisation uses IEEE fp32 multiply, correctly rounded
+// division and round-half-even, in the order above, with no contraction.
+//
+// Tiles: 256x256 outputs per workgroup of 4 waves (128x128 each), K in stages
+// of 128 bytes, double-buffered LDS.  a (k contiguous) is stored as swizzled
+// 128-byte rows and read with ds_read_b128; b (n contiguous) is copied as is
+// (swizzled 16-byte chunks) and read with the transposing ds_read_b64_tr_b8.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace omm {
+
+namespace {
+
+constexpr int NT = 256;
+constexpr int BMQ = 256, BNQ = 256;
+constexpr int KB = 128;                 // k (bytes) per stage
+constexpr int A_BYTES = BMQ * KB;       // 32 KiB
+constexpr int B_BYTES = BNQ * KB;       // 32 KiB
+constexpr int STAGE = A_BYTES + B_BYTES;
+constexpr int NC = 8;                   // 16-byte chunks per thread per operand per stage
+
+// a: chunk i of thread t = row 8 (t >> 6) + (t & 7) + 32 i, k bytes 16 ((t >> 3) & 7) .. +15
+// b: chunk i of thread t = k row (t >> 4) + 16 i, n bytes (t & 15) * 16 .. +15
+template <bool KMAJ, bool U8>
+struct QSrc {
+    const uint8_t* p0;
+    int64_t si, step;
+    int64_t mn_first, k_first, MN, K;
+
+    __device__ void init(const uint8_t* base, int64_t ld, int64_t mn0, int64_t MN_, int64_t K_, int t) {
+        MN = MN_;
+        K = K_;
+        if constexpr (KMAJ) {
+            mn_first = mn0 + ((t >> 6) << 3) + (t & 7);
+            k_first = ((t >> 3) & 7) * 16;
+            p0 = base + mn_first * ld + k_first;
+            si = 32 * ld;
+            step = KB;
+        } else {
+            k_first = t >> 4;
+            mn_first = mn0 + (t & 15) * 16;
+            p0 = base + k_first * ld + mn_first;
+            si = 16 * ld;
+            step = (int64_t)KB * ld;
+        }
+    }
+
+    template <int MODE>
+    __device__ __forceinline__ void load(u32x4_t (&reg)[NC], int kt) const {
+        const uint8_t* p = p0 + (int64_t)kt * step;
+        const int64_t k0 = k_first + (int64_t)kt * KB;
+        const uint32_t flip = U8 ? 0x80808080u : 0u;
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            const uint8_t* q = p + i * si;
+            const int64_t mn = KMAJ ? mn_first + 32 * i : mn_first;
+            const int64_t k = KMAJ ? k0 : k0 + 16 * i;
+            if constexpr (MODE == 0) {
+                reg[i] = *(const u32x4_t*)q ^ flip;
+            } else if constexpr (MODE == 1) {
+                u32x4_t v = {0u, 0u, 0u, 0u};
+                if (mn < MN && k < K) v = *(const u32x4_t*)q ^ flip;
+                reg[i] = v;
+            } else {
+                uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const bool ok = KMAJ ? (mn < MN && k + e < K) : (k < K && mn + e < MN);
+                    if (ok) w[e >> 2] |= (uint32_t)(q[e] ^ (U8 ? 0x80 : 0)) << (8 * (e & 3));
+                }
+                reg[i] = u32x4_t{w[0], w[1], w[2], w[3]};
+            }
+        }
+    }
+};
+
+__device__ __forceinline__ void stash(char* s, const u32x4_t (&ra)[NC], const u32x4_t (&rb)[NC], int t) {
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+        *(u32x4_t*)(s + kmaj_off<BMQ>(((t >> 6) << 3) + (t & 7) + 32 * i, (t >> 3) & 7)) = ra[i];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) *(u32x4_t*)(s + A_BYTES + mmaj8_off<BNQ>((t >> 4) + 16 * i, (t & 15) * 16)) = rb[i];
+}
+
+__device__ __forceinline__ i32x4_t frag_a(const char* s, int rowb, int ks, int lane) {
+    return *(const i32x4_t*)(s + ks * (BMQ * 32) + rowb * 32 + kmaj_lane(lane));
+}
+// lane l gets column colb + l%32, k = 32 ks + 16 (l/32) + 0..15
+__device__ __forceinline__ i32x4_t frag_b(const char* s, int colb, int ks, int lane) {
+    const int g = lane >> 4, i = lane & 15;
+    const int krow = 32 * ks + 16 * (g >> 1) + (i >> 1);
+    const int ncol = colb + 16 * (g & 1) + 8 * (i & 1);
+    const int off = A_BYTES + mmaj8_off<BNQ>(krow, ncol);
+    i32x2_t lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32(OMM_LDS(i32x2_t, s + off));
+    i32x2_t hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32(OMM_LDS(i32x2_t, s + off + 8 * BNQ));
+    return i32x4_t{lo.x, lo.y, hi.x, hi.y};
+}
+
+__device__ __forceinline__ int dot4sum(i32x4_t v, int acc) {
+    acc = __builtin_amdgcn_sdot4(v.x, 0x01010101, acc, false);
+    acc = __builtin_amdgcn_sdot4(v.y, 0x01010101, acc, false);
+    acc = __builtin_amdgcn_sdot4(v.z, 0x01010101, acc, false);
+    acc = __builtin_amdgcn_sdot4(v.w, 0x01010101, acc, false);
+    return acc;
+}
+
+template <bool AU8, bool BU8, int MODE>
+__device__ __forceinline__ void qloop(i32x16_t (&acc)[4][4], int (&rs)[4], int (&cs)[4], char* smem,
+                                      const QSrc<true, AU8>& sa, const QSrc<false, BU8>& sb, int nk, int t, int lane,
+                                      int wm, int wn) {
+    u32x4_t ra[NC], rb[NC];
+    if (nk > 0) {
+        sa.template load<MODE>(ra, 0);
+        sb.template load<MODE>(rb, 0);
+        stash(smem, ra, rb, t);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) {
+            sa.template load<MODE>(ra, kt + 1);
+            sb.template load<MODE>(rb, kt + 1);
+        }
+        const char* s = smem + buf * STAGE;
+#pragma unroll
+        for (int ks = 0; ks < KB / 32; ++ks) {
+            i32x4_t af[4], bf[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) af[i] = frag_a(s, wm * 128 + 32 * i, ks, lane);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bf[j] = frag_b(s, wn * 128 + 32 * j, ks, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[j], af[i], acc[i][j], 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rs[i] = dot4sum(af[i], rs[i]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) cs[j] = dot4sum(bf[j], cs[j]);
+        }
+        if (kt + 1 < nk) stash(smem + (buf ^ 1) * STAGE, ra, rb, t);
+        __syncthreads();
+    }
+}
+
+__device__ __forceinline__ int ldzp(const void* p, int64_t i, bool u8) {
+    return u8 ? (int)((const uint8_t*)p)[i] - 128 : (int)((const int8_t*)p)[i];
+}
+
+template <bool AU8, bool BU8, bool VEC>
+__global__ __launch_bounds__(NT) void qlinear_kernel(QArgs p, int tiles_m, int tiles_n) {
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int T = tiles_m * tiles_n;
+    const int w = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+    const int z = w / T;
+    int tm, tn;
+    grouped_order(w - z * T, tiles_m, tiles_n, 4, tm, tn);
+    const int64_t z0 = z / p.nb1, z1 = z - z0 * p.nb1;
+    const uint8_t* a = (const uint8_t*)p.a + z0 * p.a_bs0 + z1 * p.a_bs1;
+    const uint8_t* b = (const uint8_t*)p.b + z0 * p.b_bs0 + z1 * p.b_bs1;
+    uint8_t* y = (uint8_t*)p.y + z0 * p.y_bs0 + z1 * p.y_bs1;
+    const int64_t m0 = (int64_t)tm * BMQ, n0 = (int64_t)tn * BNQ;
+    const int64_t M = p.M, N = p.N, K = p.K;
+
+    i32x16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+    int rs[4] = {0, 0, 0, 0}, cs[4] = {0, 0, 0, 0};
+
+    QSrc<true, AU8> sa;
+    QSrc<false, BU8> sb;
+    sa.init(a, p.lda, m0, M, K, t);
+    sb.init(b, p.ldb, n0, N, K, t);
+    const int nk = (int)((K + KB - 1) / KB);
+    if (!VEC)
+        qloop<AU8, BU8, 2>(acc, rs, cs, smem, sa, sb, nk, t, lane, wm, wn);
+    else if (m0 + BMQ <= M && n0 + BNQ <= N && K % KB == 0)
+        qloop<AU8, BU8, 0>(acc, rs, cs, smem, sa, sb, nk, t, lane, wm, wn);
+    else
+        qloop<AU8, BU8, 1>(acc, rs, cs, smem, sa, sb, nk, t, lane, wm, wn);
+
+    // full row / column sums: lanes l and l^32 hold the two k-halves
+    int* rowsum = (int*)smem;        // 256 tile rows
+    int* colsum = (int*)smem + 256;  // 256 tile columns
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = rs[i] + __shfl_xor(rs[i], 32);
+        if (wn == 0 && lane < 32) rowsum[wm * 128 + 32 * i + lane] = r;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int c = cs[j] + __shfl_xor(cs[j], 32);
+        if (wm == 0 && lane < 32) colsum[wn * 128 + 32 * j + lane] = c;
+    }
+    __syncthreads();
+
+    // Per-row terms U = rowsum - K*za, za, sa and per-column terms colsum, zb, sb,
+    // one row and one column per thread, so that
+    //   acc = sum ab - zb * U - za * colsum   (mod 2^32)
+    uint32_t* U = (uint32_t*)smem + 512;
+    int* ZA = (int*)smem + 768;
+    float* SA = (float*)smem + 1024;
+    uint32_t* CB = (uint32_t*)smem + 1280;
+    int* ZB = (int*)smem + 1536;
+    float* SB = (float*)smem + 1792;
+    const uint32_t Ku = (uint32_t)K;
+    {
+        const int64_t m = m0 + t, n = n0 + t;
+        int za = 0, zb = 0;
+        float sa = 0.0f, sb = 0.0f;
+        if (m < M) {
+            const int64_t apo = z0 * p.ap_bs0 + z1 * p.ap_bs1 + m * p.ap_sm;
+            za = ldzp(p.a_zp, apo, AU8);
+            sa = p.a_scale[apo];
+        }
+        if (n < N) {
+            const int64_t bpo = z0 * p.bp_bs0 + z1 * p.bp_bs1 + n * p.bp_sn;
+            zb = ldzp(p.b_zp, bpo, BU8);
+            sb = p.b_scale[bpo];
+        }
+        U[t] = (uint32_t)rowsum[t] - Ku * (uint32_t)za;
+        ZA[t] = za;
+        SA[t] = sa;
+        CB[t] = (uint32_t)colsum[t];
+        ZB[t] = zb;
+        SB[t] = sb;
+    }
+    __syncthreads();
+
+    const float sy = p.y_scale[0];
+    const int zy = p.y_u8 ? (int)((const uint8_t*)p.y_zp)[0] : (int)((const int8_t*)p.y_zp)[0];
+    const int lo = p.y_u8 ? 0 : -128, hi = p.y_u8 ? 255 : 127;
+    const bool vec_store = VEC && (N % 4 == 0) && (p.ldy % 4 == 0);
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int mloc = wm * 128 + 32 * i + (lane & 31);
+        const int64_t m = m0 + mloc;
+        if (m >= M) continue;
+        const uint32_t Um = U[mloc];
+        const uint32_t za = (uint32_t)ZA[mloc];
+        const float sa_m = SA[mloc];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int nloc = wn * 128 + 32 * j + 8 * q + 4 * (lane >> 5);
+                const int64_t n = n0 + nloc;
+                if (n >= N) continue;
+                const u32x4_t cb = *(const u32x4_t*)(CB + nloc);
+                const i32x4_t zb = *(const i32x4_t*)(ZB + nloc);
+                const f32x4_t sb = *(const f32x4_t*)(SB + nloc);
+                uint32_t packed = 0;
+                int outv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t s32 = (uint32_t)acc[i][j][4 * q + e] - (uint32_t)zb[e] * Um - za * cb[e];
+                    const float prod = sa_m * sb[e];
+                    const float mult = prod / sy;
+                    const float x = (float)(int32_t)s32 * mult;
+                    float r = __builtin_rintf(x);
+                    r = fminf(fmaxf(r, -1.0e9f), 1.0e9f);
+                    int qv = (int)r + zy;
+                    qv = qv < lo ? lo : (qv > hi ? hi : qv);
+                    outv[e] = qv;
+                    packed |= ((uint32_t)qv & 0xffu) << (8 * e);
+                }
+                uint8_t* yr = y + m * p.ldy + n;
+                if (vec_store) {
+                    *(uint32_t*)yr = packed;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) yr[e] = (uint8_t)outv[e];
+                }
+            }
+        }
+    }
+}
+
+template <bool AU8, bool BU8, bool VEC>
+hipError_t launch_q(const QArgs& a, hipStream_t s) {
+    const int64_t tiles_m = (a.M + BMQ - 1) / BMQ, tiles_n = (a.N + BNQ - 1) / BNQ;
+    const int64_t total = tiles_m * tiles_n * a.nb0 * a.nb1;
+    if (total <= 0) return hipSuccess;
+    if (total > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((qlinear_kernel<AU8, BU8, VEC>), dim3((unsigned)total), dim3(NT), 0, s, a, (int)tiles_m,
+                       (int)tiles_n);
+    return hipGetLastError();
+}
+
+template <bool VEC>
+hipError_t launch_q_types(const QArgs& a, hipStream_t s) {
+    if (a.a_u8 && a.b_u8) return launch_q<true, true, VEC>(a, s);
+    if (a.a_u8) return launch_q<true, false, VEC>(a, s);
+    if (a.b_u8) return launch_q<false, true, VEC>(a, s);
+    return launch_q<false, false, VEC>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_qlinear(const QArgs& a, hipStream_t s) {
+    auto al16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
+    const bool vec = al16(a.a) && al16(a.b) && ((uintptr_t)a.y & 3) == 0 && a.lda % 16 == 0 && a.ldb % 16 == 0 &&
+                     a.K % 16 == 0 && a.N % 16 == 0 && a.a_bs0 % 16 == 0 && a.a_bs1 % 16 == 0 &&
+                     a.b_bs0 % 16 == 0 && a.b_bs1 % 16 == 0 && a.y_bs0 % 4 == 0 && a.y_bs1 % 4 == 0;
+    return vec ? launch_q_types<true>(a, s) : launch_q_types<false>(a, s);
+}
+
+}  // namespace omm

@@ -1,0 +1,59 @@
+"""Helpers for the GPU parity tests: host <-> device copies and the tolerance check.
+
+Tolerances (fixed for this operator family):
+  fp32 outputs:       |y_gpu - y| <= 1e-5 * t + 1e-6
+  bf16 / fp16 outputs: |y_gpu - y| <= 1e-2 * t + 1e-3
+where y is the oracle's unrounded fp64 value and t = sum_k |a_ik * b_kj|.  For
+Gemm with alpha != 1 or a beta*C term, t is taken as |alpha| t + |beta C|
+(the same bound applied to each term of the sum); the five workloads are
+checked with the plain t.  Integer results (QLinearMatMul) compare exactly.
+"""
+import numpy as np
+import torch
+
+from onnx_matmul_family_amd import synth
+
+TOL = {"f32": (1e-5, 1e-6), "bf16": (1e-2, 1e-3), "f16": (1e-2, 1e-3)}
+TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def dev(arr, dt=None):
+    """numpy array -> GPU tensor (bf16 arrays are uint16 bit patterns, pass dt='bf16')."""
+    arr = np.ascontiguousarray(arr)
+    if dt == "bf16":
+        return torch.from_numpy(arr.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    return torch.from_numpy(arr.copy()).cuda()
+
+
+def host_f64(t):
+    """GPU tensor -> float64 numpy (exact for bf16 / fp16 / fp32)."""
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        bits = t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        return synth.bf16_to_f32(bits).astype(np.float64).reshape(t.shape)
+    return t.cpu().numpy().astype(np.float64)
+
+
+def check_close(got, y, t, dt, what=""):
+    """Assert |got - y| <= rtol * t + atol elementwise; report the worst offender."""
+    rt, at = TOL[dt]
+    got = np.asarray(got, np.float64).ravel()
+    y = np.asarray(y, np.float64).ravel()
+    t = np.asarray(t, np.float64).ravel()
+    assert got.shape == y.shape, (what, got.shape, y.shape)
+    err = np.abs(got - y)
+    tol = rt * t + at
+    bad = ~(err <= tol)  # NaN counts as bad
+    if bad.any():
+        i = int(np.argmax(np.where(bad, err / tol, 0)))
+        raise AssertionError("%s: %d / %d outside tolerance; worst at %d: got %r want %r (t=%r, tol=%r)"
+                             % (what, int(bad.sum()), bad.size, i, got[i], y[i], t[i], tol[i]))
+
+
+def sample_indices(total, n, seed):
+    rng = np.random.default_rng(seed)
+    if total <= n:
+        return np.arange(total, dtype=np.int64)
+    s = rng.choice(total, size=n, replace=False).astype(np.int64)
+    # always include the first and last elements (tile corners and the ragged tail)
+    return np.unique(np.concatenate([s, [0, total - 1]]))

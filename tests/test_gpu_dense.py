@@ -1,0 +1,174 @@
+"""GPU parity of MatMul and Gemm (bf16 / fp16 / fp32) against the CPU oracle,
+through the C ABI.  Shapes span several tiles with ragged tails in every dim,
+all four transpose combinations, every C broadcast form, 1-D promotion and
+batch broadcasting, plus bit-exact small-integer cases."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from onnx_matmul_family_amd import synth
+from tests.gpu_util import check_close, dev, host_f64, sample_indices
+
+pytestmark = pytest.mark.gpu
+
+om = pytest.importorskip("onnx_matmul_family_amd._omm")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    om.lib()
+
+
+def draw(rng, shape, dt, kind="normal"):
+    x = synth.small_ints(rng, shape) if kind == "int" else synth.normal(rng, shape)
+    return synth.store(x, dt)
+
+
+GEMM_SHAPES = [(1, 1, 1), (7, 5, 3), (64, 32, 48), (300, 520, 200), (257, 129, 199), (130, 264, 136), (33, 17, 0)]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("tA,tB", [(0, 0), (0, 1), (1, 0), (1, 1)])
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_gemm_shapes(dt, tA, tB, M, N, K):
+    rng = np.random.default_rng(M * 7919 + N * 31 + K + 2 * tA + tB)
+    A = draw(rng, (K, M) if tA else (M, K), dt)
+    B = draw(rng, (N, K) if tB else (K, N), dt)
+    C = draw(rng, (N,), dt)
+    alpha, beta = 0.75, -1.25
+    Y = om.gemm(dev(A, dt), dev(B, dt), dev(C, dt), alpha, beta, tA, tB)
+    torch.cuda.synchronize()
+    y, t = oracle.gemm(A, B, C, alpha, beta, tA, tB, dt=dt)
+    cval = oracle.decode(C, dt)
+    check_close(host_f64(Y), y, abs(alpha) * t + abs(beta) * np.abs(cval)[None, :], dt,
+                "gemm %s %dx%dx%d tA=%d tB=%d" % (dt, M, N, K, tA, tB))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("cshape", [None, (), (1,), (90,), (1, 90), (70, 1), (70, 90), (1, 1)])
+def test_gemm_c_forms(dt, cshape):
+    rng = np.random.default_rng(101)
+    M, N, K = 70, 90, 40
+    A, B = draw(rng, (M, K), dt), draw(rng, (K, N), dt)
+    C = draw(rng, cshape, dt) if cshape is not None else None
+    Y = om.gemm(dev(A, dt), dev(B, dt), dev(C, dt) if C is not None else None, 1.5, 0.5)
+    torch.cuda.synchronize()
+    y, t = oracle.gemm(A, B, C, 1.5, 0.5, dt=dt)
+    cm = 0.5 * np.abs(np.broadcast_to(oracle.decode(C.ravel(), dt).reshape(cshape), (M, N))) if C is not None else 0
+    check_close(host_f64(Y), y, 1.5 * t + cm, dt, "gemm C %s" % (cshape,))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("tA,tB", [(0, 0), (0, 1), (1, 0), (1, 1)])
+def test_gemm_small_integers_exact(dt, tA, tB):
+    """Entries in {-2..2} with K = 64: every partial sum is an integer of
+    magnitude <= 256, exact in fp32 and in the output type -> bit-exact."""
+    rng = np.random.default_rng(7 + tA + 2 * tB)
+    M, N, K = 300, 270, 64
+    A = draw(rng, (K, M) if tA else (M, K), dt, "int")
+    B = draw(rng, (N, K) if tB else (K, N), dt, "int")
+    C = draw(rng, (M, N), dt, "int")
+    Y = om.gemm(dev(A, dt), dev(B, dt), dev(C, dt), 1.0, 1.0, tA, tB)
+    torch.cuda.synchronize()
+    y, _ = oracle.gemm(A, B, C, 1.0, 1.0, tA, tB, dt=dt)
+    assert np.array_equal(host_f64(Y), y)
+
+
+@pytest.mark.parametrize("tA,tB", [(0, 1), (0, 0), (1, 0)])
+def test_gemm_bf16_large_tile_path(tA, tB):
+    """Enough output tiles for the 256x256 kernel, ragged M and N, K multiple of 64."""
+    rng = np.random.default_rng(211 + tA + tB)
+    M, N, K = 4224, 4160, 256
+    A = synth.store(synth.normal(rng, (K, M) if tA else (M, K), 0.05), "bf16")
+    B = synth.store(synth.normal(rng, (N, K) if tB else (K, N), 0.05), "bf16")
+    C = synth.store(synth.uniform(rng, (N,), -0.1, 0.1), "bf16")
+    Y = om.gemm(dev(A, "bf16"), dev(B, "bf16"), dev(C, "bf16"), 1.0, 1.0, tA, tB)
+    torch.cuda.synchronize()
+    sel = sample_indices(M * N, 20000, 5)
+    y, t = oracle.gemm(A, B, C, 1.0, 1.0, tA, tB, dt="bf16", sel=sel)
+    check_close(host_f64(Y).ravel()[sel], y, t, "bf16", "gemm 256-tile tA=%d tB=%d" % (tA, tB))
+    # every element written: no NaN / untouched memory anywhere
+    assert torch.isfinite(Y.float()).all()
+
+
+MATMUL_SHAPES = [
+    ((5,), (5,)), ((3,), (3, 4)), ((4, 3), (3,)), ((2, 3, 4), (4, 5)), ((4, 5), (2, 5, 3)),
+    ((2, 1, 3, 4), (5, 4, 2)), ((1, 6, 2), (3, 1, 2, 7)), ((7,), (2, 3, 7, 2)), ((2, 3, 4, 5), (5,)),
+    ((3, 1, 70, 40), (1, 4, 40, 90)), ((2, 3, 2, 130, 72), (3, 1, 72, 66)), ((5, 200, 64), (64, 136)),
+    ((2, 2, 2, 2, 33, 17), (2, 1, 2, 1, 17, 9)), ((0, 3), (3, 4)), ((4, 0), (0, 3)),
+]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("sa,sb", MATMUL_SHAPES)
+def test_matmul_broadcast(dt, sa, sb):
+    rng = np.random.default_rng(abs(hash((sa, sb))) % 2**31)
+    A, B = draw(rng, sa, dt), draw(rng, sb, dt)
+    Y = om.matmul(dev(A, dt), dev(B, dt))
+    torch.cuda.synchronize()
+    y, t = oracle.matmul(A, B, dt=dt)
+    assert tuple(Y.shape) == y.shape
+    check_close(host_f64(Y), y, t, dt, "matmul %s %s x %s" % (dt, sa, sb))
+
+
+def test_matmul_bf16_batched_large_tile_path():
+    """The broadcast-batch structure at 1/2 scale in M, N, K: 128 batches, 256x256 tiles, n-contiguous B."""
+    c = synth.matmul_bf16_bcast(seed=11, scale=2)
+    A, B = c["A"], c["B"]
+    Y = om.matmul(dev(A, "bf16"), dev(B, "bf16"))
+    torch.cuda.synchronize()
+    ysh = oracle.matmul_shape(A.shape, B.shape)
+    sel = sample_indices(int(np.prod(ysh)), 30000, 6)
+    y, t = oracle.matmul(A, B, dt="bf16", sel=sel)
+    check_close(host_f64(Y).ravel()[sel], y, t, "bf16", "matmul batched 256-tile")
+
+
+def test_matmul_small_integers_exact_batched():
+    rng = np.random.default_rng(99)
+    A = synth.store(synth.small_ints(rng, (4, 1, 130, 64)), "bf16")
+    B = synth.store(synth.small_ints(rng, (1, 3, 64, 136)), "bf16")
+    Y = om.matmul(dev(A, "bf16"), dev(B, "bf16"))
+    torch.cuda.synchronize()
+    y, _ = oracle.matmul(A, B, dt="bf16")
+    assert np.array_equal(host_f64(Y), y)
+
+
+def test_printed_examples_on_gpu(golden):
+    """The pages' fp32 MatMul and Gemm examples through the GPU path."""
+    from tests.test_oracle_examples import arr, half_ulps
+    for ex in golden("matmul"):
+        A, B = arr(ex["inputs"]["A"]), arr(ex["inputs"]["B"])
+        Y = om.matmul(dev(A), dev(B))
+        torch.cuda.synchronize()
+        exp = arr(ex["outputs"]["Y"]).astype(np.float64)
+        y, t = oracle.matmul(A, B)
+        assert tuple(Y.shape) == exp.shape, ex["cite"]
+        check_close(host_f64(Y), y, t, "f32", ex["cite"])
+        assert np.all(np.abs(host_f64(Y) - exp) <= 1e-5 * t + 1e-6 + half_ulps(ex["outputs"]["Y"])), ex["cite"]
+    for ex in golden("gemm"):
+        at = ex["attrs"]
+        alpha, beta = float(at.get("alpha", "1.0")), float(at.get("beta", "1.0"))
+        tA, tB = int(at.get("transA", "0")), int(at.get("transB", "0"))
+        A, B = arr(ex["inputs"]["A"]), arr(ex["inputs"]["B"])
+        C = arr(ex["inputs"]["C"]) if "C" in ex["inputs"] else None
+        Y = om.gemm(dev(A), dev(B), dev(C) if C is not None else None, alpha, beta, tA, tB)
+        torch.cuda.synchronize()
+        y, t = oracle.gemm(A, B, C, alpha, beta, tA, tB)
+        cm = abs(beta) * np.abs(np.broadcast_to(C, y.shape)) if C is not None else 0
+        check_close(host_f64(Y), y, abs(alpha) * t + cm, "f32", ex["cite"])
+
+
+def test_gemm_on_side_stream_and_reuse():
+    """Work is enqueued on the caller's stream; a second call on the same buffers is consistent."""
+    rng = np.random.default_rng(5)
+    A, B = draw(rng, (200, 96), "bf16"), draw(rng, (96, 150), "bf16")
+    dA, dB = dev(A, "bf16"), dev(B, "bf16")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        Y1 = om.gemm(dA, dB, None, 1.0, 0.0)
+        Y2 = om.gemm(dA, dB, None, 1.0, 0.0)
+    s.synchronize()
+    assert torch.equal(Y1, Y2)

@@ -1,0 +1,121 @@
+"""GPU parity of GroupedMatMul against the CPU oracle (and the page's examples).
+
+Covers bf16 / fp16 / fp32, int32 and int64 indices, bias present and absent,
+ragged M/N/K and group sizes (several tiles per group, unused and empty
+groups), zero tokens / zero selections, and invalid indices (counted, their
+rows untouched, everything else still correct)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from onnx_matmul_family_amd import synth
+from tests.gpu_util import check_close, dev, host_f64
+
+pytestmark = pytest.mark.gpu
+
+om = pytest.importorskip("onnx_matmul_family_amd._omm")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    om.lib()
+
+
+def run(inp, w, idx, bias, dt):
+    out, ws = om.grouped_matmul(dev(inp, dt), dev(w, dt), dev(idx), dev(bias, dt) if bias is not None else None)
+    bad = om.grouped_matmul_check(ws)
+    return out, bad
+
+
+def test_page_examples(golden):
+    from tests.test_oracle_examples import _grouped_inputs
+    for ex in golden("groupedmatmul"):
+        for T in ex.get("T_values", [None]):
+            if T == "float64":
+                continue  # fp64 is not implemented on the GPU path
+            for Tind in ex.get("Tind_values", [None]):
+                inp, w, idx, bias = _grouped_inputs(ex, T, Tind)
+                dt = {"float16": "f16", None: "f32", "float32": "f32"}[T]
+                out, bad = run(inp, w, idx, bias, dt)
+                y, t = oracle.grouped_matmul(inp, w, idx, bias)
+                assert bad == 0 and tuple(out.shape) == y.shape, ex["cite"]
+                check_close(host_f64(out), y, t, dt, ex["cite"])
+
+
+def test_fp64_is_reported_unsupported():
+    x = torch.zeros((2, 2), dtype=torch.float64, device="cuda")
+    w = torch.zeros((1, 2, 2), dtype=torch.float64, device="cuda")
+    i = torch.zeros((2, 1), dtype=torch.int64, device="cuda")
+    with pytest.raises(om.OmmError) as e:
+        om.grouped_matmul(x, w, i)
+    assert e.value.code == -5
+
+
+CASES = [  # M, K, N, G, S
+    (300, 136, 264, 7, 3), (1000, 512, 512, 16, 4), (64, 64, 64, 1, 1), (5, 8, 8, 40, 2), (513, 200, 300, 5, 5),
+]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("M,K,N,G,S", CASES)
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_random(dt, M, K, N, G, S, with_bias):
+    rng = np.random.default_rng(M + K + N + G + S + with_bias)
+    inp = synth.store(synth.normal(rng, (M, K)), dt)
+    w = synth.store(synth.normal(rng, (G, K, N), 0.05), dt)
+    bias = synth.store(synth.uniform(rng, (G, N), -0.1, 0.1), dt) if with_bias else None
+    idx = synth.distinct_groups(rng, M, min(S, G), G, np.int64 if M % 2 else np.int32)
+    out, bad = run(inp, w, idx, bias, dt)
+    y, t = oracle.grouped_matmul(inp, w, idx, bias, dt=dt)
+    assert bad == 0
+    check_close(host_f64(out), y, t, dt, "grouped %s M=%d K=%d N=%d G=%d S=%d" % (dt, M, K, N, G, S))
+
+
+def test_skewed_groups_bf16():
+    """One hot group with many tiles, several groups of one row, empty groups."""
+    rng = np.random.default_rng(5)
+    M, K, N, G, S = 1500, 256, 512, 12, 2
+    inp = synth.store(synth.normal(rng, (M, K)), "bf16")
+    w = synth.store(synth.normal(rng, (G, K, N), 0.05), "bf16")
+    idx = np.zeros((M, S), np.int32)
+    idx[:, 1] = 3
+    idx[:4, 0] = [5, 6, 7, 11]
+    out, bad = run(inp, w, idx, None, "bf16")
+    y, t = oracle.grouped_matmul(inp, w, idx, None, dt="bf16")
+    assert bad == 0
+    check_close(host_f64(out), y, t, "bf16", "skewed groups")
+
+
+def test_invalid_indices_counted_rows_untouched():
+    rng = np.random.default_rng(9)
+    M, K, N, G, S = 50, 64, 96, 4, 2
+    inp = synth.store(synth.normal(rng, (M, K)), "bf16")
+    w = synth.store(synth.normal(rng, (G, K, N), 0.05), "bf16")
+    idx = synth.distinct_groups(rng, M, S, G, np.int64)
+    idx[3, 1] = -1
+    idx[10, 0] = G
+    idx[20, 1] = 1 << 40  # beyond int32: must not wrap into range
+    sentinel = torch.full((M, S, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    out, ws = om.grouped_matmul(dev(inp, "bf16"), dev(w, "bf16"), dev(idx), None, output=sentinel)
+    assert om.grouped_matmul_check(ws) == 3
+    got = host_f64(out)
+    for (m, i) in [(3, 1), (10, 0), (20, 1)]:
+        assert (got[m, i] == 7.0).all()
+    ok = np.ones((M, S), bool)
+    ok[3, 1] = ok[10, 0] = ok[20, 1] = False
+    idx_fixed = np.where(ok, idx, 0)
+    y, t = oracle.grouped_matmul(inp, w, idx_fixed, None, dt="bf16")
+    check_close(got[ok], y[ok], t[ok], "bf16", "valid rows next to invalid ones")
+
+
+@pytest.mark.parametrize("M,S", [(0, 3), (4, 0), (0, 0)])
+def test_empty(M, S):
+    inp = torch.zeros((M, 16), dtype=torch.bfloat16, device="cuda")
+    w = torch.ones((3, 16, 8), dtype=torch.bfloat16, device="cuda")
+    idx = torch.zeros((M, S), dtype=torch.int64, device="cuda")
+    out, ws = om.grouped_matmul(inp, w, idx)
+    assert tuple(out.shape) == (M, S, 8)
+    assert om.grouped_matmul_check(ws) == 0

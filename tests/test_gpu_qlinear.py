@@ -1,0 +1,121 @@
+"""GPU parity of QLinearMatMul against the CPU oracle: bit-exact int8/uint8 outputs.
+
+Covers the pages' printed examples, every int8/uint8 combination of a, b and y,
+per-tensor / per-row / per-column parameters (1-D and N-D forms), batched
+operands, ragged tiles, the element-wise path for unaligned extents,
+constructed round-half-even ties, saturation and 32-bit wraparound."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from onnx_matmul_family_amd import synth
+from tests.gpu_util import dev
+
+pytestmark = pytest.mark.gpu
+
+om = pytest.importorskip("onnx_matmul_family_amd._omm")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    om.lib()
+
+
+def run(a, asc, az, b, bsc, bz, ys, yz):
+    asc, bsc, ys = (np.asarray(x, np.float32) for x in (asc, bsc, ys))
+    y = om.qlinear_matmul(dev(a), dev(asc), dev(az), dev(b), dev(bsc), dev(bz), dev(ys), dev(yz))
+    torch.cuda.synchronize()
+    ref, _ = oracle.qlinear_matmul(a, asc, az, b, bsc, bz, ys, yz)
+    return y.cpu().numpy(), ref
+
+
+def test_printed_examples(golden):
+    from tests.test_oracle_examples import arr
+    for ex in golden("qlinearmatmul"):
+        i = ex["inputs"]
+        # fp16 scales are exactly representable in fp32: pass them as fp32
+        f32 = lambda k: arr(i[k]).astype(np.float32)
+        got, ref = run(arr(i["a"]), f32("a_scale"), arr(i["a_zero_point"]), arr(i["b"]), f32("b_scale"),
+                       arr(i["b_zero_point"]), f32("y_scale"), arr(i["y_zero_point"]))
+        exp = arr(ex["outputs"]["y"])
+        assert np.array_equal(got, exp), (ex["cite"], got, exp)
+        assert np.array_equal(got, ref), ex["cite"]
+
+
+TYPES = [(np.int8, np.int8, np.int8), (np.uint8, np.int8, np.uint8), (np.int8, np.uint8, np.int8),
+         (np.uint8, np.uint8, np.uint8)]
+SHAPES = [(1, 1, 1), (33, 45, 17), (300, 272, 208), (256, 256, 256), (300, 200, 272), (512, 512, 512), (5, 7, 0)]
+
+
+def rint(rng, shape, dt, lo=None, hi=None):
+    info = np.iinfo(dt)
+    return rng.integers(info.min if lo is None else lo, (info.max if hi is None else hi) + 1, size=shape).astype(dt)
+
+
+@pytest.mark.parametrize("ta,tb,ty", TYPES)
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("mode", ["tensor", "rowcol", "vector"])
+def test_random(ta, tb, ty, M, N, K, mode):
+    rng = np.random.default_rng(M * 1000 + N * 10 + K + len(mode))
+    a, b = rint(rng, (M, K), ta), rint(rng, (K, N), tb)
+    zlo = lambda d: 0 if d == np.uint8 else -16
+    zhi = lambda d: 32 if d == np.uint8 else 16
+    if mode == "tensor":
+        asc, bsc = np.float32(0.004), np.float32(0.007)
+        az, bz = np.array(rint(rng, (), ta, zlo(ta), zhi(ta))), np.array(rint(rng, (), tb, zlo(tb), zhi(tb)))
+    else:
+        ash, bsh = ((M, 1), (1, N)) if mode == "rowcol" else ((M,), (N,))
+        asc = synth.uniform(rng, ash, 0.002, 0.01)
+        bsc = synth.uniform(rng, bsh, 0.002, 0.01)
+        az, bz = rint(rng, ash, ta, zlo(ta), zhi(ta)), rint(rng, bsh, tb, zlo(tb), zhi(tb))
+        if M == 1:
+            asc, az = asc.reshape(()) if mode == "vector" else asc, az.reshape(()) if mode == "vector" else az
+        if N == 1 and mode == "vector":
+            bsc, bz = bsc.reshape(()), bz.reshape(())
+    yz = np.array(3 if ty == np.int8 else 120, ty)
+    got, ref = run(a, asc, az, b, bsc, bz, 0.05, yz)
+    assert got.dtype == ty
+    assert np.array_equal(got, ref), (np.argwhere(got != ref)[:5], M, N, K)
+
+
+def test_batched_params():
+    rng = np.random.default_rng(77)
+    D, M, K, N = 3, 130, 96, 70
+    a, b = rint(rng, (D, M, K), np.int8), rint(rng, (D, K, N), np.int8)
+    az, bz = rint(rng, (D, M, 1), np.int8, -16, 16), rint(rng, (D, 1, N), np.int8, -16, 16)
+    asc, bsc = synth.uniform(rng, (D, M, 1), 0.002, 0.01), synth.uniform(rng, (D, 1, N), 0.002, 0.01)
+    got, ref = run(a, asc, az, b, bsc, bz, 0.05, np.array(0, np.int8))
+    assert np.array_equal(got, ref)
+
+
+def test_broadcast_batch_and_shared_params():
+    rng = np.random.default_rng(78)
+    a, b = rint(rng, (2, 1, 40, 64), np.uint8), rint(rng, (3, 64, 48), np.int8)
+    az, bz = rint(rng, (40, 1), np.uint8, 100, 150), rint(rng, (1, 48), np.int8, -16, 16)
+    asc, bsc = synth.uniform(rng, (40, 1), 0.002, 0.01), synth.uniform(rng, (1, 48), 0.002, 0.01)
+    got, ref = run(a, asc, az, b, bsc, bz, 0.03, np.array(7, np.int8))
+    assert got.shape == (2, 3, 40, 48) and np.array_equal(got, ref)
+
+
+def test_round_half_even_ties():
+    """x = v / 2 exactly: y_scale 2, unit scales.  Ties must go to the even integer."""
+    v = np.array([[1, 3, 5, 7, -1, -3, -5, 9, 127, -127]], np.int8)
+    a = np.ones((1, 1), np.int8)
+    got, ref = run(a, 1.0, np.array(0, np.int8), v, 1.0, np.array(0, np.int8), 2.0, np.array(0, np.int8))
+    assert np.array_equal(got[0], [0, 2, 2, 4, 0, -2, -2, 4, 64, -64])
+    assert np.array_equal(got, ref)
+
+
+def test_saturation_and_wraparound():
+    K = 40000  # 255 * 255 * K exceeds 2^31: the int32 accumulator wraps
+    a = np.full((3, K), -128, np.int8)
+    b = np.full((K, 2), -128, np.int8)
+    got, ref = run(a, 1.0, np.array(127, np.int8), b, 1.0, np.array(127, np.int8), 1.0, np.array(0, np.int8))
+    assert np.array_equal(got, ref)
+    a = np.full((2, 64), 127, np.int8)
+    b = np.full((64, 2), 127, np.int8)
+    got, ref = run(a, 1.0, np.array(0, np.int8), b, 1.0, np.array(0, np.int8), 1.0, np.array(0, np.int8))
+    assert np.array_equal(got, ref) and (got == 127).all()
