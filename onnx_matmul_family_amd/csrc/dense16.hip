@@ -18,7 +18,8 @@ template <int BM, int BN, int DT, bool AK, bool BKM, bool VEC>
 __global__ __launch_bounds__(NT) void dense16_kernel(DenseArgs p, int tiles_m, int tiles_n) {
     constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
     constexpr int STAGE = (BM + BN) * KSTEP * 2;
-    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) char smem0[STAGE];
+    __shared__ __attribute__((aligned(1024))) char smem1[STAGE];
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -44,16 +45,22 @@ __global__ __launch_bounds__(NT) void dense16_kernel(DenseArgs p, int tiles_m, i
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     const int nk = (int)((K + KSTEP - 1) / KSTEP);
-    TileSrc<BM, AK> srcA;
-    TileSrc<BN, BKM> srcB;
-    srcA.init(A, p.lda, m0, M, K, t);
-    srcB.init(B, p.ldb, n0, N, K, t);
-    if (!VEC)
-        mainloop<BM, BN, DT, AK, BKM, 2>(acc, smem, srcA, srcB, nk, t, lane, wm, wn);
-    else if ((m0 + BM <= M) && (n0 + BN <= N) && (K % KSTEP == 0))
-        mainloop<BM, BN, DT, AK, BKM, 0>(acc, smem, srcA, srcB, nk, t, lane, wm, wn);
-    else
-        mainloop<BM, BN, DT, AK, BKM, 1>(acc, smem, srcA, srcB, nk, t, lane, wm, wn);
+    if constexpr (VEC) {
+        DmaSrc<BM, AK> srcA;
+        DmaSrc<BN, BKM> srcB;
+        srcA.init(A, p.lda, m0, M, K, lane);
+        srcB.init(B, p.ldb, n0, N, K, lane);
+        if ((m0 + BM <= M) && (n0 + BN <= N) && (K % KSTEP == 0))
+            mainloop_dma<BM, BN, DT, AK, BKM, false>(acc, smem0, smem1, srcA, srcB, nk, lane, wm, wn, wave);
+        else
+            mainloop_dma<BM, BN, DT, AK, BKM, true>(acc, smem0, smem1, srcA, srcB, nk, lane, wm, wn, wave);
+    } else {
+        TileSrc<BM, AK> srcA;
+        TileSrc<BN, BKM> srcB;
+        srcA.init(A, p.lda, m0, M, K, t);
+        srcB.init(B, p.ldb, n0, N, K, t);
+        mainloop<BM, BN, DT, AK, BKM, 2>(acc, smem0, smem1, srcA, srcB, nk, t, lane, wm, wn);
+    }
 
     // epilogue: lane holds, for each (i, j, q), row m and the 4 columns n..n+3
     const float alpha = p.alpha, beta = p.beta;
@@ -121,7 +128,10 @@ hipError_t launch_dt(const DenseArgs& a, hipStream_t s) {
     const bool b_ok = al16(a.B) && a.ldb % 8 == 0 && (a.b_kmajor ? a.K % 8 == 0 : a.N % 8 == 0) &&
                       a.b_bs0 % 8 == 0 && a.b_bs1 % 8 == 0;
     const bool y_ok = ((uintptr_t)a.Y & 7) == 0 && a.y_bs0 % 4 == 0 && a.y_bs1 % 4 == 0;
-    const bool vec = a_ok && b_ok && y_ok;
+    // DMA byte offsets are 32-bit: one tile's rows must span < 2 GiB per operand
+    const bool span_ok = (a.a_kmajor ? 256 * a.lda * 2 : 64 * a.lda * 2) < (1LL << 31) &&
+                         (a.b_kmajor ? 256 * a.ldb * 2 : 64 * a.ldb * 2) < (1LL << 31);
+    const bool vec = a_ok && b_ok && y_ok && span_ok;
     const int64_t big_tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256) * a.nb0 * a.nb1;
     if (vec && big_tiles >= 256) return launch_layout<256, 256, DT, true>(a, s);
     if (vec) return launch_layout<128, 128, DT, true>(a, s);

@@ -183,18 +183,18 @@ __device__ __forceinline__ u32x4_t read_frag(const char* lds, int mnb, int s, in
     }
 }
 
+// Register-staged K loop (element-wise loads, any shape / alignment).
 template <int BM, int BN, int DT, bool AK, bool BKM, int MODE, class SA, class SB>
-__device__ __forceinline__ void mainloop(f32x16_t (&acc)[BM / 64][BN / 64], char* smem, const SA& srcA,
-                                         const SB& srcB, int nk, int t, int lane, int wm, int wn) {
+__device__ __forceinline__ void mainloop(f32x16_t (&acc)[BM / 64][BN / 64], char* smem0, char* smem1,
+                                         const SA& srcA, const SB& srcB, int nk, int t, int lane, int wm, int wn) {
     constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
-    constexpr int A_BYTES = BM * KSTEP * 2, B_BYTES = BN * KSTEP * 2;
-    constexpr int STAGE = A_BYTES + B_BYTES;
+    constexpr int A_BYTES = BM * KSTEP * 2;
     u32x4_t ra[Chunks<BM, AK>::NC], rb[Chunks<BN, BKM>::NC];
     if (nk > 0) {
         srcA.template load<MODE>(ra, 0);
         srcB.template load<MODE>(rb, 0);
-        store_tile<BM, AK>(smem, ra, t);
-        store_tile<BN, BKM>(smem + A_BYTES, rb, t);
+        store_tile<BM, AK>(smem0, ra, t);
+        store_tile<BN, BKM>(smem0 + A_BYTES, rb, t);
     }
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
@@ -203,7 +203,7 @@ __device__ __forceinline__ void mainloop(f32x16_t (&acc)[BM / 64][BN / 64], char
             srcA.template load<MODE>(ra, kt + 1);
             srcB.template load<MODE>(rb, kt + 1);
         }
-        const char* sa = smem + buf * STAGE;
+        const char* sa = buf ? smem1 : smem0;
         const char* sb = sa + A_BYTES;
 #pragma unroll
         for (int s = 0; s < KSTEP / 16; ++s) {
@@ -218,11 +218,292 @@ __device__ __forceinline__ void mainloop(f32x16_t (&acc)[BM / 64][BN / 64], char
                 for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16<DT>(bfr[j], af[i], acc[i][j]);
         }
         if (kt + 1 < nk) {
-            char* so = smem + (buf ^ 1) * STAGE;
+            char* so = buf ? smem0 : smem1;
             store_tile<BM, AK>(so, ra, t);
             store_tile<BN, BKM>(so + A_BYTES, rb, t);
         }
         __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Direct global -> LDS path: buffer_load_dwordx4 ... lds.  Each wave
+// instruction fills one contiguous 1 KiB LDS block (lane p -> bytes 16p..16p+15),
+// so a lane chooses which global 16-byte chunk lands in its slot; the tile
+// layouts above are produced by that choice.  Out-of-range lanes get a byte
+// offset past the buffer's range and the hardware writes zeros, which pads
+// ragged tiles and K tails without branches.  Offsets are 32-bit: a tile's
+// rows must span less than 2 GiB (checked on the host).
+constexpr uint32_t DMA_OOB = 0x80000000u;
+
+// Raw buffer resource (gfx9 family): base, stride 0, 2^31-1 bytes in range.
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base) {
+    const uint64_t a = (uint64_t)base;
+    return i32x4_t{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                   __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)), 0x7fffffff, 0x00020000};
+}
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)OMM_LDS(const char, p));
+}
+// The DMA load is issued from inline assembly on purpose: the compiler's
+// wait-count pass cannot tell which LDS buffer an LDS-DMA intrinsic writes and
+// would make every later ds_read wait for all DMA traffic in flight (the
+// prefetch of the next stage included).  The kernels wait for their own DMA
+// (s_waitcnt vmcnt) before the barrier that publishes a stage.  M0 is set per
+// instruction, followed by the one wait state an M0 write needs before an
+// LDS-DMA read of it.
+__device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t lds, uint32_t voff) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds),
+        "v"(voff), "s"(rsrc)
+        : "memory", "m0");
+}
+__device__ __forceinline__ void dma16u(i32x4_t rsrc, uint32_t lds, uint32_t voff) {
+    dma16(rsrc, (uint32_t)__builtin_amdgcn_readfirstlane((int)lds), voff);
+}
+
+// One operand tile (R rows along m/n, 128 bytes of k per stage) loaded by DMA.
+// ES = element size in bytes (2: bf16/fp16, 1: int8; MN-major needs ES = 2).
+//  K-major: LDS block b = plane (b / (R/32)), rows 32 (b % (R/32)) .. +31;
+//           lane p -> row p/2, physical half p&1 (logical half (p&1)^kswz).
+//  MN-major: LDS block b = k rows RPB b .. RPB b + RPB-1 (RPB = 1024 / (2R));
+//           lane p -> row p / LPR, physical 16-byte chunk p % LPR (LPR = R/8),
+//           logical 32-byte granule = physical ^ mswz16(row).
+template <int R, bool KMAJ, int ES = 2>
+struct DmaSrc {
+    static_assert(KMAJ || ES == 2, "8-bit MN-major tiles use DmaSrcMN8");
+    static constexpr int NBLK = R / 8;  // 1 KiB blocks per stage
+    static constexpr int PER_WAVE = NBLK / 4;
+    static constexpr int RPB = KMAJ ? 32 : 1024 / (2 * R);
+    static constexpr int LPR = R / 8;
+    static constexpr int KE = 128 / ES;  // k elements per stage
+    const char* base;   // tile origin at stage 0 (bytes)
+    int64_t step;       // bytes per stage
+    uint32_t ldb;       // row stride as stored (bytes)
+    uint32_t lane_off[2];
+    int64_t MN, K, mn0;
+    int lane;
+
+    __device__ void init(const void* b, int64_t ld, int64_t mn0_, int64_t MN_, int64_t K_, int lane_) {
+        lane = lane_;
+        MN = MN_;
+        K = K_;
+        mn0 = mn0_;
+        ldb = (uint32_t)(ld * ES);
+        if constexpr (KMAJ) {
+            base = (const char*)b + mn0 * ld * ES;
+            step = 128;
+            lane_off[0] = lane_off[1] = (uint32_t)(lane >> 1) * ldb + ((uint32_t)((lane & 1) ^ kswz(lane >> 1)) << 4);
+        } else {
+            base = (const char*)b + mn0 * ES;
+            step = (int64_t)KE * ld * ES;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) lane_off[q] = (uint32_t)(lane / LPR) * ldb + (chunk(q) << 4);
+        }
+    }
+    // MN-major: logical 16-byte chunk (along m/n) of this lane in a block of parity q
+    __device__ uint32_t chunk(int q) const {
+        const int row = q * RPB + lane / LPR, C = lane % LPR;
+        return (uint32_t)(2 * ((C >> 1) ^ mswz16(row)) + (C & 1));
+    }
+
+    template <bool CHECKED>
+    __device__ __forceinline__ void issue(char* lds, int kt, int wave) const {
+        const i32x4_t r = make_rsrc(base + (int64_t)kt * step);
+        const uint32_t l0 = lds_addr(lds);
+#pragma unroll
+        for (int j = 0; j < PER_WAVE; ++j) {
+            const int b = wave * PER_WAVE + j;
+            uint32_t voff;
+            if constexpr (KMAJ) {
+                const int s = b / (R / 32), rb = b % (R / 32);
+                voff = lane_off[0] + (uint32_t)(rb * 32) * ldb + (uint32_t)(s * 32);
+                if (CHECKED) {
+                    const int64_t row = mn0 + rb * 32 + (lane >> 1);
+                    const int64_t k = (int64_t)kt * KE + (16 / ES) * (2 * s + ((lane & 1) ^ kswz(lane >> 1)));
+                    if (!(row < MN && k < K)) voff = DMA_OOB;
+                }
+            } else {
+                voff = lane_off[j & 1] + (uint32_t)(b * RPB) * ldb;
+                if (CHECKED) {
+                    const int64_t k = (int64_t)kt * KE + b * RPB + lane / LPR;
+                    const int64_t mn = mn0 + 8 * (int64_t)chunk(j & 1);
+                    if (!(k < K && mn < MN)) voff = DMA_OOB;
+                }
+            }
+            dma16u(r, l0 + b * 1024, voff);
+        }
+    }
+};
+
+// 8-bit MN-major tile (int8 b, n contiguous): 128 k rows of R bytes, 16-byte
+// chunk c of row k stored at chunk c ^ mswz8(k).  LDS block b = rows 4b..4b+3
+// (R = 256); lane p -> row p / 16, physical chunk p % 16.
+template <int R>
+struct DmaSrcMN8 {
+    static_assert(R == 256, "256-byte rows");
+    static constexpr int PER_WAVE = 8;  // 32 blocks per stage
+    const char* base;
+    int64_t step;
+    uint32_t ldb;
+    uint32_t lane_off[2];
+    int64_t MN, K, mn0;
+    int lane;
+
+    __device__ uint32_t chunk(int q) const {
+        const int row = 4 * q + (lane >> 4);
+        return (uint32_t)((lane & 15) ^ mswz8(row));
+    }
+    __device__ void init(const void* b, int64_t ld, int64_t mn0_, int64_t MN_, int64_t K_, int lane_) {
+        lane = lane_;
+        MN = MN_;
+        K = K_;
+        mn0 = mn0_;
+        ldb = (uint32_t)ld;
+        base = (const char*)b + mn0;
+        step = 128 * ld;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) lane_off[q] = (uint32_t)(lane >> 4) * ldb + (chunk(q) << 4);
+    }
+    template <bool CHECKED>
+    __device__ __forceinline__ void issue(char* lds, int kt, int wave) const {
+        const i32x4_t r = make_rsrc(base + (int64_t)kt * step);
+        const uint32_t l0 = lds_addr(lds);
+#pragma unroll
+        for (int j = 0; j < PER_WAVE; ++j) {
+            const int b = wave * PER_WAVE + j;
+            uint32_t voff = lane_off[j & 1] + (uint32_t)(b * 4) * ldb;
+            if (CHECKED) {
+                const int64_t k = (int64_t)kt * 128 + b * 4 + (lane >> 4);
+                const int64_t mn = mn0 + 16 * (int64_t)chunk(j & 1);
+                if (!(k < K && mn < MN)) voff = DMA_OOB;
+            }
+            dma16u(r, l0 + b * 1024, voff);
+        }
+    }
+};
+
+// K-major A tile whose rows are gathered (grouped product: token rows
+// input[pair / S]).  roff[rb] = byte offset of the row this lane loads in row
+// block rb (DMA_OOB for rows past the tile's valid rows) plus the lane's half.
+template <int R>
+struct GatherDma {
+    static constexpr int NBLK = R / 8;
+    static constexpr int PER_WAVE = NBLK / 4;
+    const char* base;
+    uint32_t roff[R / 32];
+    int64_t K;
+    int lane;
+
+    template <bool CHECKED>
+    __device__ __forceinline__ void issue(char* lds, int kt, int wave) const {
+        const i32x4_t r = make_rsrc(base + (int64_t)kt * KSTEP * 2);
+        const uint32_t l0 = lds_addr(lds);
+#pragma unroll
+        for (int j = 0; j < PER_WAVE; ++j) {
+            const int b = wave * PER_WAVE + j;
+            const int s = b / (R / 32), rb = b % (R / 32);
+            uint32_t voff = roff[rb] + (uint32_t)(s * 32);
+            if (CHECKED) {
+                const int64_t k = (int64_t)kt * KSTEP + 8 * (2 * s + ((lane & 1) ^ kswz(lane >> 1)));
+                if (k >= K) voff = DMA_OOB;
+            }
+            dma16u(r, l0 + b * 1024, voff);
+        }
+    }
+};
+
+template <int BM, int BN, bool AK, bool BKM>
+struct Frags {
+    static constexpr int TM = BM / 64, TN = BN / 64;
+    u32x4_t a[TM], b[TN];
+    __device__ __forceinline__ void read(const char* st, int s, int lane, int wm, int wn) {
+        constexpr int A_BYTES = BM * KSTEP * 2;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) a[i] = read_frag<BM, AK>(st, wm * (BM / 2) + 32 * i, s, lane);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) b[j] = read_frag<BN, BKM>(st + A_BYTES, wn * (BN / 2) + 32 * j, s, lane);
+    }
+};
+
+template <int DT, int TM, int TN, class F>
+__device__ __forceinline__ void mma_step(f32x16_t (&acc)[TM][TN], const F& f) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16<DT>(f.b[j], f.a[i], acc[i][j]);
+}
+
+__device__ __forceinline__ void fence_sched() { __builtin_amdgcn_sched_barrier(0); }
+
+// Wait until at most n of this wave's vector-memory ops are outstanding (gfx9
+// s_waitcnt: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left unrestricted).
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+    __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+// One stage of the DMA K loop: stage kt is complete in X (barrier passed),
+// fc holds its k-block 0 fragments (requested), stage kt+1 is in flight into Y.
+// The fragments of k-block s+1 are read while k-block s's MFMAs run; stage
+// kt+2's DMA is issued right after the barrier that retires stage kt.
+template <int BM, int BN, int DT, bool AK, bool BKM, bool CHECKED, class SA, class SB, class F>
+__device__ __forceinline__ void dma_stage(f32x16_t (&acc)[BM / 64][BN / 64], F& fc, F& fn, char* X, char* Y,
+                                          const SA& srcA, const SB& srcB, int kt, int nk, int lane, int wm, int wn,
+                                          int wave) {
+    constexpr int A_BYTES = BM * KSTEP * 2;
+    fence_sched();
+    fn.read(X, 1, lane, wm, wn);
+    fence_sched();
+    mma_step<DT>(acc, fc);
+    fence_sched();
+    fc.read(X, 2, lane, wm, wn);
+    fence_sched();
+    mma_step<DT>(acc, fn);
+    fence_sched();
+    fn.read(X, 3, lane, wm, wn);
+    fence_sched();
+    mma_step<DT>(acc, fc);
+    fence_sched();
+    if (kt + 1 < nk) wait_vm<0>();  // stage kt+1 has landed (this wave's part)
+    __syncthreads();                 // ... for every wave; and every read of X is done
+    if (kt + 1 < nk) fc.read(Y, 0, lane, wm, wn);
+    if (kt + 2 < nk) {
+        srcA.template issue<CHECKED>(X, kt + 2, wave);
+        srcB.template issue<CHECKED>(X + A_BYTES, kt + 2, wave);
+    }
+    fence_sched();
+    mma_step<DT>(acc, fn);
+}
+
+// DMA K loop over nk stages; stage kt lives in buffer kt & 1 (s0 / s1).  The
+// loop body covers two stages so that each LDS access names its buffer
+// statically.
+template <int BM, int BN, int DT, bool AK, bool BKM, bool CHECKED, class SA, class SB>
+__device__ __forceinline__ void mainloop_dma(f32x16_t (&acc)[BM / 64][BN / 64], char* __restrict__ s0,
+                                             char* __restrict__ s1, const SA& srcA, const SB& srcB, int nk, int lane,
+                                             int wm, int wn, int wave) {
+    constexpr int A_BYTES = BM * KSTEP * 2;
+    constexpr int LOADS = SA::PER_WAVE + SB::PER_WAVE;  // DMA instructions per stage per wave
+    if (nk <= 0) return;
+    srcA.template issue<CHECKED>(s0, 0, wave);
+    srcB.template issue<CHECKED>(s0 + A_BYTES, 0, wave);
+    if (nk > 1) {
+        srcA.template issue<CHECKED>(s1, 1, wave);
+        srcB.template issue<CHECKED>(s1 + A_BYTES, 1, wave);
+        wait_vm<LOADS>();
+    } else {
+        wait_vm<0>();
+    }
+    __syncthreads();
+    Frags<BM, BN, AK, BKM> fc, fn;
+    fc.read(s0, 0, lane, wm, wn);
+    for (int kt = 0; kt < nk; kt += 2) {
+        dma_stage<BM, BN, DT, AK, BKM, CHECKED>(acc, fc, fn, s0, s1, srcA, srcB, kt, nk, lane, wm, wn, wave);
+        if (kt + 1 < nk)
+            dma_stage<BM, BN, DT, AK, BKM, CHECKED>(acc, fc, fn, s1, s0, srcA, srcB, kt + 1, nk, lane, wm, wn, wave);
     }
 }
 

@@ -7,11 +7,13 @@
 // (M*S, K, N) weights.  Here the (m, i) pairs are counting-sorted by group on
 // the device and every group's pairs run as the rows of one GEMM against
 // weights[g]:
-//   1. route_kernel (one workgroup): histogram of the M*S indices over the G
-//      groups (invalid indices are counted, not routed), exclusive scans of
-//      the counts and of the per-group tile counts, the tile table
-//      (group, first sorted pair, rows) and the scatter of pair ids
-//      p = m*S + i into group order;
+//   1. routing, four short kernels: zero the counters; per-workgroup LDS
+//      histograms of the M*S indices over the G groups folded into global
+//      counts (invalid indices are counted, not routed); exclusive scans of
+//      the counts and of the per-group tile counts into the tile table
+//      (group, first sorted pair, rows); the scatter of pair ids p = m*S + i
+//      into group order, each workgroup reserving its range per group with
+//      one global atomic;
 //   2. grouped16_kernel: one 256x256 output tile per workgroup, rows gathered
 //      from input[p / S], B = weights[g] (n contiguous, read through the
 //      transposing LDS path), epilogue adds bias[g] in fp32, rounds once and
@@ -31,14 +33,19 @@ constexpr int GBM = 256, GBN = 256;  // grouped tile
 constexpr int MAX_G = 8192;          // groups handled by the single-workgroup router
 
 // workspace layout (bytes, from a 256-byte aligned base)
-//   [0, 64)           header: int32 num_tiles, int32 invalid_count
-//   [64, 64+16*TT)    tile table: int4 (group, first sorted pair, rows, 0), TT = P/BM_MIN + G + 1
-//   [.., + 4*P)       sorted pair ids
+//   [0, 64)                   header: int32 num_tiles, int32 invalid_count
+//   [64, 64 + 4G)             per-group pair counts
+//   [64 + 4G, 64 + 8G)        per-group scatter cursors
+//   [tiles, + 16 TT)          tile table: int4 (group, first sorted pair, rows, 0), TT = P/BM_MIN + G + 1
+//   [sorted, + 4P)            pair ids p = m*S + i in group order
 constexpr int BM_MIN = 128;
+constexpr int ROUTE_CHUNK = 1024;  // pairs per routing workgroup
 __host__ __device__ inline int64_t tiles_cap(int64_t P, int64_t G) { return P / BM_MIN + G + 1; }
-__host__ __device__ inline int64_t off_tiles() { return 64; }
+__host__ __device__ inline int64_t off_counts() { return 64; }
+__host__ __device__ inline int64_t off_cursor(int64_t G) { return 64 + 4 * G; }
+__host__ __device__ inline int64_t off_tiles(int64_t G) { return (64 + 8 * G + 255) / 256 * 256; }
 __host__ __device__ inline int64_t off_sorted(int64_t P, int64_t G) {
-    return (off_tiles() + 16 * tiles_cap(P, G) + 255) / 256 * 256;
+    return (off_tiles(G) + 16 * tiles_cap(P, G) + 255) / 256 * 256;
 }
 
 __device__ __forceinline__ int64_t load_idx(const void* idx, int64_t p, int idx64) {
@@ -71,23 +78,40 @@ __device__ int block_exclusive_scan(int* v, int n, int* part) {
     return total;
 }
 
-__global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(const void* idx, int idx64, int64_t P, int G, int BM,
-                                                              char* ws) {
-    __shared__ int cnt[MAX_G];    // pairs per group
-    __shared__ int tile0[MAX_G];  // first tile of each group
-    __shared__ int row0[MAX_G];   // first sorted position of each group, then the scatter cursor
-    __shared__ int part[ROUTE_THREADS];
+// 1. zero the counts and the header
+__global__ void route_zero_kernel(char* ws, int G) {
+    int* c = (int*)(ws + off_counts());
+    for (int g = threadIdx.x; g < G; g += blockDim.x) c[g] = 0;
+    if (threadIdx.x < 16) ((int*)ws)[threadIdx.x] = 0;
+}
+
+// 2. per-group pair counts: an LDS histogram per workgroup, one global add per used group
+__global__ __launch_bounds__(256) void route_hist_kernel(const void* idx, int idx64, int64_t P, int G, char* ws) {
+    __shared__ int h[MAX_G];
     __shared__ int bad;
-    const int t = threadIdx.x;
-    for (int g = t; g < G; g += ROUTE_THREADS) cnt[g] = 0;
-    if (t == 0) bad = 0;
+    for (int g = threadIdx.x; g < G; g += 256) h[g] = 0;
+    if (threadIdx.x == 0) bad = 0;
     __syncthreads();
-    for (int64_t p = t; p < P; p += ROUTE_THREADS) {
+    const int64_t p0 = (int64_t)blockIdx.x * ROUTE_CHUNK, p1 = min(P, p0 + ROUTE_CHUNK);
+    for (int64_t p = p0 + threadIdx.x; p < p1; p += 256) {
         const int64_t g = load_idx(idx, p, idx64);
-        if (g >= 0 && g < G) atomicAdd(&cnt[g], 1);
+        if (g >= 0 && g < G) atomicAdd(&h[g], 1);
         else atomicAdd(&bad, 1);
     }
     __syncthreads();
+    int* c = (int*)(ws + off_counts());
+    for (int g = threadIdx.x; g < G; g += 256)
+        if (h[g]) atomicAdd(&c[g], h[g]);
+    if (threadIdx.x == 0 && bad) atomicAdd(&((int*)ws)[1], bad);
+}
+
+// 3. scans: first sorted position and first tile of each group, the tile table, the cursors
+__global__ __launch_bounds__(ROUTE_THREADS) void route_scan_kernel(int64_t P, int G, int BM, char* ws) {
+    __shared__ int tile0[MAX_G];
+    __shared__ int row0[MAX_G];
+    __shared__ int part[ROUTE_THREADS];
+    const int t = threadIdx.x;
+    const int* cnt = (const int*)(ws + off_counts());
     for (int g = t; g < G; g += ROUTE_THREADS) {
         tile0[g] = (cnt[g] + BM - 1) / BM;
         row0[g] = cnt[g];
@@ -95,26 +119,45 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(const void* idx, i
     __syncthreads();
     const int ntiles = block_exclusive_scan(tile0, G, part);
     block_exclusive_scan(row0, G, part);
-    int4* tiles = (int4*)(ws + off_tiles());
+    int4* tiles = (int4*)(ws + off_tiles(G));
+    int* cur = (int*)(ws + off_cursor(G));
     for (int g = t; g < G; g += ROUTE_THREADS) {
         const int c = cnt[g], nt = (c + BM - 1) / BM;
         for (int tt = 0; tt < nt; ++tt) tiles[tile0[g] + tt] = make_int4(g, row0[g] + tt * BM, min(BM, c - tt * BM), 0);
+        cur[g] = row0[g];
+    }
+    if (t == 0) ((int*)ws)[0] = ntiles;
+}
+
+// 4. scatter pair ids into group order: each workgroup reserves its range per
+//    group with one global add, then places its pairs with LDS cursors
+__global__ __launch_bounds__(256) void route_scatter_kernel(const void* idx, int idx64, int64_t P, int G, char* ws) {
+    __shared__ int h[MAX_G];
+    for (int g = threadIdx.x; g < G; g += 256) h[g] = 0;
+    __syncthreads();
+    const int64_t p0 = (int64_t)blockIdx.x * ROUTE_CHUNK, p1 = min(P, p0 + ROUTE_CHUNK);
+    for (int64_t p = p0 + threadIdx.x; p < p1; p += 256) {
+        const int64_t g = load_idx(idx, p, idx64);
+        if (g >= 0 && g < G) atomicAdd(&h[g], 1);
     }
     __syncthreads();
+    int* cur = (int*)(ws + off_cursor(G));
+    for (int g = threadIdx.x; g < G; g += 256)
+        if (h[g]) h[g] = atomicAdd(&cur[g], h[g]);
+    __syncthreads();
     int* sorted = (int*)(ws + off_sorted(P, G));
-    for (int64_t p = t; p < P; p += ROUTE_THREADS) {
+    for (int64_t p = p0 + threadIdx.x; p < p1; p += 256) {
         const int64_t g = load_idx(idx, p, idx64);
-        if (g >= 0 && g < G) sorted[atomicAdd(&row0[g], 1)] = (int)p;
-    }
-    if (t == 0) {
-        ((int*)ws)[0] = ntiles;
-        ((int*)ws)[1] = bad;
+        if (g >= 0 && g < G) sorted[atomicAdd(&h[g], 1)] = (int)p;
     }
 }
 
-template <int DT, int MODE>
-__device__ __forceinline__ void grouped_body(const GroupedArgs& a, const char* ws, int tile, int tn, char* smem) {
-    const int4 te = ((const int4*)(ws + off_tiles()))[tile];
+// One 256x256 tile of the grouped product.  VEC: DMA path (CHECKED pads ragged
+// rows / columns / K with zeros); otherwise element-wise register-staged loads.
+template <int DT, bool VEC>
+__device__ __forceinline__ void grouped_body(const GroupedArgs& a, const char* ws, int tile, int tn, char* s0,
+                                             char* s1) {
+    const int4 te = ((const int4*)(ws + off_tiles(a.G)))[tile];
     const int g = te.x, start = te.y, rows = te.z;
     const int* sorted = (const int*)(ws + off_sorted(a.M * a.S, a.G));
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -123,26 +166,6 @@ __device__ __forceinline__ void grouped_body(const GroupedArgs& a, const char* w
     const int64_t n0 = (int64_t)tn * GBN;
 
     using namespace core16;
-    GatherSrc<GBM> srcA;
-    srcA.base = (const uint16_t*)a.input;
-    srcA.K = K;
-    int r0, lk;
-    Chunks<GBM, true>::coords(t, 0, r0, lk);
-    srcA.lk = lk;
-    srcA.valid = 0;
-#pragma unroll
-    for (int i = 0; i < GatherSrc<GBM>::NC; ++i) {
-        const int r = r0 + 32 * i;
-        int64_t off = 0;
-        if (r < rows) {
-            srcA.valid |= 1u << i;
-            off = (int64_t)(sorted[start + r] / S) * K;
-        }
-        srcA.roff[i] = off + srcA.lk;
-    }
-    TileSrc<GBN, false> srcB;
-    srcB.init((const uint16_t*)a.weights + (int64_t)g * K * N, N, n0, N, K, t);
-
     f32x16_t acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -151,11 +174,51 @@ __device__ __forceinline__ void grouped_body(const GroupedArgs& a, const char* w
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     const int nk = (int)((K + KSTEP - 1) / KSTEP);
-    mainloop<GBM, GBN, DT, true, false, MODE>(acc, smem, srcA, srcB, nk, t, lane, wm, wn);
+    const uint16_t* wg = (const uint16_t*)a.weights + (int64_t)g * K * N;
+
+    if constexpr (VEC) {
+        GatherDma<GBM> srcA;
+        srcA.base = (const char*)a.input;
+        srcA.K = K;
+        srcA.lane = lane;
+        const uint32_t half = (uint32_t)((lane & 1) ^ kswz(lane >> 1)) << 4;
+#pragma unroll
+        for (int rb = 0; rb < GBM / 32; ++rb) {
+            const int r = rb * 32 + (lane >> 1);
+            srcA.roff[rb] = r < rows ? (uint32_t)((int64_t)(sorted[start + r] / S) * K * 2) + half : DMA_OOB;
+        }
+        DmaSrc<GBN, false> srcB;
+        srcB.init(wg, N, n0, N, K, lane);
+        if (rows == GBM && n0 + GBN <= N && K % KSTEP == 0)
+            mainloop_dma<GBM, GBN, DT, true, false, false>(acc, s0, s1, srcA, srcB, nk, lane, wm, wn, wave);
+        else
+            mainloop_dma<GBM, GBN, DT, true, false, true>(acc, s0, s1, srcA, srcB, nk, lane, wm, wn, wave);
+    } else {
+        GatherSrc<GBM> srcA;
+        srcA.base = (const uint16_t*)a.input;
+        srcA.K = K;
+        int r0, lk;
+        Chunks<GBM, true>::coords(t, 0, r0, lk);
+        srcA.lk = lk;
+        srcA.valid = 0;
+#pragma unroll
+        for (int i = 0; i < GatherSrc<GBM>::NC; ++i) {
+            const int r = r0 + 32 * i;
+            int64_t off = 0;
+            if (r < rows) {
+                srcA.valid |= 1u << i;
+                off = (int64_t)(sorted[start + r] / S) * K;
+            }
+            srcA.roff[i] = off + srcA.lk;
+        }
+        TileSrc<GBN, false> srcB;
+        srcB.init(wg, N, n0, N, K, t);
+        mainloop<GBM, GBN, DT, true, false, 2>(acc, s0, s1, srcA, srcB, nk, t, lane, wm, wn);
+    }
 
     const uint16_t* bias = a.bias ? (const uint16_t*)a.bias + (int64_t)g * N : nullptr;
     uint16_t* out = (uint16_t*)a.output;
-    const bool vec_store = (MODE != 2) && (N % 4 == 0);
+    const bool vec_store = VEC && (N % 4 == 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = wm * 128 + 32 * i + (lane & 31);
@@ -191,20 +254,15 @@ __device__ __forceinline__ void grouped_body(const GroupedArgs& a, const char* w
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(256) void grouped16_kernel(GroupedArgs a, const char* ws, int max_mtiles, int tiles_n) {
-    __shared__ __attribute__((aligned(1024))) char smem[2 * (GBM + GBN) * core16::KSTEP * 2];
+    __shared__ __attribute__((aligned(1024))) char s0[(GBM + GBN) * core16::KSTEP * 2];
+    __shared__ __attribute__((aligned(1024))) char s1[(GBM + GBN) * core16::KSTEP * 2];
     const int total = max_mtiles * tiles_n;
     const int w = xcd_remap((int)blockIdx.x, total);
     int tm, tn;
     grouped_order(w, max_mtiles, tiles_n, 4, tm, tn);
     const int ntiles = ((const int*)ws)[0];
     if (tm >= ntiles) return;
-    const int rows = ((const int4*)(ws + off_tiles()))[tm].z;
-    if (!VEC)
-        grouped_body<DT, 2>(a, ws, tm, tn, smem);
-    else if (rows == GBM && (int64_t)(tn + 1) * GBN <= a.N && a.K % core16::KSTEP == 0)
-        grouped_body<DT, 0>(a, ws, tm, tn, smem);
-    else
-        grouped_body<DT, 1>(a, ws, tm, tn, smem);
+    grouped_body<DT, VEC>(a, ws, tm, tn, s0, s1);
 }
 
 // fp32: one workgroup per (pair, 256 columns); plain fp32 dot products.
@@ -242,7 +300,16 @@ size_t grouped_workspace_bytes(int64_t M, int64_t S, int64_t G) {
 hipError_t launch_grouped(const GroupedArgs& a, int dt, void* ws, hipStream_t s) {
     const int64_t P = a.M * a.S;
     if (a.G > MAX_G || P > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(route_kernel, dim3(1), dim3(ROUTE_THREADS), 0, s, a.idx, a.idx64, P, (int)a.G, GBM, (char*)ws);
+    char* w = (char*)ws;
+    const unsigned nchunk = (unsigned)((P + ROUTE_CHUNK - 1) / ROUTE_CHUNK);
+    hipLaunchKernelGGL(route_zero_kernel, dim3(1), dim3(256), 0, s, w, (int)a.G);
+    if (nchunk) {
+        hipLaunchKernelGGL(route_hist_kernel, dim3(nchunk), dim3(256), 0, s, a.idx, a.idx64, P, (int)a.G, w);
+    }
+    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(ROUTE_THREADS), 0, s, P, (int)a.G, GBM, w);
+    if (nchunk) {
+        hipLaunchKernelGGL(route_scatter_kernel, dim3(nchunk), dim3(256), 0, s, a.idx, a.idx64, P, (int)a.G, w);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (P == 0 || a.N == 0) return hipSuccess;
@@ -256,8 +323,9 @@ hipError_t launch_grouped(const GroupedArgs& a, int dt, void* ws, hipStream_t s)
     const int64_t tiles_n = (a.N + GBN - 1) / GBN;
     if (max_mtiles * tiles_n > 0x7fffffff) return hipErrorInvalidValue;
     auto al16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
+    // DMA offsets are 32-bit: the gathered input and one k-stage of a group's weights must span < 2 GiB
     const bool vec = al16(a.input) && al16(a.weights) && ((uintptr_t)a.output & 7) == 0 && a.K % 8 == 0 &&
-                     a.N % 8 == 0;
+                     a.N % 8 == 0 && a.M * a.K * 2 < (1LL << 31) && 64 * a.N * 2 < (1LL << 31);
     dim3 grid((unsigned)(max_mtiles * tiles_n));
     const char* wsc = (const char*)ws;
     if (dt == 0) {

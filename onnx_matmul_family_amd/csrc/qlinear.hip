@@ -18,7 +18,7 @@
 // of 128 bytes, double-buffered LDS.  a (k contiguous) is stored as swizzled
 // 128-byte rows and read with ds_read_b128; b (n contiguous) is copied as is
 // (swizzled 16-byte chunks) and read with the transposing ds_read_b64_tr_b8.
-#include "device_common.hpp"
+#include "gemm16_core.hpp"
 #include "kernels.hpp"
 
 namespace omm {
@@ -120,8 +120,8 @@ __device__ __forceinline__ int dot4sum(i32x4_t v, int acc) {
 
 template <bool AU8, bool BU8, int MODE>
 __device__ __forceinline__ void qloop(i32x16_t (&acc)[4][4], int (&rs)[4], int (&cs)[4], char* smem,
-                                      const QSrc<true, AU8>& sa, const QSrc<false, BU8>& sb, int nk, int t, int lane,
-                                      int wm, int wn) {
+                                      char* smem1, const QSrc<true, AU8>& sa, const QSrc<false, BU8>& sb, int nk, int t,
+                                      int lane, int wm, int wn) {
     u32x4_t ra[NC], rb[NC];
     if (nk > 0) {
         sa.template load<MODE>(ra, 0);
@@ -135,7 +135,7 @@ __device__ __forceinline__ void qloop(i32x16_t (&acc)[4][4], int (&rs)[4], int (
             sa.template load<MODE>(ra, kt + 1);
             sb.template load<MODE>(rb, kt + 1);
         }
-        const char* s = smem + buf * STAGE;
+        const char* s = buf ? smem1 : smem;
 #pragma unroll
         for (int ks = 0; ks < KB / 32; ++ks) {
             i32x4_t af[4], bf[4];
@@ -153,8 +153,95 @@ __device__ __forceinline__ void qloop(i32x16_t (&acc)[4][4], int (&rs)[4], int (
 #pragma unroll
             for (int j = 0; j < 4; ++j) cs[j] = dot4sum(bf[j], cs[j]);
         }
-        if (kt + 1 < nk) stash(smem + (buf ^ 1) * STAGE, ra, rb, t);
+        if (kt + 1 < nk) stash(buf ? smem : smem1, ra, rb, t);
         __syncthreads();
+    }
+}
+
+// int8 MFMA operand fragments of one 32-value k-block (uint8 operands flipped
+// to int8 here: the DMA copies raw bytes).
+template <bool AU8, bool BU8>
+struct QFrags {
+    i32x4_t a[4], b[4];
+    __device__ __forceinline__ void read(const char* st, int ks, int lane, int wm, int wn) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            a[i] = frag_a(st, wm * 128 + 32 * i, ks, lane);
+            if (AU8) a[i] ^= (int)0x80808080;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            b[j] = frag_b(st, wn * 128 + 32 * j, ks, lane);
+            if (BU8) b[j] ^= (int)0x80808080;
+        }
+    }
+};
+
+template <class F>
+__device__ __forceinline__ void q_step(i32x16_t (&acc)[4][4], int (&rs)[4], int (&cs)[4], const F& f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rs[i] = dot4sum(f.a[i], rs[i]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cs[j] = dot4sum(f.b[j], cs[j]);
+}
+
+// One stage of the DMA loop; same schedule as the bf16 core (fragments one
+// k-block ahead, stage kt+2's DMA issued after the barrier retiring stage kt).
+template <bool CHECKED, class SA, class SB, class F>
+__device__ __forceinline__ void q_stage(i32x16_t (&acc)[4][4], int (&rs)[4], int (&cs)[4], F& fc, F& fn, char* X,
+                                        char* Y, const SA& sa, const SB& sb, int kt, int nk, int lane, int wm, int wn,
+                                        int wave) {
+    using namespace core16;
+    fence_sched();
+    fn.read(X, 1, lane, wm, wn);
+    fence_sched();
+    q_step(acc, rs, cs, fc);
+    fence_sched();
+    fc.read(X, 2, lane, wm, wn);
+    fence_sched();
+    q_step(acc, rs, cs, fn);
+    fence_sched();
+    fn.read(X, 3, lane, wm, wn);
+    fence_sched();
+    q_step(acc, rs, cs, fc);
+    fence_sched();
+    if (kt + 1 < nk) wait_vm<0>();
+    __syncthreads();
+    if (kt + 1 < nk) fc.read(Y, 0, lane, wm, wn);
+    if (kt + 2 < nk) {
+        sa.template issue<CHECKED>(X, kt + 2, wave);
+        sb.template issue<CHECKED>(X + A_BYTES, kt + 2, wave);
+    }
+    fence_sched();
+    q_step(acc, rs, cs, fn);
+}
+
+template <bool AU8, bool BU8, bool CHECKED, class SA, class SB>
+__device__ __forceinline__ void qloop_dma(i32x16_t (&acc)[4][4], int (&rs)[4], int (&cs)[4], char* __restrict__ s0,
+                                          char* __restrict__ s1, const SA& sa, const SB& sb, int nk, int lane, int wm,
+                                          int wn, int wave) {
+    using namespace core16;
+    constexpr int LOADS = SA::PER_WAVE + SB::PER_WAVE;
+    if (nk <= 0) return;
+    sa.template issue<CHECKED>(s0, 0, wave);
+    sb.template issue<CHECKED>(s0 + A_BYTES, 0, wave);
+    if (nk > 1) {
+        sa.template issue<CHECKED>(s1, 1, wave);
+        sb.template issue<CHECKED>(s1 + A_BYTES, 1, wave);
+        wait_vm<LOADS>();
+    } else {
+        wait_vm<0>();
+    }
+    __syncthreads();
+    QFrags<AU8, BU8> fc, fn;
+    fc.read(s0, 0, lane, wm, wn);
+    for (int kt = 0; kt < nk; kt += 2) {
+        q_stage<CHECKED>(acc, rs, cs, fc, fn, s0, s1, sa, sb, kt, nk, lane, wm, wn, wave);
+        if (kt + 1 < nk) q_stage<CHECKED>(acc, rs, cs, fc, fn, s1, s0, sa, sb, kt + 1, nk, lane, wm, wn, wave);
     }
 }
 
@@ -164,7 +251,8 @@ __device__ __forceinline__ int ldzp(const void* p, int64_t i, bool u8) {
 
 template <bool AU8, bool BU8, bool VEC>
 __global__ __launch_bounds__(NT) void qlinear_kernel(QArgs p, int tiles_m, int tiles_n) {
-    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) char smem[STAGE];
+    __shared__ __attribute__((aligned(1024))) char smem1[STAGE];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int T = tiles_m * tiles_n;
@@ -188,17 +276,23 @@ __global__ __launch_bounds__(NT) void qlinear_kernel(QArgs p, int tiles_m, int t
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
     int rs[4] = {0, 0, 0, 0}, cs[4] = {0, 0, 0, 0};
 
-    QSrc<true, AU8> sa;
-    QSrc<false, BU8> sb;
-    sa.init(a, p.lda, m0, M, K, t);
-    sb.init(b, p.ldb, n0, N, K, t);
     const int nk = (int)((K + KB - 1) / KB);
-    if (!VEC)
-        qloop<AU8, BU8, 2>(acc, rs, cs, smem, sa, sb, nk, t, lane, wm, wn);
-    else if (m0 + BMQ <= M && n0 + BNQ <= N && K % KB == 0)
-        qloop<AU8, BU8, 0>(acc, rs, cs, smem, sa, sb, nk, t, lane, wm, wn);
-    else
-        qloop<AU8, BU8, 1>(acc, rs, cs, smem, sa, sb, nk, t, lane, wm, wn);
+    if constexpr (VEC) {
+        core16::DmaSrc<BMQ, true, 1> sa;
+        core16::DmaSrcMN8<BNQ> sb;
+        sa.init(a, p.lda, m0, M, K, lane);
+        sb.init(b, p.ldb, n0, N, K, lane);
+        if (m0 + BMQ <= M && n0 + BNQ <= N && K % KB == 0)
+            qloop_dma<AU8, BU8, false>(acc, rs, cs, smem, smem1, sa, sb, nk, lane, wm, wn, wave);
+        else
+            qloop_dma<AU8, BU8, true>(acc, rs, cs, smem, smem1, sa, sb, nk, lane, wm, wn, wave);
+    } else {
+        QSrc<true, AU8> sa;
+        QSrc<false, BU8> sb;
+        sa.init(a, p.lda, m0, M, K, t);
+        sb.init(b, p.ldb, n0, N, K, t);
+        qloop<AU8, BU8, 2>(acc, rs, cs, smem, smem1, sa, sb, nk, t, lane, wm, wn);
+    }
 
     // full row / column sums: lanes l and l^32 hold the two k-halves
     int* rowsum = (int*)smem;        // 256 tile rows
@@ -324,7 +418,10 @@ hipError_t launch_qlinear(const QArgs& a, hipStream_t s) {
     auto al16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
     const bool vec = al16(a.a) && al16(a.b) && ((uintptr_t)a.y & 3) == 0 && a.lda % 16 == 0 && a.ldb % 16 == 0 &&
                      a.K % 16 == 0 && a.N % 16 == 0 && a.a_bs0 % 16 == 0 && a.a_bs1 % 16 == 0 &&
-                     a.b_bs0 % 16 == 0 && a.b_bs1 % 16 == 0 && a.y_bs0 % 4 == 0 && a.y_bs1 % 4 == 0;
+                     a.b_bs0 % 16 == 0 && a.b_bs1 % 16 == 0 && a.y_bs0 % 4 == 0 && a.y_bs1 % 4 == 0 &&
+                     256 * a.lda < (1LL << 31) && 128 * a.ldb < (1LL << 31) &&
+                     // the DMA path zero-pads a K tail in LDS; a flipped uint8 zero would not be zero
+                     (a.K % KB == 0 || (!a.a_u8 && !a.b_u8));
     return vec ? launch_q_types<true>(a, s) : launch_q_types<false>(a, s);
 }
 
