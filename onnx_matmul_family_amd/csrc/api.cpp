@@ -8,7 +8,7 @@
 #include <algorithm>
 #include <vector>
 
-#include "../../include/omm.h"
+#include "omm.h"
 #include "kernels.hpp"
 
 using omm::DenseArgs;

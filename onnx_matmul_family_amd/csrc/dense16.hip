@@ -14,6 +14,100 @@ namespace {
 
 using namespace core16;
 
+// Y = alpha * acc + beta * C.  A C that does not vary along m (bias vector or
+// scalar) is loaded once per lane for all its columns before any store, so the
+// loads are in flight together; a C that varies along m is loaded per row block.
+template <int BM, int BN, int DT, bool VEC>
+__device__ __forceinline__ void epilogue16(const DenseArgs& p, const f32x16_t (&acc)[BM / 64][BN / 64],
+                                           uint16_t* __restrict__ Y, int64_t m0, int64_t n0, int lane, int wm,
+                                           int wn) {
+    constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+    const float alpha = p.alpha, beta = p.beta;
+    const int64_t M = p.M, N = p.N;
+    const uint16_t* __restrict__ Cp = (const uint16_t*)p.C;
+    const bool vec_store = VEC && (N % 4 == 0) && (p.ldy % 4 == 0);
+    const bool c_cols = Cp && p.c_sm == 0;  // C constant along m
+    const int64_t nl = n0 + wn * WN + 4 * (lane >> 5);
+    const int64_t ml = m0 + wm * WM + (lane & 31);
+
+    // beta * C for the lane's columns: once for a C constant along m, per row
+    // block otherwise
+    float cb[TN][4][4];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cb[j][q][e] = 0.0f;
+    if (c_cols) {
+        const bool c_vec = VEC && p.c_sn == 1 && (N % 4 == 0) && (((uintptr_t)Cp & 7) == 0);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t n = nl + 32 * j + 8 * q;
+                if (c_vec && n < N) {
+                    const u32x2_t c2 = *(const u32x2_t*)(Cp + n);
+                    cb[j][q][0] = from_bits<DT>((uint16_t)c2.x);
+                    cb[j][q][1] = from_bits<DT>((uint16_t)(c2.x >> 16));
+                    cb[j][q][2] = from_bits<DT>((uint16_t)c2.y);
+                    cb[j][q][3] = from_bits<DT>((uint16_t)(c2.y >> 16));
+                } else if (!c_vec) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) cb[j][q][e] = from_bits<DT>(Cp[(n + e) * p.c_sn]);
+                }
+            }
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) cb[j][q][e] *= beta;
+    }
+
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int64_t m = ml + 32 * i;
+        if (m >= M) continue;
+        uint16_t* __restrict__ yr = Y + m * p.ldy;
+        // a C that varies along m: this row block's values, all loads first
+        if (Cp && !c_cols) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int64_t n = nl + 32 * j + 8 * q + e;
+                        cb[j][q][e] = n < N ? beta * from_bits<DT>(Cp[m * p.c_sm + n * p.c_sn]) : 0.0f;
+                    }
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t n = nl + 32 * j + 8 * q;
+                if (n >= N) continue;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[e] = alpha * acc[i][j][4 * q + e] + cb[j][q][e];
+                if (vec_store) {
+                    u32x2_t o;
+                    o.x = (uint32_t)to_bits<DT>(v[0]) | ((uint32_t)to_bits<DT>(v[1]) << 16);
+                    o.y = (uint32_t)to_bits<DT>(v[2]) | ((uint32_t)to_bits<DT>(v[3]) << 16);
+                    *(u32x2_t*)(yr + n) = o;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) yr[n + e] = to_bits<DT>(v[e]);
+                }
+            }
+        }
+    }
+}
+
 template <int BM, int BN, int DT, bool AK, bool BKM, bool VEC>
 __global__ __launch_bounds__(NT) void dense16_kernel(DenseArgs p, int tiles_m, int tiles_n) {
     constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
@@ -62,41 +156,9 @@ __global__ __launch_bounds__(NT) void dense16_kernel(DenseArgs p, int tiles_m, i
         mainloop<BM, BN, DT, AK, BKM, 2>(acc, smem0, smem1, srcA, srcB, nk, t, lane, wm, wn);
     }
 
-    // epilogue: lane holds, for each (i, j, q), row m and the 4 columns n..n+3
-    const float alpha = p.alpha, beta = p.beta;
-    const uint16_t* __restrict__ Cp = (const uint16_t*)p.C;
-    const bool vec_store = VEC && (N % 4 == 0) && (p.ldy % 4 == 0);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int64_t m = m0 + wm * WM + 32 * i + (lane & 31);
-        if (m >= M) continue;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t n = n0 + wn * WN + 32 * j + 8 * q + 4 * (lane >> 5);
-                if (n >= N) continue;
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float x = alpha * acc[i][j][4 * q + e];
-                    if (Cp && n + e < N) x += beta * from_bits<DT>(Cp[m * p.c_sm + (n + e) * p.c_sn]);
-                    v[e] = x;
-                }
-                uint16_t* yr = Y + m * p.ldy + n;
-                if (vec_store) {
-                    u32x2_t o;
-                    o.x = (uint32_t)to_bits<DT>(v[0]) | ((uint32_t)to_bits<DT>(v[1]) << 16);
-                    o.y = (uint32_t)to_bits<DT>(v[2]) | ((uint32_t)to_bits<DT>(v[3]) << 16);
-                    *(u32x2_t*)yr = o;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (n + e < N) yr[e] = to_bits<DT>(v[e]);
-                }
-            }
-        }
-    }
+    // Epilogue: for each (i, j, q) a lane holds row m = m0 + wm*WM + 32 i + l%32 and
+    // the 4 columns n .. n+3, n = n0 + wn*WN + 32 j + 8 q + 4 (l/32).
+    epilogue16<BM, BN, DT, VEC>(p, acc, Y, m0, n0, lane, wm, wn);
 }
 
 template <int BM, int BN, int DT, bool AK, bool BKM, bool VEC>

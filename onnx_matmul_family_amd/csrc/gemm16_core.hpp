@@ -12,6 +12,8 @@
 // with m/n contiguous are copied as they are (swizzled 32-byte granules) and
 // read with the transposing ds_read_b64_tr_b16, so no register transpose.
 #pragma once
+#include <type_traits>
+
 #include "device_common.hpp"
 
 namespace omm {
@@ -236,11 +238,12 @@ __device__ __forceinline__ void mainloop(f32x16_t (&acc)[BM / 64][BN / 64], char
 // rows must span less than 2 GiB (checked on the host).
 constexpr uint32_t DMA_OOB = 0x80000000u;
 
-// Raw buffer resource (gfx9 family): base, stride 0, 2^31-1 bytes in range.
-__device__ __forceinline__ i32x4_t make_rsrc(const void* base) {
+// Raw buffer resource (gfx9 family): base, stride 0, 2^31-1 bytes in range, or
+// an empty range (every access out of range: no memory access, zeros into LDS).
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, bool live = true) {
     const uint64_t a = (uint64_t)base;
     return i32x4_t{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
-                   __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)), 0x7fffffff, 0x00020000};
+                   __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)), live ? 0x7fffffff : 0, 0x00020000};
 }
 __device__ __forceinline__ uint32_t lds_addr(const char* p) {
     return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)OMM_LDS(const char, p));
@@ -263,6 +266,11 @@ __device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t lds, uint32_t voff)
 __device__ __forceinline__ void dma16u(i32x4_t rsrc, uint32_t lds, uint32_t voff) {
     dma16(rsrc, (uint32_t)__builtin_amdgcn_readfirstlane((int)lds), voff);
 }
+// buffer resource and LDS base of one stage's DMA
+struct DmaCtx {
+    i32x4_t r;
+    uint32_t l0;
+};
 
 // One operand tile (R rows along m/n, 128 bytes of k per stage) loaded by DMA.
 // ES = element size in bytes (2: bf16/fp16, 1: int8; MN-major needs ES = 2).
@@ -309,12 +317,19 @@ struct DmaSrc {
         return (uint32_t)(2 * ((C >> 1) ^ mswz16(row)) + (C & 1));
     }
 
+    __device__ __forceinline__ DmaCtx ctx(char* lds, int kt, bool live = true) const {
+        return DmaCtx{make_rsrc(base + (live ? (int64_t)kt * step : 0), live), lds_addr(lds)};
+    }
     template <bool CHECKED>
-    __device__ __forceinline__ void issue(char* lds, int kt, int wave) const {
-        const i32x4_t r = make_rsrc(base + (int64_t)kt * step);
-        const uint32_t l0 = lds_addr(lds);
+    __device__ __forceinline__ void issue(char* lds, int kt, int wave, bool live = true) const {
+        const DmaCtx c = ctx(lds, kt, live);
 #pragma unroll
-        for (int j = 0; j < PER_WAVE; ++j) {
+        for (int j = 0; j < PER_WAVE; ++j) one<CHECKED>(c, kt, wave, j);
+    }
+    // block j (0 .. PER_WAVE-1) of this wave's share of stage kt
+    template <bool CHECKED>
+    __device__ __forceinline__ void one(const DmaCtx& c, int kt, int wave, int j) const {
+        {
             const int b = wave * PER_WAVE + j;
             uint32_t voff;
             if constexpr (KMAJ) {
@@ -333,7 +348,7 @@ struct DmaSrc {
                     if (!(k < K && mn < MN)) voff = DMA_OOB;
                 }
             }
-            dma16u(r, l0 + b * 1024, voff);
+            dma16u(c.r, c.l0 + b * 1024, voff);
         }
     }
 };
@@ -367,21 +382,25 @@ struct DmaSrcMN8 {
 #pragma unroll
         for (int q = 0; q < 2; ++q) lane_off[q] = (uint32_t)(lane >> 4) * ldb + (chunk(q) << 4);
     }
+    __device__ __forceinline__ DmaCtx ctx(char* lds, int kt, bool live = true) const {
+        return DmaCtx{make_rsrc(base + (live ? (int64_t)kt * step : 0), live), lds_addr(lds)};
+    }
     template <bool CHECKED>
-    __device__ __forceinline__ void issue(char* lds, int kt, int wave) const {
-        const i32x4_t r = make_rsrc(base + (int64_t)kt * step);
-        const uint32_t l0 = lds_addr(lds);
+    __device__ __forceinline__ void issue(char* lds, int kt, int wave, bool live = true) const {
+        const DmaCtx c = ctx(lds, kt, live);
 #pragma unroll
-        for (int j = 0; j < PER_WAVE; ++j) {
-            const int b = wave * PER_WAVE + j;
-            uint32_t voff = lane_off[j & 1] + (uint32_t)(b * 4) * ldb;
-            if (CHECKED) {
-                const int64_t k = (int64_t)kt * 128 + b * 4 + (lane >> 4);
-                const int64_t mn = mn0 + 16 * (int64_t)chunk(j & 1);
-                if (!(k < K && mn < MN)) voff = DMA_OOB;
-            }
-            dma16u(r, l0 + b * 1024, voff);
+        for (int j = 0; j < PER_WAVE; ++j) one<CHECKED>(c, kt, wave, j);
+    }
+    template <bool CHECKED>
+    __device__ __forceinline__ void one(const DmaCtx& c, int kt, int wave, int j) const {
+        const int b = wave * PER_WAVE + j;
+        uint32_t voff = lane_off[j & 1] + (uint32_t)(b * 4) * ldb;
+        if (CHECKED) {
+            const int64_t k = (int64_t)kt * 128 + b * 4 + (lane >> 4);
+            const int64_t mn = mn0 + 16 * (int64_t)chunk(j & 1);
+            if (!(k < K && mn < MN)) voff = DMA_OOB;
         }
+        dma16u(c.r, c.l0 + b * 1024, voff);
     }
 };
 
@@ -397,21 +416,25 @@ struct GatherDma {
     int64_t K;
     int lane;
 
+    __device__ __forceinline__ DmaCtx ctx(char* lds, int kt, bool live = true) const {
+        return DmaCtx{make_rsrc(base + (live ? (int64_t)kt * KSTEP * 2 : 0), live), lds_addr(lds)};
+    }
     template <bool CHECKED>
-    __device__ __forceinline__ void issue(char* lds, int kt, int wave) const {
-        const i32x4_t r = make_rsrc(base + (int64_t)kt * KSTEP * 2);
-        const uint32_t l0 = lds_addr(lds);
+    __device__ __forceinline__ void issue(char* lds, int kt, int wave, bool live = true) const {
+        const DmaCtx c = ctx(lds, kt, live);
 #pragma unroll
-        for (int j = 0; j < PER_WAVE; ++j) {
-            const int b = wave * PER_WAVE + j;
-            const int s = b / (R / 32), rb = b % (R / 32);
-            uint32_t voff = roff[rb] + (uint32_t)(s * 32);
-            if (CHECKED) {
-                const int64_t k = (int64_t)kt * KSTEP + 8 * (2 * s + ((lane & 1) ^ kswz(lane >> 1)));
-                if (k >= K) voff = DMA_OOB;
-            }
-            dma16u(r, l0 + b * 1024, voff);
+        for (int j = 0; j < PER_WAVE; ++j) one<CHECKED>(c, kt, wave, j);
+    }
+    template <bool CHECKED>
+    __device__ __forceinline__ void one(const DmaCtx& c, int kt, int wave, int j) const {
+        const int b = wave * PER_WAVE + j;
+        const int s = b / (R / 32), rb = b % (R / 32);
+        uint32_t voff = roff[rb] + (uint32_t)(s * 32);
+        if (CHECKED) {
+            const int64_t k = (int64_t)kt * KSTEP + 8 * (2 * s + ((lane & 1) ^ kswz(lane >> 1)));
+            if (k >= K) voff = DMA_OOB;
         }
+        dma16u(c.r, c.l0 + b * 1024, voff);
     }
 };
 
@@ -425,6 +448,15 @@ struct Frags {
         for (int i = 0; i < TM; ++i) a[i] = read_frag<BM, AK>(st, wm * (BM / 2) + 32 * i, s, lane);
 #pragma unroll
         for (int j = 0; j < TN; ++j) b[j] = read_frag<BN, BKM>(st + A_BYTES, wn * (BN / 2) + 32 * j, s, lane);
+    }
+    // fragment R of k-block s: R < TM -> a[R], else b[R - TM]
+    template <int R>
+    __device__ __forceinline__ void read_one(const char* st, int s, int lane, int wm, int wn) {
+        constexpr int A_BYTES = BM * KSTEP * 2;
+        if constexpr (R < TM)
+            a[R] = read_frag<BM, AK>(st, wm * (BM / 2) + 32 * R, s, lane);
+        else
+            b[R - TM] = read_frag<BN, BKM>(st + A_BYTES, wn * (BN / 2) + 32 * (R - TM), s, lane);
     }
 };
 
@@ -445,42 +477,93 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
 }
 
+// Compile-time loop: f(integral_constant<int, I>) for I = B .. E-1, so every
+// register-array index below is a constant.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// MFMA number X (0 .. TM*TN-1) of a k-block: tile (X / TN, X % TN).
+template <int X, int DT, int TM, int TN, class F>
+__device__ __forceinline__ void mma_one(f32x16_t (&acc)[TM][TN], const F& f) {
+    acc[X / TN][X % TN] = mfma32x32x16<DT>(f.b[X % TN], f.a[X / TN], acc[X / TN][X % TN]);
+}
+
+// One k-block of MFMAs on `cur`, with the TM+TN fragment reads of k-block s of
+// `lds` into `nxt` spread evenly between them (read r after MFMA r*NM/NR), so
+// the LDS sees a steady stream instead of bursts.
+template <int DT, int TM, int TN, class F>
+__device__ __forceinline__ void kblock_read(f32x16_t (&acc)[TM][TN], const F& cur, F& nxt, const char* lds, int s,
+                                            int lane, int wm, int wn) {
+    constexpr int NM = TM * TN, NR = TM + TN;
+    static_for<0, NM>([&](auto xc) {
+        constexpr int x = decltype(xc)::value;
+        mma_one<x, DT>(acc, cur);
+        static_for<(x * NR + NM - 1) / NM, ((x + 1) * NR + NM - 1) / NM>([&](auto rc) {
+            nxt.template read_one<decltype(rc)::value>(lds, s, lane, wm, wn);
+        });
+        fence_sched();
+    });
+}
+
+// The k-block after the barrier: MFMAs on `cur`, interleaved with the reads of
+// the next stage's k-block 0 (from Y) and this wave's DMA of stage kt+2 (into X).
+template <int DT, int TM, int TN, bool CHECKED, class F, class SA, class SB>
+__device__ __forceinline__ void kblock_read_dma(f32x16_t (&acc)[TM][TN], const F& cur, F& nxt, const char* Y, char* X,
+                                                int A_BYTES, const SA& srcA, const SB& srcB, int kt2, bool live,
+                                                int lane, int wm, int wn, int wave) {
+    constexpr int NM = TM * TN, NR = TM + TN;
+    constexpr int LA = SA::PER_WAVE, LD = SA::PER_WAVE + SB::PER_WAVE;
+    const DmaCtx ca = srcA.ctx(X, kt2, live), cb = srcB.ctx(X + A_BYTES, kt2, live);
+    static_for<0, NM>([&](auto xc) {
+        constexpr int x = decltype(xc)::value;
+        static_for<(x * LD + NM - 1) / NM, ((x + 1) * LD + NM - 1) / NM>([&](auto dc) {
+            constexpr int d = decltype(dc)::value;
+            if constexpr (d < LA)
+                srcA.template one<CHECKED>(ca, kt2, wave, d);
+            else
+                srcB.template one<CHECKED>(cb, kt2, wave, d - LA);
+        });
+        mma_one<x, DT>(acc, cur);
+        static_for<(x * NR + NM - 1) / NM, ((x + 1) * NR + NM - 1) / NM>([&](auto rc) {
+            nxt.template read_one<decltype(rc)::value>(Y, 0, lane, wm, wn);
+        });
+        fence_sched();
+    });
+}
+
 // One stage of the DMA K loop: stage kt is complete in X (barrier passed),
 // fc holds its k-block 0 fragments (requested), stage kt+1 is in flight into Y.
 // The fragments of k-block s+1 are read while k-block s's MFMAs run; stage
-// kt+2's DMA is issued right after the barrier that retires stage kt.
+// kt+2's DMA is issued right after the barrier that retires stage kt, spread
+// over the MFMAs of the last k-block.  Past the last stage the DMA targets an
+// empty range (zeros into a buffer no later stage reads) and the reads of Y
+// fetch values nobody uses: the stage has no data-dependent branches, so the
+// accumulators flow through straight-line code.
 template <int BM, int BN, int DT, bool AK, bool BKM, bool CHECKED, class SA, class SB, class F>
 __device__ __forceinline__ void dma_stage(f32x16_t (&acc)[BM / 64][BN / 64], F& fc, F& fn, char* X, char* Y,
                                           const SA& srcA, const SB& srcB, int kt, int nk, int lane, int wm, int wn,
                                           int wave) {
     constexpr int A_BYTES = BM * KSTEP * 2;
     fence_sched();
-    fn.read(X, 1, lane, wm, wn);
+    kblock_read<DT>(acc, fc, fn, X, 1, lane, wm, wn);
+    kblock_read<DT>(acc, fn, fc, X, 2, lane, wm, wn);
+    kblock_read<DT>(acc, fc, fn, X, 3, lane, wm, wn);
+    wait_vm<0>();     // this wave's DMA of stage kt+1 has landed
+    __syncthreads();  // ... every wave's; and every read of X is done
     fence_sched();
-    mma_step<DT>(acc, fc);
-    fence_sched();
-    fc.read(X, 2, lane, wm, wn);
-    fence_sched();
-    mma_step<DT>(acc, fn);
-    fence_sched();
-    fn.read(X, 3, lane, wm, wn);
-    fence_sched();
-    mma_step<DT>(acc, fc);
-    fence_sched();
-    if (kt + 1 < nk) wait_vm<0>();  // stage kt+1 has landed (this wave's part)
-    __syncthreads();                 // ... for every wave; and every read of X is done
-    if (kt + 1 < nk) fc.read(Y, 0, lane, wm, wn);
-    if (kt + 2 < nk) {
-        srcA.template issue<CHECKED>(X, kt + 2, wave);
-        srcB.template issue<CHECKED>(X + A_BYTES, kt + 2, wave);
-    }
-    fence_sched();
-    mma_step<DT>(acc, fn);
+    kblock_read_dma<DT, BM / 64, BN / 64, CHECKED>(acc, fn, fc, Y, X, A_BYTES, srcA, srcB, kt + 2, kt + 2 < nk, lane,
+                                                  wm, wn, wave);
 }
 
 // DMA K loop over nk stages; stage kt lives in buffer kt & 1 (s0 / s1).  The
 // loop body covers two stages so that each LDS access names its buffer
-// statically.
+// statically; an odd stage count runs one more stage of zeros.  On return no
+// DMA is in flight.
 template <int BM, int BN, int DT, bool AK, bool BKM, bool CHECKED, class SA, class SB>
 __device__ __forceinline__ void mainloop_dma(f32x16_t (&acc)[BM / 64][BN / 64], char* __restrict__ s0,
                                              char* __restrict__ s1, const SA& srcA, const SB& srcB, int nk, int lane,
@@ -490,21 +573,17 @@ __device__ __forceinline__ void mainloop_dma(f32x16_t (&acc)[BM / 64][BN / 64], 
     if (nk <= 0) return;
     srcA.template issue<CHECKED>(s0, 0, wave);
     srcB.template issue<CHECKED>(s0 + A_BYTES, 0, wave);
-    if (nk > 1) {
-        srcA.template issue<CHECKED>(s1, 1, wave);
-        srcB.template issue<CHECKED>(s1 + A_BYTES, 1, wave);
-        wait_vm<LOADS>();
-    } else {
-        wait_vm<0>();
-    }
+    srcA.template issue<CHECKED>(s1, 1, wave, nk > 1);
+    srcB.template issue<CHECKED>(s1 + A_BYTES, 1, wave, nk > 1);
+    wait_vm<LOADS>();
     __syncthreads();
     Frags<BM, BN, AK, BKM> fc, fn;
     fc.read(s0, 0, lane, wm, wn);
     for (int kt = 0; kt < nk; kt += 2) {
         dma_stage<BM, BN, DT, AK, BKM, CHECKED>(acc, fc, fn, s0, s1, srcA, srcB, kt, nk, lane, wm, wn, wave);
-        if (kt + 1 < nk)
-            dma_stage<BM, BN, DT, AK, BKM, CHECKED>(acc, fc, fn, s1, s0, srcA, srcB, kt + 1, nk, lane, wm, wn, wave);
+        dma_stage<BM, BN, DT, AK, BKM, CHECKED>(acc, fc, fn, s1, s0, srcA, srcB, kt + 1, nk, lane, wm, wn, wave);
     }
+    wait_vm<0>();
 }
 
 }  // namespace core16

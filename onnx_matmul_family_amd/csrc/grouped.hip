@@ -216,36 +216,60 @@ __device__ __forceinline__ void grouped_body(const GroupedArgs& a, const char* w
         mainloop<GBM, GBN, DT, true, false, 2>(acc, s0, s1, srcA, srcB, nk, t, lane, wm, wn);
     }
 
-    const uint16_t* bias = a.bias ? (const uint16_t*)a.bias + (int64_t)g * N : nullptr;
-    uint16_t* out = (uint16_t*)a.output;
+    // Epilogue: + bias[g] (loaded once per lane for all its columns, before any
+    // store), one rounding, each row to output[pair].
+    const uint16_t* __restrict__ bias = a.bias ? (const uint16_t*)a.bias + (int64_t)g * N : nullptr;
+    uint16_t* __restrict__ out = (uint16_t*)a.output;
     const bool vec_store = VEC && (N % 4 == 0);
+    const int64_t nl = n0 + wn * 128 + 4 * (lane >> 5);
+    float bv[4][4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t n = nl + 32 * j + 8 * q;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bv[j][q][e] = 0.0f;
+            if (bias && vec_store && n < N) {
+                const u32x2_t b2 = *(const u32x2_t*)(bias + n);
+                bv[j][q][0] = from_bits<DT>((uint16_t)b2.x);
+                bv[j][q][1] = from_bits<DT>((uint16_t)(b2.x >> 16));
+                bv[j][q][2] = from_bits<DT>((uint16_t)b2.y);
+                bv[j][q][3] = from_bits<DT>((uint16_t)(b2.y >> 16));
+            } else if (bias) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < N) bv[j][q][e] = from_bits<DT>(bias[n + e]);
+            }
+        }
+    int orow[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = wm * 128 + 32 * i + (lane & 31);
-        if (r >= rows) continue;
-        uint16_t* orow = out + (int64_t)sorted[start + r] * N;
+        orow[i] = r < rows ? sorted[start + r] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (orow[i] < 0) continue;
+        uint16_t* __restrict__ yr = out + (int64_t)orow[i] * N;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int64_t n = n0 + wn * 128 + 32 * j + 8 * q + 4 * (lane >> 5);
+                const int64_t n = nl + 32 * j + 8 * q;
                 if (n >= N) continue;
                 float v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float x = acc[i][j][4 * q + e];
-                    if (bias && n + e < N) x += from_bits<DT>(bias[n + e]);
-                    v[e] = x;
-                }
+                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e] + bv[j][q][e];
                 if (vec_store) {
                     u32x2_t o;
                     o.x = (uint32_t)to_bits<DT>(v[0]) | ((uint32_t)to_bits<DT>(v[1]) << 16);
                     o.y = (uint32_t)to_bits<DT>(v[2]) | ((uint32_t)to_bits<DT>(v[3]) << 16);
-                    *(u32x2_t*)(orow + n) = o;
+                    *(u32x2_t*)(yr + n) = o;
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (n + e < N) orow[n + e] = to_bits<DT>(v[e]);
+                        if (n + e < N) yr[n + e] = to_bits<DT>(v[e]);
                 }
             }
         }

@@ -163,63 +163,84 @@ __device__ __forceinline__ void qloop(i32x16_t (&acc)[4][4], int (&rs)[4], int (
 template <bool AU8, bool BU8>
 struct QFrags {
     i32x4_t a[4], b[4];
+    template <int R>
+    __device__ __forceinline__ void read_one(const char* st, int ks, int lane, int wm, int wn) {
+        if constexpr (R < 4) {
+            a[R] = frag_a(st, wm * 128 + 32 * R, ks, lane);
+            if (AU8) a[R] ^= (int)0x80808080;
+        } else {
+            b[R - 4] = frag_b(st, wn * 128 + 32 * (R - 4), ks, lane);
+            if (BU8) b[R - 4] ^= (int)0x80808080;
+        }
+    }
     __device__ __forceinline__ void read(const char* st, int ks, int lane, int wm, int wn) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            a[i] = frag_a(st, wm * 128 + 32 * i, ks, lane);
-            if (AU8) a[i] ^= (int)0x80808080;
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            b[j] = frag_b(st, wn * 128 + 32 * j, ks, lane);
-            if (BU8) b[j] ^= (int)0x80808080;
-        }
+        core16::static_for<0, 8>([&](auto rc) { read_one<decltype(rc)::value>(st, ks, lane, wm, wn); });
     }
 };
 
+// MFMA X of a k-block (tile (X/4, X%4)) plus one dword of the row-sum and one
+// of the column-sum dot products, so the 32 sums ride along the 16 MFMAs.
+template <int X, class F>
+__device__ __forceinline__ void q_one(i32x16_t (&acc)[4][4], int (&rs)[4], int (&cs)[4], const F& f) {
+    acc[X / 4][X % 4] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.b[X % 4], f.a[X / 4], acc[X / 4][X % 4], 0, 0, 0);
+    rs[X / 4] = __builtin_amdgcn_sdot4(f.a[X / 4][X % 4], 0x01010101, rs[X / 4], false);
+    cs[X / 4] = __builtin_amdgcn_sdot4(f.b[X / 4][X % 4], 0x01010101, cs[X / 4], false);
+}
+
 template <class F>
-__device__ __forceinline__ void q_step(i32x16_t (&acc)[4][4], int (&rs)[4], int (&cs)[4], const F& f) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) rs[i] = dot4sum(f.a[i], rs[i]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) cs[j] = dot4sum(f.b[j], cs[j]);
+__device__ __forceinline__ void q_kblock(i32x16_t (&acc)[4][4], int (&rs)[4], int (&cs)[4], const F& cur, F& nxt,
+                                         const char* lds, int ks, int lane, int wm, int wn) {
+    using namespace core16;
+    static_for<0, 16>([&](auto xc) {
+        constexpr int x = decltype(xc)::value;
+        q_one<x>(acc, rs, cs, cur);
+        if constexpr ((x & 1) == 0) nxt.template read_one<x / 2>(lds, ks, lane, wm, wn);
+        fence_sched();
+    });
+}
+
+template <bool CHECKED, class F, class SA, class SB>
+__device__ __forceinline__ void q_kblock_dma(i32x16_t (&acc)[4][4], int (&rs)[4], int (&cs)[4], const F& cur, F& nxt,
+                                             const char* Y, char* X, const SA& sa, const SB& sb, int kt2, bool live,
+                                             int lane, int wm, int wn, int wave) {
+    using namespace core16;
+    constexpr int LA = SA::PER_WAVE, LD = SA::PER_WAVE + SB::PER_WAVE;  // 8 + 8
+    const DmaCtx ca = sa.ctx(X, kt2, live), cb = sb.ctx(X + A_BYTES, kt2, live);
+    static_for<0, 16>([&](auto xc) {
+        constexpr int x = decltype(xc)::value;
+        static_for<x * LD / 16, (x + 1) * LD / 16>([&](auto dc) {
+            constexpr int d = decltype(dc)::value;
+            if constexpr (d < LA)
+                sa.template one<CHECKED>(ca, kt2, wave, d);
+            else
+                sb.template one<CHECKED>(cb, kt2, wave, d - LA);
+        });
+        q_one<x>(acc, rs, cs, cur);
+        if constexpr ((x & 1) == 0) nxt.template read_one<x / 2>(Y, 0, lane, wm, wn);
+        fence_sched();
+    });
 }
 
 // One stage of the DMA loop; same schedule as the bf16 core (fragments one
-// k-block ahead, stage kt+2's DMA issued after the barrier retiring stage kt).
+// k-block ahead, stage kt+2's DMA spread over the k-block after the barrier,
+// no data-dependent branches).
 template <bool CHECKED, class SA, class SB, class F>
 __device__ __forceinline__ void q_stage(i32x16_t (&acc)[4][4], int (&rs)[4], int (&cs)[4], F& fc, F& fn, char* X,
                                         char* Y, const SA& sa, const SB& sb, int kt, int nk, int lane, int wm, int wn,
                                         int wave) {
     using namespace core16;
     fence_sched();
-    fn.read(X, 1, lane, wm, wn);
-    fence_sched();
-    q_step(acc, rs, cs, fc);
-    fence_sched();
-    fc.read(X, 2, lane, wm, wn);
-    fence_sched();
-    q_step(acc, rs, cs, fn);
-    fence_sched();
-    fn.read(X, 3, lane, wm, wn);
-    fence_sched();
-    q_step(acc, rs, cs, fc);
-    fence_sched();
-    if (kt + 1 < nk) wait_vm<0>();
+    q_kblock(acc, rs, cs, fc, fn, X, 1, lane, wm, wn);
+    q_kblock(acc, rs, cs, fn, fc, X, 2, lane, wm, wn);
+    q_kblock(acc, rs, cs, fc, fn, X, 3, lane, wm, wn);
+    wait_vm<0>();
     __syncthreads();
-    if (kt + 1 < nk) fc.read(Y, 0, lane, wm, wn);
-    if (kt + 2 < nk) {
-        sa.template issue<CHECKED>(X, kt + 2, wave);
-        sb.template issue<CHECKED>(X + A_BYTES, kt + 2, wave);
-    }
     fence_sched();
-    q_step(acc, rs, cs, fn);
+    q_kblock_dma<CHECKED>(acc, rs, cs, fn, fc, Y, X, sa, sb, kt + 2, kt + 2 < nk, lane, wm, wn, wave);
 }
 
+// An odd stage count runs one more stage of zeros (no effect on the products
+// or the sums).  On return no DMA is in flight and every wave is done with LDS.
 template <bool AU8, bool BU8, bool CHECKED, class SA, class SB>
 __device__ __forceinline__ void qloop_dma(i32x16_t (&acc)[4][4], int (&rs)[4], int (&cs)[4], char* __restrict__ s0,
                                           char* __restrict__ s1, const SA& sa, const SB& sb, int nk, int lane, int wm,
@@ -229,20 +250,18 @@ __device__ __forceinline__ void qloop_dma(i32x16_t (&acc)[4][4], int (&rs)[4], i
     if (nk <= 0) return;
     sa.template issue<CHECKED>(s0, 0, wave);
     sb.template issue<CHECKED>(s0 + A_BYTES, 0, wave);
-    if (nk > 1) {
-        sa.template issue<CHECKED>(s1, 1, wave);
-        sb.template issue<CHECKED>(s1 + A_BYTES, 1, wave);
-        wait_vm<LOADS>();
-    } else {
-        wait_vm<0>();
-    }
+    sa.template issue<CHECKED>(s1, 1, wave, nk > 1);
+    sb.template issue<CHECKED>(s1 + A_BYTES, 1, wave, nk > 1);
+    wait_vm<LOADS>();
     __syncthreads();
     QFrags<AU8, BU8> fc, fn;
     fc.read(s0, 0, lane, wm, wn);
     for (int kt = 0; kt < nk; kt += 2) {
         q_stage<CHECKED>(acc, rs, cs, fc, fn, s0, s1, sa, sb, kt, nk, lane, wm, wn, wave);
-        if (kt + 1 < nk) q_stage<CHECKED>(acc, rs, cs, fc, fn, s1, s0, sa, sb, kt + 1, nk, lane, wm, wn, wave);
+        q_stage<CHECKED>(acc, rs, cs, fc, fn, s1, s0, sa, sb, kt + 1, nk, lane, wm, wn, wave);
     }
+    wait_vm<0>();
+    __syncthreads();
 }
 
 __device__ __forceinline__ int ldzp(const void* p, int64_t i, bool u8) {
@@ -420,8 +439,9 @@ hipError_t launch_qlinear(const QArgs& a, hipStream_t s) {
                      a.K % 16 == 0 && a.N % 16 == 0 && a.a_bs0 % 16 == 0 && a.a_bs1 % 16 == 0 &&
                      a.b_bs0 % 16 == 0 && a.b_bs1 % 16 == 0 && a.y_bs0 % 4 == 0 && a.y_bs1 % 4 == 0 &&
                      256 * a.lda < (1LL << 31) && 128 * a.ldb < (1LL << 31) &&
-                     // the DMA path zero-pads a K tail in LDS; a flipped uint8 zero would not be zero
-                     (a.K % KB == 0 || (!a.a_u8 && !a.b_u8));
+                     // the DMA path zero-pads a K tail and an odd stage count in LDS, and a
+                     // flipped uint8 zero is not zero: uint8 needs an even number of full stages
+                     (a.K % (2 * KB) == 0 || (!a.a_u8 && !a.b_u8));
     return vec ? launch_q_types<true>(a, s) : launch_q_types<false>(a, s);
 }
 
