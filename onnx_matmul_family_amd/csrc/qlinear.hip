@@ -268,6 +268,76 @@ __device__ __forceinline__ int ldzp(const void* p, int64_t i, bool u8) {
     return u8 ? (int)((const uint8_t*)p)[i] - 128 : (int)((const int8_t*)p)[i];
 }
 
+// Requantisation of the lane's 4 x 64 outputs.  Per element:
+//   acc  = sum ab - zb * U[m] - za[m] * colsum[n]          (int32, mod 2^32)
+//   mult = fp32(fp32(sa[m] * sb[n]) / sy)                   (correctly rounded divide)
+//   y    = saturate(rint(fp32(acc) * mult) + zy)
+// rint(.) + zy and the saturation run in fp32: the sum is exact below 2^24 and
+// beyond it the result saturates either way, so this equals the integer add
+// and clamp.  Per-column terms are read once per group of 4 columns and reused
+// for the 4 row blocks.
+template <bool SMALL, bool VEC>
+__device__ __forceinline__ void q_epilogue(const QArgs& p, const i32x16_t (&acc)[4][4], uint8_t* __restrict__ y,
+                                           const uint32_t* U, const int* ZA, const float* SA, const uint32_t* CB,
+                                           const int* ZB, const float* SB, int64_t m0, int64_t n0, int lane, int wm,
+                                           int wn, float sy, float zyf, float lo, float hi, bool vec_store) {
+    const int64_t M = p.M, N = p.N;
+    uint32_t Um[4];
+    int za[4];
+    float sa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int mloc = wm * 128 + 32 * i + (lane & 31);
+        Um[i] = U[mloc];
+        za[i] = ZA[mloc];
+        sa[i] = SA[mloc];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int nloc = wn * 128 + 32 * j + 8 * q + 4 * (lane >> 5);
+            const int64_t n = n0 + nloc;
+            if (n >= N) continue;
+            const u32x4_t cb = *(const u32x4_t*)(CB + nloc);
+            const i32x4_t zb = *(const i32x4_t*)(ZB + nloc);
+            const f32x4_t sb = *(const f32x4_t*)(SB + nloc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t m = m0 + wm * 128 + 32 * i + (lane & 31);
+                if (m >= M) continue;
+                uint32_t packed = 0;
+                int outv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    int32_t s32;
+                    if constexpr (SMALL)  // exact 24-bit products, wrapping 32-bit sums
+                        s32 = (int32_t)((uint32_t)acc[i][j][4 * q + e] - (uint32_t)__mul24(zb[e], (int)Um[i]) -
+                                        (uint32_t)__mul24(za[i], (int)cb[e]));
+                    else
+                        s32 = (int32_t)((uint32_t)acc[i][j][4 * q + e] - (uint32_t)zb[e] * Um[i] -
+                                        (uint32_t)za[i] * cb[e]);
+                    const float prod = sa[i] * sb[e];
+                    const float mult = prod / sy;
+                    const float x = (float)s32 * mult;
+                    const float r = __builtin_amdgcn_fmed3f(__builtin_rintf(x) + zyf, lo, hi);
+                    const int qv = (int)r;
+                    outv[e] = qv;
+                    packed |= ((uint32_t)qv & 0xffu) << (8 * e);
+                }
+                uint8_t* yr = y + m * p.ldy + n;
+                if (vec_store) {
+                    *(uint32_t*)yr = packed;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) yr[e] = (uint8_t)outv[e];
+                }
+            }
+        }
+    }
+}
+
 template <bool AU8, bool BU8, bool VEC>
 __global__ __launch_bounds__(NT) void qlinear_kernel(QArgs p, int tiles_m, int tiles_n) {
     __shared__ __attribute__((aligned(1024))) char smem[STAGE];
@@ -362,54 +432,15 @@ __global__ __launch_bounds__(NT) void qlinear_kernel(QArgs p, int tiles_m, int t
     __syncthreads();
 
     const float sy = p.y_scale[0];
-    const int zy = p.y_u8 ? (int)((const uint8_t*)p.y_zp)[0] : (int)((const int8_t*)p.y_zp)[0];
-    const int lo = p.y_u8 ? 0 : -128, hi = p.y_u8 ? 255 : 127;
+    const float zyf = (float)(p.y_u8 ? (int)((const uint8_t*)p.y_zp)[0] : (int)((const int8_t*)p.y_zp)[0]);
+    const float lo = p.y_u8 ? 0.0f : -128.0f, hi = p.y_u8 ? 255.0f : 127.0f;
     const bool vec_store = VEC && (N % 4 == 0) && (p.ldy % 4 == 0);
-
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int mloc = wm * 128 + 32 * i + (lane & 31);
-        const int64_t m = m0 + mloc;
-        if (m >= M) continue;
-        const uint32_t Um = U[mloc];
-        const uint32_t za = (uint32_t)ZA[mloc];
-        const float sa_m = SA[mloc];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int nloc = wn * 128 + 32 * j + 8 * q + 4 * (lane >> 5);
-                const int64_t n = n0 + nloc;
-                if (n >= N) continue;
-                const u32x4_t cb = *(const u32x4_t*)(CB + nloc);
-                const i32x4_t zb = *(const i32x4_t*)(ZB + nloc);
-                const f32x4_t sb = *(const f32x4_t*)(SB + nloc);
-                uint32_t packed = 0;
-                int outv[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t s32 = (uint32_t)acc[i][j][4 * q + e] - (uint32_t)zb[e] * Um - za * cb[e];
-                    const float prod = sa_m * sb[e];
-                    const float mult = prod / sy;
-                    const float x = (float)(int32_t)s32 * mult;
-                    float r = __builtin_rintf(x);
-                    r = fminf(fmaxf(r, -1.0e9f), 1.0e9f);
-                    int qv = (int)r + zy;
-                    qv = qv < lo ? lo : (qv > hi ? hi : qv);
-                    outv[e] = qv;
-                    packed |= ((uint32_t)qv & 0xffu) << (8 * e);
-                }
-                uint8_t* yr = y + m * p.ldy + n;
-                if (vec_store) {
-                    *(uint32_t*)yr = packed;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (n + e < N) yr[e] = (uint8_t)outv[e];
-                }
-            }
-        }
-    }
+    // |U| <= 256 K and |colsum| <= 128 K: below 2^23 for K <= 32768, where the
+    // 24-bit multiply-adds are exact
+    if (K <= 32768)
+        q_epilogue<true, VEC>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi, vec_store);
+    else
+        q_epilogue<false, VEC>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi, vec_store);
 }
 
 template <bool AU8, bool BU8, bool VEC>
