@@ -13,8 +13,15 @@ also timed on its own (median of HIP-event intervals around its call) and
 reported against the MI355X dense MFMA peak of its type under `per_config`.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--only NAME]
+       python bench.py --copy-calibration      (1 GiB device-to-device copies, for
+                                                 scaling the HBM byte counters)
+
+`roofline.traffic` comes from profiles/traffic_grouped_bf16_moe.txt (FETCH_SIZE and
+WRITE_SIZE of the grouped kernel, scaled by the same counters on a plain copy); it
+is null when the kernel sources differ from the ones the counters were taken on.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -108,6 +115,38 @@ def time_each(torch, fn, reps):
     return ms[len(ms) // 2], ms
 
 
+def kernel_source_hash():
+    """sha256 over the kernel sources (csrc/*.hip, *.hpp): identifies the build the counters describe."""
+    d = os.path.join(ROOT, "onnx_matmul_family_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp")):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel_key):
+    """HBM bytes per launch from the committed counter summary, or None if stale/missing."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.txt" % kernel_key)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    try:
+        if kv.get("source_sha256") != kernel_source_hash():
+            return None
+        fetch = float(kv["fetch_kib_per_launch"]) * 1024 * float(kv["copy_fetch_factor"])
+        write = float(kv["write_kib_per_launch"]) * 1024 * float(kv["copy_write_factor"])
+        return fetch + write
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(W, budget_s):
     """The oracle as it stands, timed on a bounded sample of each workload's outputs."""
     import oracle
@@ -135,14 +174,21 @@ def cpu_baseline(W, budget_s):
 
         rng = np.random.default_rng(0)
         n = min(nout, 256)
-        while True:
+        # grow the sample until it takes about a tenth of this workload's share,
+        # then run the sample sized to fill the share, and time that run
+        while n < nout:
             sel = rng.integers(0, nout, n).astype(np.int64)
             t0 = time.perf_counter()
             call(sel)
             dt = time.perf_counter() - t0
-            if dt >= per * 0.3 or n >= nout:
+            if dt >= per * 0.1:
                 break
-            n = int(min(nout, max(n * 2, n * per * 0.5 / max(dt, 1e-4))))
+            n = min(nout, n * 4)
+        n = int(min(nout, max(1, n * per / max(dt, 1e-6)))) if n < nout else nout
+        sel = rng.integers(0, nout, n).astype(np.int64)
+        t0 = time.perf_counter()
+        call(sel)
+        dt = time.perf_counter() - t0
         total_ops += 2.0 * K * n
         total_t += dt
         parts.append("%s: %d outputs (%.2fs)" % (name, n, dt))
@@ -154,17 +200,28 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--reps", type=int, default=30, help="timed calls per workload for the per-config medians")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the baseline")
     ap.add_argument("--only", default=None, help="comma-separated workload names")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 1 GiB device-to-device copies (reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        X = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        Z = torch.empty_like(X)
+        for _ in range(max(1, args.steps)):
+            Z.copy_(X)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"bytes_read_per_copy": 1 << 30, "bytes_written_per_copy": 1 << 30,
+                                               "copies": max(1, args.steps)}}))
+        return
     from onnx_matmul_family_amd import _omm as om
     from onnx_matmul_family_amd import synth
     from tests.gpu_util import dev
@@ -208,7 +265,8 @@ def main():
     wd = W[dom["workload"]]
     ach = wd["ops"] / (dom["ms"] * 1e-3) / 1e12
     roof = dict(bound="mfma", achieved=round(ach, 2), peak=PEAK[wd["dtype"]], unit="TFLOP/s",
-                frac=round(ach / PEAK[wd["dtype"]], 4), traffic=None, kernel=dom["workload"])
+                frac=round(ach / PEAK[wd["dtype"]], 4), traffic=measured_traffic(dom["workload"]),
+                kernel=dom["workload"], launch_ms=dom["ms"])
 
     out = {
         "metric": METRIC, "value": round(total_ops / step_s / 1e12, 2), "unit": UNIT, "n_gpus": 1,
