@@ -16,7 +16,8 @@ import subprocess
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB = os.path.join(HERE, "liboracle.so")
+# OMM_ORACLE_LIB lets the mutation tests load a deliberately broken build
+LIB = os.environ.get("OMM_ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
 SRC = os.path.join(HERE, "oracle.c")
 
 F32, F16, BF16, F64, I8, U8, I32, I64 = range(8)

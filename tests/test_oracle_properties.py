@@ -281,6 +281,58 @@ def test_qlinear_requant_order_fp32():
     assert np.array_equal(y, exp)
 
 
+def _f32(x):
+    """Round a rational to the nearest IEEE binary32 value, ties to even
+    (normal range only: 24 significant bits, the unit of the last place is
+    2^(e-23) for 2^e <= |x| < 2^(e+1))."""
+    from fractions import Fraction
+    if x == 0:
+        return Fraction(0)
+    s, ax = (-1 if x < 0 else 1), abs(x)
+    e = ax.numerator.bit_length() - ax.denominator.bit_length()
+    if Fraction(2) ** e > ax:
+        e -= 1
+    ulp = Fraction(2) ** (e - 23)
+    return s * round(ax / ulp) * ulp  # round() of a Fraction is half-to-even
+
+
+def _requant_exact(acc, sa, sb, sy, zy, lo, hi):
+    """The requantisation reading in exact arithmetic: every step an exactly
+    evaluated operation followed by one binary32 rounding."""
+    from fractions import Fraction
+    mult = _f32(_f32(Fraction(sa) * Fraction(sb)) / Fraction(sy))
+    x = _f32(_f32(Fraction(acc)) * mult)
+    return min(hi, max(lo, round(x) + zy))
+
+
+def test_qlinear_requant_rounding_chain_near_ties():
+    """Cases built so that the real-valued x sits within a few binary32 ulps of
+    a half-integer: evaluating in double, or multiplying the scales in another
+    order, changes the integer result on many of them.  The oracle must give
+    the binary32 chain's answer on every case."""
+    from fractions import Fraction
+    rng = np.random.default_rng(97)
+    i8 = lambda v: np.array(v, np.int8)
+    n_real_differs = 0
+    for _ in range(400):
+        pa, pb = int(rng.integers(40, 128)), int(rng.integers(40, 128))
+        acc = pa * pb
+        sa, sb = np.float32(rng.uniform(0.002, 0.01)), np.float32(rng.uniform(0.002, 0.01))
+        j = int(rng.integers(0, 100))
+        sign = 1 if rng.random() < 0.5 else -1
+        # y_scale that puts the real-valued |x| at j + 0.5
+        sy = np.float32(float(Fraction(acc) * Fraction(float(sa)) * Fraction(float(sb)) / (Fraction(j) + Fraction(1, 2))))
+        exp = _requant_exact(acc, float(sa), float(sb), float(sy), 0, -128, 127)
+        real = Fraction(acc) * Fraction(float(sa)) * Fraction(float(sb)) / Fraction(float(sy))
+        if min(127, max(-128, round(real))) != exp:
+            n_real_differs += 1
+        y, got_acc = q(i8([[pa]]), float(sa), i8(0), i8([[sign * pb]]), float(sb), i8(0), float(sy), i8(0))
+        assert got_acc[0, 0] == sign * acc
+        exp = _requant_exact(sign * acc, float(sa), float(sb), float(sy), 0, -128, 127)
+        assert y[0, 0] == exp, (pa, pb, sa, sb, sy)
+    assert n_real_differs > 20  # the cases really discriminate
+
+
 def test_qlinear_scale_zp_shape_mismatch():
     a = np.zeros((2, 3), np.int8)
     b = np.zeros((3, 2), np.int8)
