@@ -95,8 +95,8 @@ __device__ __forceinline__ void epilogue16(const DenseArgs& p, const f32x16_t (&
                     v[e] = alpha * acc[i][j][4 * q + e] + cb[j][q][e];
                 if (vec_store) {
                     u32x2_t o;
-                    o.x = (uint32_t)to_bits<DT>(v[0]) | ((uint32_t)to_bits<DT>(v[1]) << 16);
-                    o.y = (uint32_t)to_bits<DT>(v[2]) | ((uint32_t)to_bits<DT>(v[3]) << 16);
+                    o.x = pack2<DT>(v[0], v[1]);
+                    o.y = pack2<DT>(v[2], v[3]);
                     *(u32x2_t*)(yr + n) = o;
                 } else {
 #pragma unroll
@@ -108,8 +108,66 @@ __device__ __forceinline__ void epilogue16(const DenseArgs& p, const f32x16_t (&
     }
 }
 
-template <int BM, int BN, int DT, bool AK, bool BKM, bool VEC>
+// Epilogue of a tile that lies wholly inside Y (rows 8-byte aligned): no
+// bounds checks.  CM = 0: no C; CM = 1: C constant along m and contiguous
+// along n (a bias row), loaded once per lane for all of its columns.
+template <int BM, int BN, int DT, int CM>
+__device__ __forceinline__ void epilogue16_full(const DenseArgs& p, const f32x16_t (&acc)[BM / 64][BN / 64],
+                                                uint16_t* __restrict__ Y, int64_t m0, int64_t n0, int lane, int wm,
+                                                int wn) {
+    constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+    const float alpha = p.alpha;
+    const int64_t nl = n0 + wn * WN + 4 * (lane >> 5);
+    const int64_t ml = m0 + wm * WM + (lane & 31);
+    // the bias row stays packed (two 16-bit values per register) until its
+    // column block is stored
+    u32x2_t craw[TN][4];
+    if constexpr (CM == 1) {
+        const uint16_t* __restrict__ Cp = (const uint16_t*)p.C + nl;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) craw[j][q] = *(const u32x2_t*)(Cp + 32 * j + 8 * q);
+    }
+    uint16_t* __restrict__ yb = Y + ml * p.ldy + nl;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        float cb[4][4];
+        if constexpr (CM == 1) {
+            const float beta = p.beta;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                cb[q][0] = beta * from_bits<DT>((uint16_t)craw[j][q].x);
+                cb[q][1] = beta * from_bits<DT>((uint16_t)(craw[j][q].x >> 16));
+                cb[q][2] = beta * from_bits<DT>((uint16_t)craw[j][q].y);
+                cb[q][3] = beta * from_bits<DT>((uint16_t)(craw[j][q].y >> 16));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            uint16_t* __restrict__ yr = yb + 32 * i * p.ldy + 32 * j;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[e] = CM == 1 ? alpha * acc[i][j][4 * q + e] + cb[q][e] : alpha * acc[i][j][4 * q + e];
+                u32x2_t o;
+                o.x = pack2<DT>(v[0], v[1]);
+                o.y = pack2<DT>(v[2], v[3]);
+                *(u32x2_t*)(yr + 8 * q) = o;
+            }
+        }
+    }
+}
+
+// MODE 0: register-staged loads, any shape.  MODE 1: DMA loads, ragged edge
+// tiles handled in the loads and the epilogue.  MODE 2 / 3: DMA loads, every
+// tile full and K a multiple of the K step (checked on the host), epilogue
+// without bounds checks, with no C (2) or a bias row C (3).
+template <int BM, int BN, int DT, bool AK, bool BKM, int MODE>
 __global__ __launch_bounds__(NT) void dense16_kernel(DenseArgs p, int tiles_m, int tiles_n) {
+    constexpr bool VEC = MODE != 0;
     constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
     constexpr int STAGE = (BM + BN) * KSTEP * 2;
     __shared__ __attribute__((aligned(1024))) char smem0[STAGE];
@@ -144,7 +202,9 @@ __global__ __launch_bounds__(NT) void dense16_kernel(DenseArgs p, int tiles_m, i
         DmaSrc<BN, BKM> srcB;
         srcA.init(A, p.lda, m0, M, K, lane);
         srcB.init(B, p.ldb, n0, N, K, lane);
-        if ((m0 + BM <= M) && (n0 + BN <= N) && (K % KSTEP == 0))
+        if constexpr (MODE >= 2)
+            mainloop_dma<BM, BN, DT, AK, BKM, false>(acc, smem0, smem1, srcA, srcB, nk, lane, wm, wn, wave);
+        else if ((m0 + BM <= M) && (n0 + BN <= N) && (K % KSTEP == 0))
             mainloop_dma<BM, BN, DT, AK, BKM, false>(acc, smem0, smem1, srcA, srcB, nk, lane, wm, wn, wave);
         else
             mainloop_dma<BM, BN, DT, AK, BKM, true>(acc, smem0, smem1, srcA, srcB, nk, lane, wm, wn, wave);
@@ -158,26 +218,29 @@ __global__ __launch_bounds__(NT) void dense16_kernel(DenseArgs p, int tiles_m, i
 
     // Epilogue: for each (i, j, q) a lane holds row m = m0 + wm*WM + 32 i + l%32 and
     // the 4 columns n .. n+3, n = n0 + wn*WN + 32 j + 8 q + 4 (l/32).
-    epilogue16<BM, BN, DT, VEC>(p, acc, Y, m0, n0, lane, wm, wn);
+    if constexpr (MODE >= 2)
+        epilogue16_full<BM, BN, DT, MODE - 2>(p, acc, Y, m0, n0, lane, wm, wn);
+    else
+        epilogue16<BM, BN, DT, VEC>(p, acc, Y, m0, n0, lane, wm, wn);
 }
 
-template <int BM, int BN, int DT, bool AK, bool BKM, bool VEC>
+template <int BM, int BN, int DT, bool AK, bool BKM, int MODE>
 hipError_t launch_cfg(const DenseArgs& a, hipStream_t s) {
     const int64_t tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
     const int64_t total = tiles_m * tiles_n * a.nb0 * a.nb1;
     if (total <= 0) return hipSuccess;
     if (total > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((dense16_kernel<BM, BN, DT, AK, BKM, VEC>), dim3((unsigned)total), dim3(NT), 0, s, a,
+    hipLaunchKernelGGL((dense16_kernel<BM, BN, DT, AK, BKM, MODE>), dim3((unsigned)total), dim3(NT), 0, s, a,
                        (int)tiles_m, (int)tiles_n);
     return hipGetLastError();
 }
 
-template <int BM, int BN, int DT, bool VEC>
+template <int BM, int BN, int DT, int MODE>
 hipError_t launch_layout(const DenseArgs& a, hipStream_t s) {
-    if (a.a_kmajor && a.b_kmajor) return launch_cfg<BM, BN, DT, true, true, VEC>(a, s);
-    if (a.a_kmajor && !a.b_kmajor) return launch_cfg<BM, BN, DT, true, false, VEC>(a, s);
-    if (!a.a_kmajor && a.b_kmajor) return launch_cfg<BM, BN, DT, false, true, VEC>(a, s);
-    return launch_cfg<BM, BN, DT, false, false, VEC>(a, s);
+    if (a.a_kmajor && a.b_kmajor) return launch_cfg<BM, BN, DT, true, true, MODE>(a, s);
+    if (a.a_kmajor && !a.b_kmajor) return launch_cfg<BM, BN, DT, true, false, MODE>(a, s);
+    if (!a.a_kmajor && a.b_kmajor) return launch_cfg<BM, BN, DT, false, true, MODE>(a, s);
+    return launch_cfg<BM, BN, DT, false, false, MODE>(a, s);
 }
 
 template <int DT>
@@ -195,9 +258,16 @@ hipError_t launch_dt(const DenseArgs& a, hipStream_t s) {
                          (a.b_kmajor ? 256 * a.ldb * 2 : 64 * a.ldb * 2) < (1LL << 31);
     const bool vec = a_ok && b_ok && y_ok && span_ok;
     const int64_t big_tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256) * a.nb0 * a.nb1;
-    if (vec && big_tiles >= 256) return launch_layout<256, 256, DT, true>(a, s);
-    if (vec) return launch_layout<128, 128, DT, true>(a, s);
-    return launch_layout<128, 128, DT, false>(a, s);
+    if (vec && big_tiles >= 256) {
+        // every tile full: epilogue without bounds checks (8-byte stores need
+        // N and the row stride to be multiples of 4)
+        const bool full = a.M % 256 == 0 && a.N % 256 == 0 && a.K % KSTEP == 0 && a.K > 0 && a.ldy % 4 == 0;
+        if (full && !a.C) return launch_layout<256, 256, DT, 2>(a, s);
+        if (full && a.c_sm == 0 && a.c_sn == 1 && ((uintptr_t)a.C & 7) == 0) return launch_layout<256, 256, DT, 3>(a, s);
+        return launch_layout<256, 256, DT, 1>(a, s);
+    }
+    if (vec) return launch_layout<128, 128, DT, 1>(a, s);
+    return launch_layout<128, 128, DT, 0>(a, s);
 }
 
 }  // namespace

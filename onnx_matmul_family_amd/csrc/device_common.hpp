@@ -75,11 +75,14 @@ __device__ __forceinline__ int mmaj8_off(int k, int byte_in_row) {
 
 // ---------------------------------------------------------------------------
 // Conversions (round to nearest even).
+// gfx950 converts fp32 to bf16 / fp16 in hardware (v_cvt_pk_bf16_f32,
+// v_cvt_pk_f16_f32), rounding to nearest even under the default mode.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);  // quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
     _Float16 h = (_Float16)f;  // v_cvt_f16_f32, round to nearest even
@@ -91,6 +94,15 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) { return (float)__b
 template <int DT>  // 0 = bf16, 1 = fp16
 __device__ __forceinline__ uint16_t to_bits(float f) {
     return DT == 0 ? f32_to_bf16_bits(f) : f32_to_f16_bits(f);
+}
+// two fp32 values -> one register of two 16-bit values (a in the low half)
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    const f32x2_t v = {a, b};
+    if constexpr (DT == 0)
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
 }
 template <int DT>
 __device__ __forceinline__ float from_bits(uint16_t b) {

@@ -510,54 +510,67 @@ __device__ __forceinline__ void kblock_read(f32x16_t (&acc)[TM][TN], const F& cu
     });
 }
 
-// The k-block after the barrier: MFMAs on `cur`, interleaved with the reads of
-// the next stage's k-block 0 (from Y) and this wave's DMA of stage kt+2 (into X).
-template <int DT, int TM, int TN, bool CHECKED, class F, class SA, class SB>
-__device__ __forceinline__ void kblock_read_dma(f32x16_t (&acc)[TM][TN], const F& cur, F& nxt, const char* Y, char* X,
-                                                int A_BYTES, const SA& srcA, const SB& srcB, int kt2, bool live,
-                                                int lane, int wm, int wn, int wave) {
-    constexpr int NM = TM * TN, NR = TM + TN;
-    constexpr int LA = SA::PER_WAVE, LD = SA::PER_WAVE + SB::PER_WAVE;
-    const DmaCtx ca = srcA.ctx(X, kt2, live), cb = srcB.ctx(X + A_BYTES, kt2, live);
+// DMA instruction d (0 .. LA+LB-1) of this wave's share of one stage: the
+// first LA go to operand A, the rest to operand B.
+template <bool CHECKED, int LA, int d, class SA, class SB>
+__device__ __forceinline__ void dma_one(const SA& srcA, const SB& srcB, const DmaCtx& ca, const DmaCtx& cb, int kt,
+                                        int wave) {
+    if constexpr (d < LA)
+        srcA.template one<CHECKED>(ca, kt, wave, d);
+    else
+        srcB.template one<CHECKED>(cb, kt, wave, d - LA);
+}
+
+// One k-block of MFMAs on `cur` with the fragment reads of k-block s of `lds`
+// into `nxt`, and this wave's DMA instructions D0 .. D1-1 of stage kt (into
+// buffer X) spread evenly between the MFMAs: issuing them back to back would
+// stall the wave on the memory pipeline.
+template <int DT, int TM, int TN, bool CHECKED, int D0, int D1, class F, class SA, class SB>
+__device__ __forceinline__ void kblock_read_dma(f32x16_t (&acc)[TM][TN], const F& cur, F& nxt, const char* lds, int s,
+                                                char* X, int A_BYTES, const SA& srcA, const SB& srcB, int kt,
+                                                bool live, int lane, int wm, int wn, int wave) {
+    constexpr int NM = TM * TN, NR = TM + TN, ND = D1 - D0;
+    constexpr int LA = SA::PER_WAVE;
+    const DmaCtx ca = srcA.ctx(X, kt, live), cb = srcB.ctx(X + A_BYTES, kt, live);
     static_for<0, NM>([&](auto xc) {
         constexpr int x = decltype(xc)::value;
-        static_for<(x * LD + NM - 1) / NM, ((x + 1) * LD + NM - 1) / NM>([&](auto dc) {
-            constexpr int d = decltype(dc)::value;
-            if constexpr (d < LA)
-                srcA.template one<CHECKED>(ca, kt2, wave, d);
-            else
-                srcB.template one<CHECKED>(cb, kt2, wave, d - LA);
-        });
         mma_one<x, DT>(acc, cur);
+        static_for<D0 + (x * ND + NM - 1) / NM, D0 + ((x + 1) * ND + NM - 1) / NM>(
+            [&](auto dc) { dma_one<CHECKED, LA, decltype(dc)::value>(srcA, srcB, ca, cb, kt, wave); });
         static_for<(x * NR + NM - 1) / NM, ((x + 1) * NR + NM - 1) / NM>([&](auto rc) {
-            nxt.template read_one<decltype(rc)::value>(Y, 0, lane, wm, wn);
+            nxt.template read_one<decltype(rc)::value>(lds, s, lane, wm, wn);
         });
         fence_sched();
     });
 }
 
-// One stage of the DMA K loop: stage kt is complete in X (barrier passed),
-// fc holds its k-block 0 fragments (requested), stage kt+1 is in flight into Y.
-// The fragments of k-block s+1 are read while k-block s's MFMAs run; stage
-// kt+2's DMA is issued right after the barrier that retires stage kt, spread
-// over the MFMAs of the last k-block.  Past the last stage the DMA targets an
-// empty range (zeros into a buffer no later stage reads) and the reads of Y
-// fetch values nobody uses: the stage has no data-dependent branches, so the
-// accumulators flow through straight-line code.
+// One stage of the DMA K loop.  On entry stage kt is complete in X (barrier
+// passed), fc holds its k-block 0 fragments (requested), and the first half of
+// stage kt+1's DMA into Y is in flight.  The second half of stage kt+1's DMA
+// goes out during k-block 0, the barrier after k-block 2 retires X and lands
+// Y, and the first half of stage kt+2's DMA into X goes out during k-block 3.
+// Each DMA thus has at least two k-blocks of MFMAs to land before its barrier.
+// Past the last stage the DMA targets an empty range (zeros into a buffer no
+// later stage reads) and the reads of Y fetch values nobody uses: the stage
+// has no data-dependent branches, so the accumulators flow through
+// straight-line code.
 template <int BM, int BN, int DT, bool AK, bool BKM, bool CHECKED, class SA, class SB, class F>
 __device__ __forceinline__ void dma_stage(f32x16_t (&acc)[BM / 64][BN / 64], F& fc, F& fn, char* X, char* Y,
                                           const SA& srcA, const SB& srcB, int kt, int nk, int lane, int wm, int wn,
                                           int wave) {
     constexpr int A_BYTES = BM * KSTEP * 2;
+    constexpr int LD = SA::PER_WAVE + SB::PER_WAVE, H = LD / 2;
+    constexpr int TM = BM / 64, TN = BN / 64;
     fence_sched();
-    kblock_read<DT>(acc, fc, fn, X, 1, lane, wm, wn);
+    kblock_read_dma<DT, TM, TN, CHECKED, H, LD>(acc, fc, fn, X, 1, Y, A_BYTES, srcA, srcB, kt + 1, kt + 1 < nk,
+                                                lane, wm, wn, wave);
     kblock_read<DT>(acc, fn, fc, X, 2, lane, wm, wn);
     kblock_read<DT>(acc, fc, fn, X, 3, lane, wm, wn);
     wait_vm<0>();     // this wave's DMA of stage kt+1 has landed
     __syncthreads();  // ... every wave's; and every read of X is done
     fence_sched();
-    kblock_read_dma<DT, BM / 64, BN / 64, CHECKED>(acc, fn, fc, Y, X, A_BYTES, srcA, srcB, kt + 2, kt + 2 < nk, lane,
-                                                  wm, wn, wave);
+    kblock_read_dma<DT, TM, TN, CHECKED, 0, H>(acc, fn, fc, Y, 0, X, A_BYTES, srcA, srcB, kt + 2, kt + 2 < nk, lane,
+                                               wm, wn, wave);
 }
 
 // DMA K loop over nk stages; stage kt lives in buffer kt & 1 (s0 / s1).  The
@@ -569,13 +582,16 @@ __device__ __forceinline__ void mainloop_dma(f32x16_t (&acc)[BM / 64][BN / 64], 
                                              char* __restrict__ s1, const SA& srcA, const SB& srcB, int nk, int lane,
                                              int wm, int wn, int wave) {
     constexpr int A_BYTES = BM * KSTEP * 2;
-    constexpr int LOADS = SA::PER_WAVE + SB::PER_WAVE;  // DMA instructions per stage per wave
+    constexpr int LA = SA::PER_WAVE, LD = SA::PER_WAVE + SB::PER_WAVE, H = LD / 2;
     if (nk <= 0) return;
-    srcA.template issue<CHECKED>(s0, 0, wave);
-    srcB.template issue<CHECKED>(s0 + A_BYTES, 0, wave);
-    srcA.template issue<CHECKED>(s1, 1, wave, nk > 1);
-    srcB.template issue<CHECKED>(s1 + A_BYTES, 1, wave, nk > 1);
-    wait_vm<LOADS>();
+    {
+        // stage 0 whole, the first half of stage 1
+        const DmaCtx a0 = srcA.ctx(s0, 0, true), b0 = srcB.ctx(s0 + A_BYTES, 0, true);
+        static_for<0, LD>([&](auto dc) { dma_one<CHECKED, LA, decltype(dc)::value>(srcA, srcB, a0, b0, 0, wave); });
+        const DmaCtx a1 = srcA.ctx(s1, 1, nk > 1), b1 = srcB.ctx(s1 + A_BYTES, 1, nk > 1);
+        static_for<0, H>([&](auto dc) { dma_one<CHECKED, LA, decltype(dc)::value>(srcA, srcB, a1, b1, 1, wave); });
+    }
+    wait_vm<H>();
     __syncthreads();
     Frags<BM, BN, AK, BKM> fc, fn;
     fc.read(s0, 0, lane, wm, wn);

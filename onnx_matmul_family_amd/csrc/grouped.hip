@@ -263,8 +263,8 @@ __device__ __forceinline__ void grouped_body(const GroupedArgs& a, const char* w
                 for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e] + bv[j][q][e];
                 if (vec_store) {
                     u32x2_t o;
-                    o.x = (uint32_t)to_bits<DT>(v[0]) | ((uint32_t)to_bits<DT>(v[1]) << 16);
-                    o.y = (uint32_t)to_bits<DT>(v[2]) | ((uint32_t)to_bits<DT>(v[3]) << 16);
+                    o.x = pack2<DT>(v[0], v[1]);
+                    o.y = pack2<DT>(v[2], v[3]);
                     *(u32x2_t*)(yr + n) = o;
                 } else {
 #pragma unroll

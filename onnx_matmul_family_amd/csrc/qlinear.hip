@@ -8,8 +8,11 @@
 // zero points enter through the expansion (exact mod 2^32)
 //   acc = sum ab - zb * sum_k a[m,k] - za * sum_k b[k,n] + K * za * zb.
 // The row sums of a and column sums of b come from the MFMA operand fragments
-// already in registers (v_dot4_i32_i8 against 0x01010101), so no extra pass
-// over memory.  uint8 operands are mapped to int8 by flipping the top bit
+// already in registers, so no extra pass over memory: each dword of 4 signed
+// bytes is biased to unsigned (xor 0x80) and summed with v_sad_u8 against
+// zero, and the bias is taken off at the end.  (The v_dot4 instructions would
+// do it in one step, but on gfx950 they hold up the MFMAs issued around them;
+// v_sad_u8 and v_xor do not.)  uint8 operands are mapped to int8 by flipping the top bit
 // (a - 128) and their zero points shifted by 128, which leaves every a - za
 // unchanged.  The requantisation uses IEEE fp32 multiply, correctly rounded
 // division and round-half-even, in the order above, with no contraction.
@@ -110,12 +113,20 @@ __device__ __forceinline__ i32x4_t frag_b(const char* s, int colb, int ks, int l
     return i32x4_t{lo.x, lo.y, hi.x, hi.y};
 }
 
-__device__ __forceinline__ int dot4sum(i32x4_t v, int acc) {
-    acc = __builtin_amdgcn_sdot4(v.x, 0x01010101, acc, false);
-    acc = __builtin_amdgcn_sdot4(v.y, 0x01010101, acc, false);
-    acc = __builtin_amdgcn_sdot4(v.z, 0x01010101, acc, false);
-    acc = __builtin_amdgcn_sdot4(v.w, 0x01010101, acc, false);
-    return acc;
+// acc + sum of the 4 bytes of v taken as int8, each biased by +128 (the bias,
+// 128 per byte summed, is removed once after the K loop)
+__device__ __forceinline__ int bytesum1(int v, int acc) {
+    // the xor is opaque to the compiler: for uint8 operands v is itself a
+    // flipped value, and folding the two flips would keep both copies live
+    uint32_t u;
+    asm("v_xor_b32 %0, 0x80808080, %1" : "=v"(u) : "v"(v));
+    return (int)__builtin_amdgcn_sad_u8(u, 0u, (uint32_t)acc);
+}
+__device__ __forceinline__ int bytesum(i32x4_t v, int acc) {
+    acc = bytesum1(v.x, acc);
+    acc = bytesum1(v.y, acc);
+    acc = bytesum1(v.z, acc);
+    return bytesum1(v.w, acc);
 }
 
 template <bool AU8, bool BU8, int MODE>
@@ -149,9 +160,9 @@ __device__ __forceinline__ void qloop(i32x16_t (&acc)[4][4], int (&rs)[4], int (
                 for (int j = 0; j < 4; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[j], af[i], acc[i][j], 0, 0, 0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) rs[i] = dot4sum(af[i], rs[i]);
+            for (int i = 0; i < 4; ++i) rs[i] = bytesum(af[i], rs[i]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) cs[j] = dot4sum(bf[j], cs[j]);
+            for (int j = 0; j < 4; ++j) cs[j] = bytesum(bf[j], cs[j]);
         }
         if (kt + 1 < nk) stash(buf ? smem : smem1, ra, rb, t);
         __syncthreads();
@@ -160,6 +171,13 @@ __device__ __forceinline__ void qloop(i32x16_t (&acc)[4][4], int (&rs)[4], int (
 
 // int8 MFMA operand fragments of one 32-value k-block (uint8 operands flipped
 // to int8 here: the DMA copies raw bytes).
+// uint8 -> int8 (a - 128) in place; opaque to the compiler so that it keeps
+// one copy of each fragment
+__device__ __forceinline__ void flip(i32x4_t& v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) asm("v_xor_b32 %0, 0x80808080, %0" : "+v"(v[e]));
+}
+
 template <bool AU8, bool BU8>
 struct QFrags {
     i32x4_t a[4], b[4];
@@ -167,10 +185,10 @@ struct QFrags {
     __device__ __forceinline__ void read_one(const char* st, int ks, int lane, int wm, int wn) {
         if constexpr (R < 4) {
             a[R] = frag_a(st, wm * 128 + 32 * R, ks, lane);
-            if (AU8) a[R] ^= (int)0x80808080;
+            if constexpr (AU8) flip(a[R]);
         } else {
             b[R - 4] = frag_b(st, wn * 128 + 32 * (R - 4), ks, lane);
-            if (BU8) b[R - 4] ^= (int)0x80808080;
+            if constexpr (BU8) flip(b[R - 4]);
         }
     }
     __device__ __forceinline__ void read(const char* st, int ks, int lane, int wm, int wn) {
@@ -178,13 +196,13 @@ struct QFrags {
     }
 };
 
-// MFMA X of a k-block (tile (X/4, X%4)) plus one dword of the row-sum and one
-// of the column-sum dot products, so the 32 sums ride along the 16 MFMAs.
+// MFMA X of a k-block (tile (X/4, X%4)) plus one dword of the row sums and
+// one of the column sums, so the 32 sums ride along the 16 MFMAs.
 template <int X, class F>
 __device__ __forceinline__ void q_one(i32x16_t (&acc)[4][4], int (&rs)[4], int (&cs)[4], const F& f) {
     acc[X / 4][X % 4] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.b[X % 4], f.a[X / 4], acc[X / 4][X % 4], 0, 0, 0);
-    rs[X / 4] = __builtin_amdgcn_sdot4(f.a[X / 4][X % 4], 0x01010101, rs[X / 4], false);
-    cs[X / 4] = __builtin_amdgcn_sdot4(f.b[X / 4][X % 4], 0x01010101, cs[X / 4], false);
+    rs[X / 4] = bytesum1(f.a[X / 4][X % 4], rs[X / 4]);
+    cs[X / 4] = bytesum1(f.b[X / 4][X % 4], cs[X / 4]);
 }
 
 template <class F>
@@ -199,60 +217,64 @@ __device__ __forceinline__ void q_kblock(i32x16_t (&acc)[4][4], int (&rs)[4], in
     });
 }
 
-template <bool CHECKED, class F, class SA, class SB>
+// A k-block of MFMAs on `cur`, the reads of k-block ks of `lds` into `nxt`,
+// and this wave's DMA instructions D0 .. D1-1 of stage kt (into buffer X)
+// spread evenly between the MFMAs.
+template <bool CHECKED, int D0, int D1, class F, class SA, class SB>
 __device__ __forceinline__ void q_kblock_dma(i32x16_t (&acc)[4][4], int (&rs)[4], int (&cs)[4], const F& cur, F& nxt,
-                                             const char* Y, char* X, const SA& sa, const SB& sb, int kt2, bool live,
-                                             int lane, int wm, int wn, int wave) {
+                                             const char* lds, int ks, char* X, const SA& sa, const SB& sb, int kt,
+                                             bool live, int lane, int wm, int wn, int wave) {
     using namespace core16;
-    constexpr int LA = SA::PER_WAVE, LD = SA::PER_WAVE + SB::PER_WAVE;  // 8 + 8
-    const DmaCtx ca = sa.ctx(X, kt2, live), cb = sb.ctx(X + A_BYTES, kt2, live);
+    constexpr int LA = SA::PER_WAVE, ND = D1 - D0;
+    const DmaCtx ca = sa.ctx(X, kt, live), cb = sb.ctx(X + A_BYTES, kt, live);
     static_for<0, 16>([&](auto xc) {
         constexpr int x = decltype(xc)::value;
-        static_for<x * LD / 16, (x + 1) * LD / 16>([&](auto dc) {
-            constexpr int d = decltype(dc)::value;
-            if constexpr (d < LA)
-                sa.template one<CHECKED>(ca, kt2, wave, d);
-            else
-                sb.template one<CHECKED>(cb, kt2, wave, d - LA);
-        });
         q_one<x>(acc, rs, cs, cur);
-        if constexpr ((x & 1) == 0) nxt.template read_one<x / 2>(Y, 0, lane, wm, wn);
+        static_for<D0 + (x * ND + 15) / 16, D0 + ((x + 1) * ND + 15) / 16>(
+            [&](auto dc) { dma_one<CHECKED, LA, decltype(dc)::value>(sa, sb, ca, cb, kt, wave); });
+        if constexpr ((x & 1) == 0) nxt.template read_one<x / 2>(lds, ks, lane, wm, wn);
         fence_sched();
     });
 }
 
-// One stage of the DMA loop; same schedule as the bf16 core (fragments one
-// k-block ahead, stage kt+2's DMA spread over the k-block after the barrier,
-// no data-dependent branches).
+// One stage of the DMA loop, on the schedule of the bf16 core: fragments one
+// k-block ahead; the second half of stage kt+1's DMA (into Y) during k-block
+// 0, the barrier after k-block 2, the first half of stage kt+2's DMA (into X)
+// during k-block 3; no data-dependent branches.
 template <bool CHECKED, class SA, class SB, class F>
 __device__ __forceinline__ void q_stage(i32x16_t (&acc)[4][4], int (&rs)[4], int (&cs)[4], F& fc, F& fn, char* X,
                                         char* Y, const SA& sa, const SB& sb, int kt, int nk, int lane, int wm, int wn,
                                         int wave) {
     using namespace core16;
+    constexpr int LD = SA::PER_WAVE + SB::PER_WAVE, H = LD / 2;
     fence_sched();
-    q_kblock(acc, rs, cs, fc, fn, X, 1, lane, wm, wn);
+    q_kblock_dma<CHECKED, H, LD>(acc, rs, cs, fc, fn, X, 1, Y, sa, sb, kt + 1, kt + 1 < nk, lane, wm, wn, wave);
     q_kblock(acc, rs, cs, fn, fc, X, 2, lane, wm, wn);
     q_kblock(acc, rs, cs, fc, fn, X, 3, lane, wm, wn);
     wait_vm<0>();
     __syncthreads();
     fence_sched();
-    q_kblock_dma<CHECKED>(acc, rs, cs, fn, fc, Y, X, sa, sb, kt + 2, kt + 2 < nk, lane, wm, wn, wave);
+    q_kblock_dma<CHECKED, 0, H>(acc, rs, cs, fn, fc, Y, 0, X, sa, sb, kt + 2, kt + 2 < nk, lane, wm, wn, wave);
 }
 
-// An odd stage count runs one more stage of zeros (no effect on the products
-// or the sums).  On return no DMA is in flight and every wave is done with LDS.
+// An odd stage count runs one more stage of zeros (no effect on the products;
+// the sums count its bytes like any other).  On return no DMA is in flight and
+// every wave is done with LDS.
 template <bool AU8, bool BU8, bool CHECKED, class SA, class SB>
 __device__ __forceinline__ void qloop_dma(i32x16_t (&acc)[4][4], int (&rs)[4], int (&cs)[4], char* __restrict__ s0,
                                           char* __restrict__ s1, const SA& sa, const SB& sb, int nk, int lane, int wm,
                                           int wn, int wave) {
     using namespace core16;
-    constexpr int LOADS = SA::PER_WAVE + SB::PER_WAVE;
+    constexpr int LA = SA::PER_WAVE, LD = SA::PER_WAVE + SB::PER_WAVE, H = LD / 2;
     if (nk <= 0) return;
-    sa.template issue<CHECKED>(s0, 0, wave);
-    sb.template issue<CHECKED>(s0 + A_BYTES, 0, wave);
-    sa.template issue<CHECKED>(s1, 1, wave, nk > 1);
-    sb.template issue<CHECKED>(s1 + A_BYTES, 1, wave, nk > 1);
-    wait_vm<LOADS>();
+    {
+        // stage 0 whole, the first half of stage 1
+        const DmaCtx a0 = sa.ctx(s0, 0, true), b0 = sb.ctx(s0 + A_BYTES, 0, true);
+        static_for<0, LD>([&](auto dc) { dma_one<CHECKED, LA, decltype(dc)::value>(sa, sb, a0, b0, 0, wave); });
+        const DmaCtx a1 = sa.ctx(s1, 1, nk > 1), b1 = sb.ctx(s1 + A_BYTES, 1, nk > 1);
+        static_for<0, H>([&](auto dc) { dma_one<CHECKED, LA, decltype(dc)::value>(sa, sb, a1, b1, 1, wave); });
+    }
+    wait_vm<H>();
     __syncthreads();
     QFrags<AU8, BU8> fc, fn;
     fc.read(s0, 0, lane, wm, wn);
@@ -338,8 +360,83 @@ __device__ __forceinline__ void q_epilogue(const QArgs& p, const i32x16_t (&acc)
     }
 }
 
-template <bool AU8, bool BU8, bool VEC>
+// Requantisation of a tile that lies wholly inside y (K <= 32768, 4-byte
+// aligned rows), without bounds checks.  Per element, with the per-row terms
+// U, za, sa and per-column terms colsum, zb, sb of the tile in LDS:
+//   acc  = sum ab - zb * U - za * colsum        (24-bit products, int32 wrap)
+//   mult = fp32(fp32(sa * sb) / sy)
+//   t    = (fp32(acc) * mult + 1.5*2^23) + zy, clamped to 1.5*2^23 + [lo, hi]
+// Adding 1.5*2^23 (an even integer, where fp32 spacing is 1) rounds the
+// product to the nearest integer, ties to even, exactly like rint; adding the
+// integer zy afterwards is exact; the clamp saturates, also for products too
+// large for the trick; the result is the low byte of t's bits.
+// MARK: the division as q0 = prod * r, r = fp32(1/sy) once, corrected by one
+// fused step q0 + fma(-q0, sy, prod) * r, which is the correctly rounded
+// quotient (Markstein) when nothing underflows or overflows; the caller takes
+// this branch only when every scale of the tile and sy lie in [2^-30, 2^30]
+// in magnitude (or are zero), which keeps every intermediate normal.
+template <bool MARK>
+__device__ __forceinline__ void q_epilogue_full(const QArgs& p, const i32x16_t (&acc)[4][4], uint8_t* __restrict__ y,
+                                                const uint32_t* U, const int* ZA, const float* SA, const uint32_t* CB,
+                                                const int* ZB, const float* SB, int64_t m0, int64_t n0, int lane,
+                                                int wm, int wn, float sy, float zyf, float lo, float hi) {
+    constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
+    const float r = 1.0f / sy;
+    const float tlo = MAGIC + lo, thi = MAGIC + hi;
+    int Um[4], nza[4];
+    float sa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int mloc = wm * 128 + 32 * i + (lane & 31);
+        Um[i] = (int)U[mloc];
+        nza[i] = -ZA[mloc];
+        sa[i] = SA[mloc];
+    }
+    uint8_t* __restrict__ yb = y + (m0 + wm * 128 + (lane & 31)) * p.ldy + n0 + wn * 128 + 4 * (lane >> 5);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int nloc = wn * 128 + 32 * j + 8 * q + 4 * (lane >> 5);
+            const i32x4_t cb = *(const i32x4_t*)(CB + nloc);
+            const i32x4_t zb = *(const i32x4_t*)(ZB + nloc);
+            const f32x4_t sb = *(const f32x4_t*)(SB + nloc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t bytes[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // |U| <= 2^23, |colsum| <= 2^22, |z| <= 255: exact 24-bit products
+                    const int s32 = (int)((uint32_t)acc[i][j][4 * q + e] + (uint32_t)__mul24(-zb[e], Um[i]) +
+                                          (uint32_t)__mul24(nza[i], cb[e]));
+                    const float prod = sa[i] * sb[e];
+                    float mult;
+                    if constexpr (MARK) {
+                        const float q0 = prod * r;
+                        mult = __builtin_fmaf(__builtin_fmaf(-q0, sy, prod), r, q0);
+                    } else {
+                        mult = prod / sy;
+                    }
+                    const float x = (float)s32 * mult;
+                    const float t = __builtin_amdgcn_fmed3f((x + MAGIC) + zyf, tlo, thi);
+                    bytes[e] = __float_as_uint(t);
+                }
+                // low bytes of the four results, in order, into one dword
+                const uint32_t lo2 = __builtin_amdgcn_perm(bytes[1], bytes[0], 0x0c0c0400u);
+                const uint32_t hi2 = __builtin_amdgcn_perm(bytes[3], bytes[2], 0x0c0c0400u);
+                *(uint32_t*)(yb + (int64_t)32 * i * p.ldy + 32 * j + 8 * q) = lo2 | (hi2 << 16);
+            }
+        }
+    }
+}
+
+// MODE 0: register-staged loads, any shape.  MODE 1: DMA loads, ragged tiles
+// handled in the loads and the epilogue.  MODE 2: DMA loads, every tile full,
+// K a multiple of the stage and at most 32768 (checked on the host), fast
+// epilogue.
+template <bool AU8, bool BU8, int MODE>
 __global__ __launch_bounds__(NT) void qlinear_kernel(QArgs p, int tiles_m, int tiles_n) {
+    constexpr bool VEC = MODE != 0;
     __shared__ __attribute__((aligned(1024))) char smem[STAGE];
     __shared__ __attribute__((aligned(1024))) char smem1[STAGE];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -366,35 +463,43 @@ __global__ __launch_bounds__(NT) void qlinear_kernel(QArgs p, int tiles_m, int t
     int rs[4] = {0, 0, 0, 0}, cs[4] = {0, 0, 0, 0};
 
     const int nk = (int)((K + KB - 1) / KB);
+    int nk_run;  // stages the loop ran: every lane summed 64 biased bytes per stage
     if constexpr (VEC) {
         core16::DmaSrc<BMQ, true, 1> sa;
         core16::DmaSrcMN8<BNQ> sb;
         sa.init(a, p.lda, m0, M, K, lane);
         sb.init(b, p.ldb, n0, N, K, lane);
-        if (m0 + BMQ <= M && n0 + BNQ <= N && K % KB == 0)
+        if constexpr (MODE == 2)
+            qloop_dma<AU8, BU8, false>(acc, rs, cs, smem, smem1, sa, sb, nk, lane, wm, wn, wave);
+        else if (m0 + BMQ <= M && n0 + BNQ <= N && K % KB == 0)
             qloop_dma<AU8, BU8, false>(acc, rs, cs, smem, smem1, sa, sb, nk, lane, wm, wn, wave);
         else
             qloop_dma<AU8, BU8, true>(acc, rs, cs, smem, smem1, sa, sb, nk, lane, wm, wn, wave);
+        nk_run = nk > 0 ? (nk + 1) & ~1 : 0;
     } else {
         QSrc<true, AU8> sa;
         QSrc<false, BU8> sb;
         sa.init(a, p.lda, m0, M, K, t);
         sb.init(b, p.ldb, n0, N, K, t);
         qloop<AU8, BU8, 2>(acc, rs, cs, smem, smem1, sa, sb, nk, t, lane, wm, wn);
+        nk_run = nk;
     }
+    const uint32_t bias = 128u * 64u * (uint32_t)nk_run;
 
     // full row / column sums: lanes l and l^32 hold the two k-halves
     int* rowsum = (int*)smem;        // 256 tile rows
     int* colsum = (int*)smem + 256;  // 256 tile columns
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int r = rs[i] + __shfl_xor(rs[i], 32);
-        if (wn == 0 && lane < 32) rowsum[wm * 128 + 32 * i + lane] = r;
+        const uint32_t r = (uint32_t)rs[i] - bias;
+        const int rr = (int)(r + (uint32_t)__shfl_xor((int)r, 32));
+        if (wn == 0 && lane < 32) rowsum[wm * 128 + 32 * i + lane] = rr;
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int c = cs[j] + __shfl_xor(cs[j], 32);
-        if (wm == 0 && lane < 32) colsum[wn * 128 + 32 * j + lane] = c;
+        const uint32_t c = (uint32_t)cs[j] - bias;
+        const int cc = (int)(c + (uint32_t)__shfl_xor((int)c, 32));
+        if (wm == 0 && lane < 32) colsum[wn * 128 + 32 * j + lane] = cc;
     }
     __syncthreads();
 
@@ -408,6 +513,13 @@ __global__ __launch_bounds__(NT) void qlinear_kernel(QArgs p, int tiles_m, int t
     int* ZB = (int*)smem + 1536;
     float* SB = (float*)smem + 1792;
     const uint32_t Ku = (uint32_t)K;
+    const float sy = p.y_scale[0];
+    // scales inside [2^-30, 2^30] (or zero) keep the fast division exact
+    auto tame = [](float v) {
+        const float av = __builtin_fabsf(v);
+        return av == 0.0f || (av >= 0x1p-30f && av <= 0x1p30f);
+    };
+    int scales_ok;
     {
         const int64_t m = m0 + t, n = n0 + t;
         int za = 0, zb = 0;
@@ -428,38 +540,46 @@ __global__ __launch_bounds__(NT) void qlinear_kernel(QArgs p, int tiles_m, int t
         CB[t] = (uint32_t)colsum[t];
         ZB[t] = zb;
         SB[t] = sb;
+        scales_ok = tame(sa) && tame(sb) && sy != 0.0f && tame(sy);
     }
-    __syncthreads();
+    scales_ok = __syncthreads_and(scales_ok);
 
-    const float sy = p.y_scale[0];
     const float zyf = (float)(p.y_u8 ? (int)((const uint8_t*)p.y_zp)[0] : (int)((const int8_t*)p.y_zp)[0]);
     const float lo = p.y_u8 ? 0.0f : -128.0f, hi = p.y_u8 ? 255.0f : 127.0f;
-    const bool vec_store = VEC && (N % 4 == 0) && (p.ldy % 4 == 0);
-    // |U| <= 256 K and |colsum| <= 128 K: below 2^23 for K <= 32768, where the
-    // 24-bit multiply-adds are exact
-    if (K <= 32768)
-        q_epilogue<true, VEC>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi, vec_store);
-    else
-        q_epilogue<false, VEC>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi, vec_store);
+    if constexpr (MODE == 2) {
+        if (scales_ok)
+            q_epilogue_full<true>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi);
+        else
+            q_epilogue_full<false>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi);
+    } else {
+        const bool vec_store = VEC && (N % 4 == 0) && (p.ldy % 4 == 0);
+        // |U| <= 256 K and |colsum| <= 128 K: below 2^23 for K <= 32768, where the
+        // 24-bit multiply-adds are exact
+        if (K <= 32768)
+            q_epilogue<true, VEC>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi, vec_store);
+        else
+            q_epilogue<false, VEC>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi,
+                                   vec_store);
+    }
 }
 
-template <bool AU8, bool BU8, bool VEC>
+template <bool AU8, bool BU8, int MODE>
 hipError_t launch_q(const QArgs& a, hipStream_t s) {
     const int64_t tiles_m = (a.M + BMQ - 1) / BMQ, tiles_n = (a.N + BNQ - 1) / BNQ;
     const int64_t total = tiles_m * tiles_n * a.nb0 * a.nb1;
     if (total <= 0) return hipSuccess;
     if (total > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((qlinear_kernel<AU8, BU8, VEC>), dim3((unsigned)total), dim3(NT), 0, s, a, (int)tiles_m,
+    hipLaunchKernelGGL((qlinear_kernel<AU8, BU8, MODE>), dim3((unsigned)total), dim3(NT), 0, s, a, (int)tiles_m,
                        (int)tiles_n);
     return hipGetLastError();
 }
 
-template <bool VEC>
+template <int MODE>
 hipError_t launch_q_types(const QArgs& a, hipStream_t s) {
-    if (a.a_u8 && a.b_u8) return launch_q<true, true, VEC>(a, s);
-    if (a.a_u8) return launch_q<true, false, VEC>(a, s);
-    if (a.b_u8) return launch_q<false, true, VEC>(a, s);
-    return launch_q<false, false, VEC>(a, s);
+    if (a.a_u8 && a.b_u8) return launch_q<true, true, MODE>(a, s);
+    if (a.a_u8) return launch_q<true, false, MODE>(a, s);
+    if (a.b_u8) return launch_q<false, true, MODE>(a, s);
+    return launch_q<false, false, MODE>(a, s);
 }
 
 }  // namespace
@@ -473,7 +593,10 @@ hipError_t launch_qlinear(const QArgs& a, hipStream_t s) {
                      // the DMA path zero-pads a K tail and an odd stage count in LDS, and a
                      // flipped uint8 zero is not zero: uint8 needs an even number of full stages
                      (a.K % (2 * KB) == 0 || (!a.a_u8 && !a.b_u8));
-    return vec ? launch_q_types<true>(a, s) : launch_q_types<false>(a, s);
+    if (!vec) return launch_q_types<0>(a, s);
+    const bool full = a.M % BMQ == 0 && a.N % BNQ == 0 && a.K % KB == 0 && a.K > 0 && a.K <= 32768 &&
+                      a.ldy % 4 == 0;
+    return full ? launch_q_types<2>(a, s) : launch_q_types<1>(a, s);
 }
 
 }  // namespace omm
