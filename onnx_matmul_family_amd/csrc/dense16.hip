@@ -111,25 +111,30 @@ __device__ __forceinline__ void epilogue16(const DenseArgs& p, const f32x16_t (&
 // Epilogue of a tile that lies wholly inside Y (rows 8-byte aligned): no
 // bounds checks.  CM = 0: no C; CM = 1: C constant along m and contiguous
 // along n (a bias row), loaded once per lane for all of its columns.
+// The results leave through LDS: each wave converts its 128 x 128 block into
+// its own 32 KiB (row-major, 256 bytes per row, 16-byte chunk c of row r in
+// slot c ^ (r % 16)) and reads it back as 16-byte lanes, 16 lanes per row, so
+// every store instruction writes 4 whole 256-byte row segments instead of 32
+// scattered 16-byte pieces.  The caller has passed a barrier after the K loop.
 template <int BM, int BN, int DT, int CM>
 __device__ __forceinline__ void epilogue16_full(const DenseArgs& p, const f32x16_t (&acc)[BM / 64][BN / 64],
                                                 uint16_t* __restrict__ Y, int64_t m0, int64_t n0, int lane, int wm,
-                                                int wn) {
+                                                int wn, char* stage) {
     constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+    constexpr int ROWB = WN * 2;          // bytes per staged row
+    constexpr int NCH = ROWB / 16;        // 16-byte chunks per row
     const float alpha = p.alpha;
-    const int64_t nl = n0 + wn * WN + 4 * (lane >> 5);
-    const int64_t ml = m0 + wm * WM + (lane & 31);
+    const int h = lane >> 5;
     // the bias row stays packed (two 16-bit values per register) until its
-    // column block is stored
+    // column block is converted
     u32x2_t craw[TN][4];
     if constexpr (CM == 1) {
-        const uint16_t* __restrict__ Cp = (const uint16_t*)p.C + nl;
+        const uint16_t* __restrict__ Cp = (const uint16_t*)p.C + n0 + wn * WN + 4 * h;
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) craw[j][q] = *(const u32x2_t*)(Cp + 32 * j + 8 * q);
     }
-    uint16_t* __restrict__ yb = Y + ml * p.ldy + nl;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
         float cb[4][4];
@@ -145,7 +150,7 @@ __device__ __forceinline__ void epilogue16_full(const DenseArgs& p, const f32x16
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            uint16_t* __restrict__ yr = yb + 32 * i * p.ldy + 32 * j;
+            const int r = 32 * i + (lane & 31);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 float v[4];
@@ -155,9 +160,19 @@ __device__ __forceinline__ void epilogue16_full(const DenseArgs& p, const f32x16
                 u32x2_t o;
                 o.x = pack2<DT>(v[0], v[1]);
                 o.y = pack2<DT>(v[2], v[3]);
-                *(u32x2_t*)(yr + 8 * q) = o;
+                const int c = 4 * j + q;
+                *(u32x2_t*)(stage + r * ROWB + ((c ^ (r % NCH)) << 4) + (h << 3)) = o;
             }
         }
+    }
+    // read back whole row segments: lane -> row 4 k + lane / 16, chunk lane % 16
+    uint16_t* __restrict__ yb = Y + (m0 + wm * WM) * p.ldy + n0 + wn * WN;
+    constexpr int RPI = 64 / NCH;  // rows per instruction
+#pragma unroll
+    for (int k = 0; k < WM / RPI; ++k) {
+        const int r = RPI * k + lane / NCH, c = lane % NCH;
+        const u32x4_t d = *(const u32x4_t*)(stage + r * ROWB + ((c ^ (r % NCH)) << 4));
+        *(u32x4_t*)(yb + (int64_t)r * p.ldy + 8 * c) = d;
     }
 }
 
@@ -218,9 +233,12 @@ __global__ __launch_bounds__(NT) void dense16_kernel(DenseArgs p, int tiles_m, i
 
     // Epilogue: for each (i, j, q) a lane holds row m = m0 + wm*WM + 32 i + l%32 and
     // the 4 columns n .. n+3, n = n0 + wn*WN + 32 j + 8 q + 4 (l/32).
-    if constexpr (MODE >= 2)
-        epilogue16_full<BM, BN, DT, MODE - 2>(p, acc, Y, m0, n0, lane, wm, wn);
-    else
+    if constexpr (MODE >= 2) {
+        static_assert(BM == 256 && BN == 256, "four 32 KiB wave blocks in the two stage buffers");
+        __syncthreads();  // every wave is done reading the last stage
+        char* stage = (wave < 2 ? smem0 : smem1) + (wave & 1) * (STAGE / 2);
+        epilogue16_full<BM, BN, DT, MODE - 2>(p, acc, Y, m0, n0, lane, wm, wn, stage);
+    } else
         epilogue16<BM, BN, DT, VEC>(p, acc, Y, m0, n0, lane, wm, wn);
 }
 

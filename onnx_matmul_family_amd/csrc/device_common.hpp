@@ -32,23 +32,21 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 //
 // "K-major" tile (operand stored with k contiguous in memory): R rows (m or n)
 // of 128 bytes of k (64 x 16-bit or 128 x 8-bit values) = 8 chunks of 16 bytes.
-// The tile is split into 4 planes, one per MFMA k-block (2 chunks = 32 bytes
-// of k): plane s holds R rows of 32 bytes, and half h of row r sits at half
-// h ^ kswz(r).  A fragment read has lanes 0-31 on 32 consecutive rows and
-// lanes 32-63 on the other half; with kswz any 8 consecutive rows cover all
-// 16-byte slots of a 128-byte window and any 16 rows those of a 256-byte
-// window (no bank conflict with 32 or 64 banks), and every (row block, plane)
-// offset is a compile-time constant from one per-lane base address.
-__device__ __forceinline__ int kswz(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+// Row r occupies bytes 128 r .. 128 r + 127 and its chunk c sits in slot
+// c ^ kswz(r), kswz(r) = (r / 2) % 8.  A fragment read (ds_read_b128) puts 16
+// consecutive lanes on 16 consecutive rows and one chunk; with the xor they
+// cover the 16 slots of a 256-byte window (two rows): no bank conflicts with 64
+// banks.  Any 8 consecutive rows are one 1 KiB block, which one DMA
+// instruction fills from 8 whole 128-byte row segments.
+__device__ __forceinline__ int kswz(int r) { return (r >> 1) & 7; }
 template <int R>
 __device__ __forceinline__ int kmaj_off(int r, int c) {
-    return (c >> 1) * (R * 32) + (r << 5) + (((c & 1) ^ kswz(r)) << 4);
+    return (r << 7) + ((c ^ kswz(r)) << 4);
 }
-// per-lane part of a fragment read at row block `rb` (multiple of 32) in plane s:
-// kmaj_off(rb + l%32, 2 s + l/32) == s*R*32 + rb*32 + kmaj_lane(l)
-__device__ __forceinline__ int kmaj_lane(int lane) {
-    const int r = lane & 31;
-    return (r << 5) + (((lane >> 5) ^ kswz(r)) << 4);
+// per-lane part of a fragment read of chunk 2 s + l/32 at row block rb (a
+// multiple of 32): kmaj_off(rb + l%32, 2 s + l/32) == rb*128 + kmaj_lane(l, s)
+__device__ __forceinline__ int kmaj_lane(int lane, int s) {
+    return ((lane & 31) << 7) + ((((2 * s) + (lane >> 5)) ^ kswz(lane & 31)) << 4);
 }
 
 // "MN-major" tile of 16-bit elements (operand stored with m or n contiguous):

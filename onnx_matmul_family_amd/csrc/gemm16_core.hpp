@@ -172,7 +172,7 @@ __device__ __forceinline__ void store_tile(char* lds, const u32x4_t (&reg)[NC], 
 template <int R, bool KMAJ>
 __device__ __forceinline__ u32x4_t read_frag(const char* lds, int mnb, int s, int lane) {
     if constexpr (KMAJ) {
-        return *(const u32x4_t*)(lds + s * (R * 32) + mnb * 32 + kmaj_lane(lane));
+        return *(const u32x4_t*)(lds + mnb * 128 + kmaj_lane(lane, s));
     } else {
         const int g = lane >> 4, i = lane & 15;
         const int krow = 16 * s + 8 * (g >> 1) + (i >> 2);
@@ -274,17 +274,19 @@ struct DmaCtx {
 
 // One operand tile (R rows along m/n, 128 bytes of k per stage) loaded by DMA.
 // ES = element size in bytes (2: bf16/fp16, 1: int8; MN-major needs ES = 2).
-//  K-major: LDS block b = plane (b / (R/32)), rows 32 (b % (R/32)) .. +31;
-//           lane p -> row p/2, physical half p&1 (logical half (p&1)^kswz).
+//  K-major: LDS block b = rows 8b .. 8b+7; lane p -> row 8b + p/8, slot p%8,
+//           logical chunk (p%8) ^ kswz(row): 8 whole 128-byte row segments
+//           (kswz(row) = 4 (b & 1) + p/16 depends on the block's parity).
 //  MN-major: LDS block b = k rows RPB b .. RPB b + RPB-1 (RPB = 1024 / (2R));
 //           lane p -> row p / LPR, physical 16-byte chunk p % LPR (LPR = R/8),
 //           logical 32-byte granule = physical ^ mswz16(row).
 template <int R, bool KMAJ, int ES = 2>
 struct DmaSrc {
     static_assert(KMAJ || ES == 2, "8-bit MN-major tiles use DmaSrcMN8");
+    static_assert((R / 32) % 2 == 0, "block parity == parity of the wave-local block index");
     static constexpr int NBLK = R / 8;  // 1 KiB blocks per stage
     static constexpr int PER_WAVE = NBLK / 4;
-    static constexpr int RPB = KMAJ ? 32 : 1024 / (2 * R);
+    static constexpr int RPB = KMAJ ? 8 : 1024 / (2 * R);
     static constexpr int LPR = R / 8;
     static constexpr int KE = 128 / ES;  // k elements per stage
     const char* base;   // tile origin at stage 0 (bytes)
@@ -303,7 +305,8 @@ struct DmaSrc {
         if constexpr (KMAJ) {
             base = (const char*)b + mn0 * ld * ES;
             step = 128;
-            lane_off[0] = lane_off[1] = (uint32_t)(lane >> 1) * ldb + ((uint32_t)((lane & 1) ^ kswz(lane >> 1)) << 4);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) lane_off[q] = (uint32_t)(lane >> 3) * ldb + (kchunk(q) << 4);
         } else {
             base = (const char*)b + mn0 * ES;
             step = (int64_t)KE * ld * ES;
@@ -311,6 +314,8 @@ struct DmaSrc {
             for (int q = 0; q < 2; ++q) lane_off[q] = (uint32_t)(lane / LPR) * ldb + (chunk(q) << 4);
         }
     }
+    // K-major: logical 16-byte chunk (along k) of this lane in a block of parity q
+    __device__ uint32_t kchunk(int q) const { return (uint32_t)((lane & 7) ^ kswz(8 * q + (lane >> 3))); }
     // MN-major: logical 16-byte chunk (along m/n) of this lane in a block of parity q
     __device__ uint32_t chunk(int q) const {
         const int row = q * RPB + lane / LPR, C = lane % LPR;
@@ -333,11 +338,10 @@ struct DmaSrc {
             const int b = wave * PER_WAVE + j;
             uint32_t voff;
             if constexpr (KMAJ) {
-                const int s = b / (R / 32), rb = b % (R / 32);
-                voff = lane_off[0] + (uint32_t)(rb * 32) * ldb + (uint32_t)(s * 32);
+                voff = lane_off[j & 1] + (uint32_t)(b * 8) * ldb;
                 if (CHECKED) {
-                    const int64_t row = mn0 + rb * 32 + (lane >> 1);
-                    const int64_t k = (int64_t)kt * KE + (16 / ES) * (2 * s + ((lane & 1) ^ kswz(lane >> 1)));
+                    const int64_t row = mn0 + b * 8 + (lane >> 3);
+                    const int64_t k = (int64_t)kt * KE + (16 / ES) * kchunk(j & 1);
                     if (!(row < MN && k < K)) voff = DMA_OOB;
                 }
             } else {
@@ -405,16 +409,23 @@ struct DmaSrcMN8 {
 };
 
 // K-major A tile whose rows are gathered (grouped product: token rows
-// input[pair / S]).  roff[rb] = byte offset of the row this lane loads in row
-// block rb (DMA_OOB for rows past the tile's valid rows) plus the lane's half.
+// input[pair / S]), same layout as DmaSrc K-major.  Wave w fills blocks
+// w*PER_WAVE + j; roff[j] = byte offset of the row this lane loads in block j
+// (DMA_OOB for rows past the tile's valid rows) plus the lane's chunk.
 template <int R>
 struct GatherDma {
     static constexpr int NBLK = R / 8;
     static constexpr int PER_WAVE = NBLK / 4;
+    static_assert(PER_WAVE % 2 == 0, "block parity == parity of the wave-local block index");
     const char* base;
-    uint32_t roff[R / 32];
+    uint32_t roff[PER_WAVE];
     int64_t K;
     int lane;
+
+    // tile row loaded by this lane in block j of wave w, and its chunk's byte offset
+    __device__ static int row_of(int w, int j, int lane) { return 8 * (w * PER_WAVE + j) + (lane >> 3); }
+    // logical chunk of this lane in block j (kswz of its row depends on j's parity)
+    __device__ static uint32_t chunk(int j, int lane) { return (uint32_t)((lane & 7) ^ kswz(8 * (j & 1) + (lane >> 3))); }
 
     __device__ __forceinline__ DmaCtx ctx(char* lds, int kt, bool live = true) const {
         return DmaCtx{make_rsrc(base + (live ? (int64_t)kt * KSTEP * 2 : 0), live), lds_addr(lds)};
@@ -428,10 +439,9 @@ struct GatherDma {
     template <bool CHECKED>
     __device__ __forceinline__ void one(const DmaCtx& c, int kt, int wave, int j) const {
         const int b = wave * PER_WAVE + j;
-        const int s = b / (R / 32), rb = b % (R / 32);
-        uint32_t voff = roff[rb] + (uint32_t)(s * 32);
+        uint32_t voff = roff[j];
         if (CHECKED) {
-            const int64_t k = (int64_t)kt * KSTEP + 8 * (2 * s + ((lane & 1) ^ kswz(lane >> 1)));
+            const int64_t k = (int64_t)kt * KSTEP + 8 * chunk(j, lane);
             if (k >= K) voff = DMA_OOB;
         }
         dma16u(c.r, c.l0 + b * 1024, voff);
@@ -487,6 +497,27 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
+// Fragment read order within a k-block.  MFMA X of a k-block uses A fragment
+// X / TN (first needed by MFMA i*TN) and B fragment X % TN (first needed by
+// MFMA j); reading the next k-block's fragments in order of first use (B
+// before A on ties) leaves every read the most MFMAs to land.  Fragment ids:
+// 0 .. TM-1 = A, TM .. TM+TN-1 = B.
+constexpr int frag_order(int TM, int TN, int r) {
+    int done[16] = {};
+    int pick = 0;
+    for (int n = 0; n <= r; ++n) {
+        int best = -1, bt = 1 << 20;
+        for (int f = 0; f < TM + TN; ++f) {
+            if (done[f]) continue;
+            const int t = f < TM ? 2 * (f * TN) + 1 : 2 * (f - TM);  // B first on equal times
+            if (t < bt) { bt = t; best = f; }
+        }
+        done[best] = 1;
+        pick = best;
+    }
+    return pick;
+}
+
 // MFMA number X (0 .. TM*TN-1) of a k-block: tile (X / TN, X % TN).
 template <int X, int DT, int TM, int TN, class F>
 __device__ __forceinline__ void mma_one(f32x16_t (&acc)[TM][TN], const F& f) {
@@ -504,7 +535,7 @@ __device__ __forceinline__ void kblock_read(f32x16_t (&acc)[TM][TN], const F& cu
         constexpr int x = decltype(xc)::value;
         mma_one<x, DT>(acc, cur);
         static_for<(x * NR + NM - 1) / NM, ((x + 1) * NR + NM - 1) / NM>([&](auto rc) {
-            nxt.template read_one<decltype(rc)::value>(lds, s, lane, wm, wn);
+            nxt.template read_one<frag_order(TM, TN, decltype(rc)::value)>(lds, s, lane, wm, wn);
         });
         fence_sched();
     });
@@ -538,7 +569,7 @@ __device__ __forceinline__ void kblock_read_dma(f32x16_t (&acc)[TM][TN], const F
         static_for<D0 + (x * ND + NM - 1) / NM, D0 + ((x + 1) * ND + NM - 1) / NM>(
             [&](auto dc) { dma_one<CHECKED, LA, decltype(dc)::value>(srcA, srcB, ca, cb, kt, wave); });
         static_for<(x * NR + NM - 1) / NM, ((x + 1) * NR + NM - 1) / NM>([&](auto rc) {
-            nxt.template read_one<decltype(rc)::value>(lds, s, lane, wm, wn);
+            nxt.template read_one<frag_order(TM, TN, decltype(rc)::value)>(lds, s, lane, wm, wn);
         });
         fence_sched();
     });

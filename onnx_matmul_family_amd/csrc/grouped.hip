@@ -181,11 +181,12 @@ __device__ __forceinline__ void grouped_body(const GroupedArgs& a, const char* w
         srcA.base = (const char*)a.input;
         srcA.K = K;
         srcA.lane = lane;
-        const uint32_t half = (uint32_t)((lane & 1) ^ kswz(lane >> 1)) << 4;
 #pragma unroll
-        for (int rb = 0; rb < GBM / 32; ++rb) {
-            const int r = rb * 32 + (lane >> 1);
-            srcA.roff[rb] = r < rows ? (uint32_t)((int64_t)(sorted[start + r] / S) * K * 2) + half : DMA_OOB;
+        for (int j = 0; j < GatherDma<GBM>::PER_WAVE; ++j) {
+            const int r = GatherDma<GBM>::row_of(wave, j, lane);
+            srcA.roff[j] = r < rows ? (uint32_t)((int64_t)(sorted[start + r] / S) * K * 2) +
+                                          (GatherDma<GBM>::chunk(j, lane) << 4)
+                                    : DMA_OOB;
         }
         DmaSrc<GBN, false> srcB;
         srcB.init(wg, N, n0, N, K, lane);

@@ -100,7 +100,7 @@ __device__ __forceinline__ void stash(char* s, const u32x4_t (&ra)[NC], const u3
 }
 
 __device__ __forceinline__ i32x4_t frag_a(const char* s, int rowb, int ks, int lane) {
-    return *(const i32x4_t*)(s + ks * (BMQ * 32) + rowb * 32 + kmaj_lane(lane));
+    return *(const i32x4_t*)(s + rowb * 128 + kmaj_lane(lane, ks));
 }
 // lane l gets column colb + l%32, k = 32 ks + 16 (l/32) + 0..15
 __device__ __forceinline__ i32x4_t frag_b(const char* s, int colb, int ks, int lane) {
@@ -212,7 +212,7 @@ __device__ __forceinline__ void q_kblock(i32x16_t (&acc)[4][4], int (&rs)[4], in
     static_for<0, 16>([&](auto xc) {
         constexpr int x = decltype(xc)::value;
         q_one<x>(acc, rs, cs, cur);
-        if constexpr ((x & 1) == 0) nxt.template read_one<x / 2>(lds, ks, lane, wm, wn);
+        if constexpr ((x & 1) == 0) nxt.template read_one<core16::frag_order(4, 4, x / 2)>(lds, ks, lane, wm, wn);
         fence_sched();
     });
 }
@@ -232,7 +232,7 @@ __device__ __forceinline__ void q_kblock_dma(i32x16_t (&acc)[4][4], int (&rs)[4]
         q_one<x>(acc, rs, cs, cur);
         static_for<D0 + (x * ND + 15) / 16, D0 + ((x + 1) * ND + 15) / 16>(
             [&](auto dc) { dma_one<CHECKED, LA, decltype(dc)::value>(sa, sb, ca, cb, kt, wave); });
-        if constexpr ((x & 1) == 0) nxt.template read_one<x / 2>(lds, ks, lane, wm, wn);
+        if constexpr ((x & 1) == 0) nxt.template read_one<core16::frag_order(4, 4, x / 2)>(lds, ks, lane, wm, wn);
         fence_sched();
     });
 }
