@@ -108,74 +108,6 @@ __device__ __forceinline__ void epilogue16(const DenseArgs& p, const f32x16_t (&
     }
 }
 
-// Epilogue of a tile that lies wholly inside Y (rows 8-byte aligned): no
-// bounds checks.  CM = 0: no C; CM = 1: C constant along m and contiguous
-// along n (a bias row), loaded once per lane for all of its columns.
-// The results leave through LDS: each wave converts its 128 x 128 block into
-// its own 32 KiB (row-major, 256 bytes per row, 16-byte chunk c of row r in
-// slot c ^ (r % 16)) and reads it back as 16-byte lanes, 16 lanes per row, so
-// every store instruction writes 4 whole 256-byte row segments instead of 32
-// scattered 16-byte pieces.  The caller has passed a barrier after the K loop.
-template <int BM, int BN, int DT, int CM>
-__device__ __forceinline__ void epilogue16_full(const DenseArgs& p, const f32x16_t (&acc)[BM / 64][BN / 64],
-                                                uint16_t* __restrict__ Y, int64_t m0, int64_t n0, int lane, int wm,
-                                                int wn, char* stage) {
-    constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
-    constexpr int ROWB = WN * 2;          // bytes per staged row
-    constexpr int NCH = ROWB / 16;        // 16-byte chunks per row
-    const float alpha = p.alpha;
-    const int h = lane >> 5;
-    // the bias row stays packed (two 16-bit values per register) until its
-    // column block is converted
-    u32x2_t craw[TN][4];
-    if constexpr (CM == 1) {
-        const uint16_t* __restrict__ Cp = (const uint16_t*)p.C + n0 + wn * WN + 4 * h;
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) craw[j][q] = *(const u32x2_t*)(Cp + 32 * j + 8 * q);
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        float cb[4][4];
-        if constexpr (CM == 1) {
-            const float beta = p.beta;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                cb[q][0] = beta * from_bits<DT>((uint16_t)craw[j][q].x);
-                cb[q][1] = beta * from_bits<DT>((uint16_t)(craw[j][q].x >> 16));
-                cb[q][2] = beta * from_bits<DT>((uint16_t)craw[j][q].y);
-                cb[q][3] = beta * from_bits<DT>((uint16_t)(craw[j][q].y >> 16));
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int r = 32 * i + (lane & 31);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    v[e] = CM == 1 ? alpha * acc[i][j][4 * q + e] + cb[q][e] : alpha * acc[i][j][4 * q + e];
-                u32x2_t o;
-                o.x = pack2<DT>(v[0], v[1]);
-                o.y = pack2<DT>(v[2], v[3]);
-                const int c = 4 * j + q;
-                *(u32x2_t*)(stage + r * ROWB + ((c ^ (r % NCH)) << 4) + (h << 3)) = o;
-            }
-        }
-    }
-    // read back whole row segments: lane -> row 4 k + lane / 16, chunk lane % 16
-    uint16_t* __restrict__ yb = Y + (m0 + wm * WM) * p.ldy + n0 + wn * WN;
-    constexpr int RPI = 64 / NCH;  // rows per instruction
-#pragma unroll
-    for (int k = 0; k < WM / RPI; ++k) {
-        const int r = RPI * k + lane / NCH, c = lane % NCH;
-        const u32x4_t d = *(const u32x4_t*)(stage + r * ROWB + ((c ^ (r % NCH)) << 4));
-        *(u32x4_t*)(yb + (int64_t)r * p.ldy + 8 * c) = d;
-    }
-}
-
 // MODE 0: register-staged loads, any shape.  MODE 1: DMA loads, ragged edge
 // tiles handled in the loads and the epilogue.  MODE 2 / 3: DMA loads, every
 // tile full and K a multiple of the K step (checked on the host), epilogue
@@ -236,8 +168,16 @@ __global__ __launch_bounds__(NT) void dense16_kernel(DenseArgs p, int tiles_m, i
     if constexpr (MODE >= 2) {
         static_assert(BM == 256 && BN == 256, "four 32 KiB wave blocks in the two stage buffers");
         __syncthreads();  // every wave is done reading the last stage
+        // full tile, no bounds checks; the results leave through LDS as whole
+        // row segments.  MODE 3: C is a bias row (constant along m, contiguous
+        // along n).
         char* stage = (wave < 2 ? smem0 : smem1) + (wave & 1) * (STAGE / 2);
-        epilogue16_full<BM, BN, DT, MODE - 2>(p, acc, Y, m0, n0, lane, wm, wn, stage);
+        const int64_t col0 = n0 + wn * (BN / 2);
+        const uint16_t* bias = MODE == 3 ? (const uint16_t*)p.C + col0 : nullptr;
+        uint16_t* yb = Y + (m0 + wm * (BM / 2)) * p.ldy + col0;
+        const int64_t ldy = p.ldy;
+        wave_epilogue_lds<DT, MODE == 3>(acc, p.alpha, bias, p.beta, stage, lane,
+                              [&](int r) -> uint16_t* { return yb + r * ldy; });
     } else
         epilogue16<BM, BN, DT, VEC>(p, acc, Y, m0, n0, lane, wm, wn);
 }

@@ -633,5 +633,66 @@ __device__ __forceinline__ void mainloop_dma(f32x16_t (&acc)[BM / 64][BN / 64], 
     wait_vm<0>();
 }
 
+// Epilogue of one wave's 128 x 128 block of 16-bit results through LDS.  The
+// values alpha * acc + beta * bias[col] are converted and written to `stage`
+// (this wave's 32 KiB: row-major, 256 bytes per row, 16-byte chunk c of row r
+// in slot c ^ (r % 16)), then read back as 16-byte lanes, 16 lanes per row,
+// and stored to rowp(r) (the block row's first column; nullptr skips the row)
+// so that every store instruction writes 4 whole 256-byte row segments.
+// BIAS: bias holds the block's 128 column values; otherwise no term is added
+// (not even beta * 0).  The caller has synchronised the workgroup since the
+// last read of `stage` as a K buffer.
+template <int DT, bool BIAS, class RowPtr>
+__device__ __forceinline__ void wave_epilogue_lds(const f32x16_t (&acc)[4][4], float alpha, const uint16_t* bias,
+                                                  float beta, char* stage, int lane, RowPtr&& rowp) {
+    constexpr int ROWB = 256, NCH = 16;
+    const int h = lane >> 5;
+    // the bias stays packed (two 16-bit values per register) until its column
+    // block is converted
+    u32x2_t craw[4][4];
+    if constexpr (BIAS) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) craw[j][q] = *(const u32x2_t*)(bias + 32 * j + 8 * q + 4 * h);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float cb[4][4];
+        if constexpr (BIAS) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                cb[q][0] = beta * from_bits<DT>((uint16_t)craw[j][q].x);
+                cb[q][1] = beta * from_bits<DT>((uint16_t)(craw[j][q].x >> 16));
+                cb[q][2] = beta * from_bits<DT>((uint16_t)craw[j][q].y);
+                cb[q][3] = beta * from_bits<DT>((uint16_t)(craw[j][q].y >> 16));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 32 * i + (lane & 31);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[e] = BIAS ? alpha * acc[i][j][4 * q + e] + cb[q][e] : alpha * acc[i][j][4 * q + e];
+                u32x2_t o;
+                o.x = pack2<DT>(v[0], v[1]);
+                o.y = pack2<DT>(v[2], v[3]);
+                const int c = 4 * j + q;
+                *(u32x2_t*)(stage + r * ROWB + ((c ^ (r % NCH)) << 4) + (h << 3)) = o;
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+        const int r = 4 * k + (lane >> 4), c = lane & 15;
+        const u32x4_t d = *(const u32x4_t*)(stage + r * ROWB + ((c ^ (r % NCH)) << 4));
+        uint16_t* dst = rowp(r);
+        if (dst) *(u32x4_t*)(dst + 8 * c) = d;
+    }
+}
+
 }  // namespace core16
 }  // namespace omm

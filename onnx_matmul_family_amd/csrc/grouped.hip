@@ -156,7 +156,7 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(const void* idx, int
 // rows / columns / K with zeros); otherwise element-wise register-staged loads.
 template <int DT, bool VEC>
 __device__ __forceinline__ void grouped_body(const GroupedArgs& a, const char* ws, int tile, int tn, char* s0,
-                                             char* s1) {
+                                             char* s1, int* orow_s) {
     const int4 te = ((const int4*)(ws + off_tiles(a.G)))[tile];
     const int g = te.x, start = te.y, rows = te.z;
     const int* sorted = (const int*)(ws + off_sorted(a.M * a.S, a.G));
@@ -175,6 +175,7 @@ __device__ __forceinline__ void grouped_body(const GroupedArgs& a, const char* w
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     const int nk = (int)((K + KSTEP - 1) / KSTEP);
     const uint16_t* wg = (const uint16_t*)a.weights + (int64_t)g * K * N;
+    if (t < GBM) orow_s[t] = t < rows ? sorted[start + t] : -1;
 
     if constexpr (VEC) {
         GatherDma<GBM> srcA;
@@ -217,8 +218,28 @@ __device__ __forceinline__ void grouped_body(const GroupedArgs& a, const char* w
         mainloop<GBM, GBN, DT, true, false, 2>(acc, s0, s1, srcA, srcB, nk, t, lane, wm, wn);
     }
 
-    // Epilogue: + bias[g] (loaded once per lane for all its columns, before any
-    // store), one rounding, each row to output[pair].
+    // Epilogue: + bias[g], one rounding, each row to output[pair].
+    if constexpr (VEC) {
+        // whole 256-column tile with 16-byte aligned rows: through LDS as
+        // whole row segments (orow_s was filled before the K loop's barriers)
+        if (n0 + GBN <= N && N % 8 == 0 && ((uintptr_t)a.output & 15) == 0) {
+            __syncthreads();  // every wave is done reading the last stage
+            char* stage = (wave < 2 ? s0 : s1) + (wave & 1) * (GBM * KSTEP * 2);
+            const int64_t col0 = n0 + wn * (GBN / 2);
+            uint16_t* out = (uint16_t*)a.output + col0;
+            const int* orow_w = orow_s + wm * (GBM / 2);
+            auto rowp = [&](int r) -> uint16_t* {
+                const int o = orow_w[r];
+                return o >= 0 ? out + (int64_t)o * N : nullptr;
+            };
+            if (a.bias)
+                wave_epilogue_lds<DT, true>(acc, 1.0f, (const uint16_t*)a.bias + (int64_t)g * N + col0, 1.0f, stage,
+                                            lane, rowp);
+            else
+                wave_epilogue_lds<DT, false>(acc, 1.0f, nullptr, 1.0f, stage, lane, rowp);
+            return;
+        }
+    }
     const uint16_t* __restrict__ bias = a.bias ? (const uint16_t*)a.bias + (int64_t)g * N : nullptr;
     uint16_t* __restrict__ out = (uint16_t*)a.output;
     const bool vec_store = VEC && (N % 4 == 0);
@@ -281,13 +302,14 @@ template <int DT, bool VEC>
 __global__ __launch_bounds__(256) void grouped16_kernel(GroupedArgs a, const char* ws, int max_mtiles, int tiles_n) {
     __shared__ __attribute__((aligned(1024))) char s0[(GBM + GBN) * core16::KSTEP * 2];
     __shared__ __attribute__((aligned(1024))) char s1[(GBM + GBN) * core16::KSTEP * 2];
+    __shared__ int orow_s[GBM];
     const int total = max_mtiles * tiles_n;
     const int w = xcd_remap((int)blockIdx.x, total);
     int tm, tn;
     grouped_order(w, max_mtiles, tiles_n, 4, tm, tn);
     const int ntiles = ((const int*)ws)[0];
     if (tm >= ntiles) return;
-    grouped_body<DT, VEC>(a, ws, tm, tn, s0, s1);
+    grouped_body<DT, VEC>(a, ws, tm, tn, s0, s1, orow_s);
 }
 
 // fp32: one workgroup per (pair, 256 columns); plain fp32 dot products.

@@ -375,11 +375,15 @@ __device__ __forceinline__ void q_epilogue(const QArgs& p, const i32x16_t (&acc)
 // quotient (Markstein) when nothing underflows or overflows; the caller takes
 // this branch only when every scale of the tile and sy lie in [2^-30, 2^30]
 // in magnitude (or are zero), which keeps every intermediate normal.
+// The bytes leave through LDS (stage: this wave's 16 KiB; row r of 128 bytes,
+// 16-byte chunk c in slot c ^ (r / 2 % 8)): 16-byte stores of whole 128-byte
+// row segments instead of 4-byte pieces.
 template <bool MARK>
 __device__ __forceinline__ void q_epilogue_full(const QArgs& p, const i32x16_t (&acc)[4][4], uint8_t* __restrict__ y,
                                                 const uint32_t* U, const int* ZA, const float* SA, const uint32_t* CB,
                                                 const int* ZB, const float* SB, int64_t m0, int64_t n0, int lane,
-                                                int wm, int wn, float sy, float zyf, float lo, float hi) {
+                                                int wm, int wn, float sy, float zyf, float lo, float hi,
+                                                char* stage) {
     constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
     const float r = 1.0f / sy;
     const float tlo = MAGIC + lo, thi = MAGIC + hi;
@@ -392,7 +396,7 @@ __device__ __forceinline__ void q_epilogue_full(const QArgs& p, const i32x16_t (
         nza[i] = -ZA[mloc];
         sa[i] = SA[mloc];
     }
-    uint8_t* __restrict__ yb = y + (m0 + wm * 128 + (lane & 31)) * p.ldy + n0 + wn * 128 + 4 * (lane >> 5);
+    const int h = lane >> 5;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -424,9 +428,19 @@ __device__ __forceinline__ void q_epilogue_full(const QArgs& p, const i32x16_t (
                 // low bytes of the four results, in order, into one dword
                 const uint32_t lo2 = __builtin_amdgcn_perm(bytes[1], bytes[0], 0x0c0c0400u);
                 const uint32_t hi2 = __builtin_amdgcn_perm(bytes[3], bytes[2], 0x0c0c0400u);
-                *(uint32_t*)(yb + (int64_t)32 * i * p.ldy + 32 * j + 8 * q) = lo2 | (hi2 << 16);
+                const int r = 32 * i + (lane & 31), c = 2 * j + (q >> 1);
+                *(uint32_t*)(stage + r * 128 + ((c ^ ((r >> 1) & 7)) << 4) + ((q & 1) << 3) + (h << 2)) =
+                    lo2 | (hi2 << 16);
             }
         }
+    }
+    // whole 128-byte row segments: lane -> row 8 k + lane / 8, chunk lane % 8
+    uint8_t* __restrict__ yb = y + (m0 + wm * 128) * p.ldy + n0 + wn * 128;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int r = 8 * k + (lane >> 3), c = lane & 7;
+        const u32x4_t d = *(const u32x4_t*)(stage + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
+        *(u32x4_t*)(yb + (int64_t)r * p.ldy + 16 * c) = d;
     }
 }
 
@@ -547,10 +561,13 @@ __global__ __launch_bounds__(NT) void qlinear_kernel(QArgs p, int tiles_m, int t
     const float zyf = (float)(p.y_u8 ? (int)((const uint8_t*)p.y_zp)[0] : (int)((const int8_t*)p.y_zp)[0]);
     const float lo = p.y_u8 ? 0.0f : -128.0f, hi = p.y_u8 ? 255.0f : 127.0f;
     if constexpr (MODE == 2) {
+        // the per-row / per-column terms live in smem; each wave stages its
+        // output block in its own quarter of smem1 (free since the K loop ended)
+        char* stage = smem1 + wave * (STAGE / 4);
         if (scales_ok)
-            q_epilogue_full<true>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi);
+            q_epilogue_full<true>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi, stage);
         else
-            q_epilogue_full<false>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi);
+            q_epilogue_full<false>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi, stage);
     } else {
         const bool vec_store = VEC && (N % 4 == 0) && (p.ldy % 4 == 0);
         // |U| <= 256 K and |colsum| <= 128 K: below 2^23 for K <= 32768, where the
