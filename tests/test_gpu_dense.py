@@ -172,3 +172,29 @@ def test_gemm_on_side_stream_and_reuse():
         Y2 = om.gemm(dA, dB, None, 1.0, 0.0)
     s.synchronize()
     assert torch.equal(Y1, Y2)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("tA,tB", [(0, 1), (0, 0), (1, 0), (1, 1)])
+@pytest.mark.parametrize("cform", ["none", "row", "matrix"])
+def test_full_tile_modes_exact(dt, tA, tB, cform):
+    """Every tile whole (the epilogue without bounds checks, staged through
+    LDS): no C, a bias row, and a full C (general epilogue).  Small integers
+    make every sum exact, so sampled outputs must match bit for bit."""
+    rng = np.random.default_rng(300 + 2 * tA + tB + len(cform))
+    M, N, K = 4096, 4096, 64
+    # |sum| <= 64 + 8: every partial sum and result is an integer exact in bf16
+    A = synth.store(synth.small_ints(rng, (K, M) if tA else (M, K), -1, 1), dt)
+    B = synth.store(synth.small_ints(rng, (N, K) if tB else (K, N), -1, 1), dt)
+    C = None
+    if cform == "row":
+        C = synth.store(synth.small_ints(rng, (N,), -8, 8), dt)
+    elif cform == "matrix":
+        C = synth.store(synth.small_ints(rng, (M, N), -8, 8), dt)
+    Y = om.gemm(dev(A, dt), dev(B, dt), dev(C, dt) if C is not None else None, 1.0, 1.0, tA, tB)
+    torch.cuda.synchronize()
+    sel = sample_indices(M * N, 20000, 7)
+    y, _ = oracle.gemm(A, B, C, 1.0, 1.0, tA, tB, dt=dt, sel=sel)
+    got = host_f64(Y).ravel()[sel]
+    assert np.array_equal(got, y), np.argwhere(got != y)[:5]
+    assert torch.isfinite(Y.float()).all()

@@ -119,3 +119,33 @@ def test_saturation_and_wraparound():
     b = np.full((64, 2), 127, np.int8)
     got, ref = run(a, 1.0, np.array(0, np.int8), b, 1.0, np.array(0, np.int8), 1.0, np.array(0, np.int8))
     assert np.array_equal(got, ref) and (got == 127).all()
+
+
+@pytest.mark.parametrize("ta,tb", [(np.int8, np.int8), (np.uint8, np.int8), (np.int8, np.uint8), (np.uint8, np.uint8)])
+@pytest.mark.parametrize("scales", ["tame", "tiny", "huge", "zeros"])
+def test_full_tiles_scale_ranges(ta, tb, scales):
+    """Whole 256x256 tiles (the fast requantisation path): scales inside and
+    outside the range where the corrected reciprocal divide is used, and zero
+    scales, all bit-exact against the oracle's true division."""
+    rng = np.random.default_rng(501 + len(scales) + 3 * (ta == np.uint8) + 7 * (tb == np.uint8))
+    M, N, K = 512, 768, 512
+    a, b = rint(rng, (M, K), ta), rint(rng, (K, N), tb)
+    zlo = lambda d: 0 if d == np.uint8 else -16
+    zhi = lambda d: 32 if d == np.uint8 else 16
+    az, bz = rint(rng, (M, 1), ta, zlo(ta), zhi(ta)), rint(rng, (1, N), tb, zlo(tb), zhi(tb))
+    asc = synth.uniform(rng, (M, 1), 0.002, 0.01)
+    bsc = synth.uniform(rng, (1, N), 0.002, 0.01)
+    # uint8 operands sit far from their zero points: a larger y_scale keeps y off the rails
+    ys = np.float32(0.05 * (64 if (ta == np.uint8 or tb == np.uint8) else 1))
+    if scales == "tiny":     # products near 2^-80: outside the fast range
+        asc, bsc, ys = asc * np.float32(2.0 ** -32), bsc * np.float32(2.0 ** -32), ys * np.float32(2.0 ** -64)
+    elif scales == "huge":   # a scale beyond 2^30
+        asc = asc * np.float32(2.0 ** 40)
+        ys = ys * np.float32(2.0 ** 40)
+    elif scales == "zeros":
+        asc[::7] = 0.0
+        bsc[:, ::5] = 0.0
+    got, ref = run(a, asc, az, b, bsc, bz, ys, np.array(5 if ta == np.int8 else 9, np.int8))
+    assert np.array_equal(got, ref), (scales, np.argwhere(got != ref)[:5])
+    if scales != "zeros":
+        assert len(np.unique(got)) > 50  # the test is not trivially saturated
