@@ -177,9 +177,9 @@ __device__ __forceinline__ u32x4_t read_frag(const char* lds, int mnb, int s, in
         const int g = lane >> 4, i = lane & 15;
         const int krow = 16 * s + 8 * (g >> 1) + (i >> 2);
         const int n = mnb + 16 * (g & 1) + 4 * (i & 3);
-        const int off = mmaj16_off<R * 2>(krow, n * 2);
+        const int off = mmaj16_off<R * 2>(krow, n * 2), off4 = mmaj16_off<R * 2>(krow + 4, n * 2);
         i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(OMM_LDS(i16x4_t, lds + off));
-        i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(OMM_LDS(i16x4_t, lds + off + 4 * R * 2));
+        i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(OMM_LDS(i16x4_t, lds + off4));
         u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
         return u32x4_t{l2.x, l2.y, h2.x, h2.y};
     }
@@ -288,11 +288,14 @@ struct DmaSrc {
     static constexpr int PER_WAVE = NBLK / 4;
     static constexpr int RPB = KMAJ ? 8 : 1024 / (2 * R);
     static constexpr int LPR = R / 8;
+    // MN-major: the swizzle repeats every 8 rows, so blocks come in 8 / RPB phases
+    static constexpr int NQ = KMAJ ? 2 : (8 / RPB > 1 ? 8 / RPB : 1);
+    static_assert(KMAJ || PER_WAVE % NQ == 0, "block phase == phase of the wave-local block index");
     static constexpr int KE = 128 / ES;  // k elements per stage
     const char* base;   // tile origin at stage 0 (bytes)
     int64_t step;       // bytes per stage
     uint32_t ldb;       // row stride as stored (bytes)
-    uint32_t lane_off[2];
+    uint32_t lane_off[NQ];
     int64_t MN, K, mn0;
     int lane;
 
@@ -311,12 +314,12 @@ struct DmaSrc {
             base = (const char*)b + mn0 * ES;
             step = (int64_t)KE * ld * ES;
 #pragma unroll
-            for (int q = 0; q < 2; ++q) lane_off[q] = (uint32_t)(lane / LPR) * ldb + (chunk(q) << 4);
+            for (int q = 0; q < NQ; ++q) lane_off[q] = (uint32_t)(lane / LPR) * ldb + (chunk(q) << 4);
         }
     }
     // K-major: logical 16-byte chunk (along k) of this lane in a block of parity q
     __device__ uint32_t kchunk(int q) const { return (uint32_t)((lane & 7) ^ kswz(8 * q + (lane >> 3))); }
-    // MN-major: logical 16-byte chunk (along m/n) of this lane in a block of parity q
+    // MN-major: logical 16-byte chunk (along m/n) of this lane in a block of phase q
     __device__ uint32_t chunk(int q) const {
         const int row = q * RPB + lane / LPR, C = lane % LPR;
         return (uint32_t)(2 * ((C >> 1) ^ mswz16(row)) + (C & 1));
@@ -345,10 +348,10 @@ struct DmaSrc {
                     if (!(row < MN && k < K)) voff = DMA_OOB;
                 }
             } else {
-                voff = lane_off[j & 1] + (uint32_t)(b * RPB) * ldb;
+                voff = lane_off[j % NQ] + (uint32_t)(b * RPB) * ldb;
                 if (CHECKED) {
                     const int64_t k = (int64_t)kt * KE + b * RPB + lane / LPR;
-                    const int64_t mn = mn0 + 8 * (int64_t)chunk(j & 1);
+                    const int64_t mn = mn0 + 8 * (int64_t)chunk(j % NQ);
                     if (!(k < K && mn < MN)) voff = DMA_OOB;
                 }
             }
