@@ -5,6 +5,8 @@
 // fp32 accumulation, one round-to-nearest-even conversion to the output type.
 // The K loop is the shared MFMA core; this file adds the batch / tile mapping
 // and the alpha-beta-C epilogue, which stores 4 consecutive outputs per lane.
+#include <algorithm>
+
 #include "gemm16_core.hpp"
 #include "kernels.hpp"
 
@@ -108,10 +110,43 @@ __device__ __forceinline__ void epilogue16(const DenseArgs& p, const f32x16_t (&
     }
 }
 
+// fp32 partial sums of a split-K workgroup: the lane's 4 consecutive columns
+// of each (i, j, q) go to ws[split][z] (row-major M x N)
+template <int BM, int BN>
+__device__ __forceinline__ void store_partial(const DenseArgs& p, const f32x16_t (&acc)[BM / 64][BN / 64],
+                                              float* __restrict__ ws, int64_t m0, int64_t n0, int lane, int wm,
+                                              int wn) {
+    constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+    const int64_t M = p.M, N = p.N;
+    const int64_t nl = n0 + wn * WN + 4 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int64_t m = m0 + wm * WM + 32 * i + (lane & 31);
+        if (m >= M) continue;
+        float* __restrict__ row = ws + m * N;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t n = nl + 32 * j + 8 * q;
+                if (N % 4 == 0 && n < N) {
+                    *(f32x4_t*)(row + n) = f32x4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                                   acc[i][j][4 * q + 3]};
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) row[n + e] = acc[i][j][4 * q + e];
+                }
+            }
+    }
+}
+
 // MODE 0: register-staged loads, any shape.  MODE 1: DMA loads, ragged edge
 // tiles handled in the loads and the epilogue.  MODE 2 / 3: DMA loads, every
 // tile full and K a multiple of the K step (checked on the host), epilogue
-// without bounds checks, with no C (2) or a bias row C (3).
+// without bounds checks, with no C (2) or a bias row C (3).  MODE 4: split-K,
+// DMA loads over one K range, fp32 partial tile to the workspace (the
+// reduction kernel applies alpha, beta and C).
 template <int BM, int BN, int DT, bool AK, bool BKM, int MODE>
 __global__ __launch_bounds__(NT) void dense16_kernel(DenseArgs p, int tiles_m, int tiles_n) {
     constexpr bool VEC = MODE != 0;
@@ -125,15 +160,29 @@ __global__ __launch_bounds__(NT) void dense16_kernel(DenseArgs p, int tiles_m, i
 
     const int T = tiles_m * tiles_n;
     const int w = xcd_remap((int)blockIdx.x, (int)gridDim.x);
-    const int z = w / T;
+    int z = w / T;
     int tm, tn;
     grouped_order(w - z * T, tiles_m, tiles_n, 4, tm, tn);
+    int split = 0;
+    if constexpr (MODE == 4) {
+        const int NB = (int)(p.nb0 * p.nb1);
+        split = z / NB;
+        z -= split * NB;
+    }
     const int64_t z0 = z / p.nb1, z1 = z - z0 * p.nb1;
     const uint16_t* __restrict__ A = (const uint16_t*)p.A + z0 * p.a_bs0 + z1 * p.a_bs1;
     const uint16_t* __restrict__ B = (const uint16_t*)p.B + z0 * p.b_bs0 + z1 * p.b_bs1;
     uint16_t* __restrict__ Y = (uint16_t*)p.Y + z0 * p.y_bs0 + z1 * p.y_bs1;
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-    const int64_t M = p.M, N = p.N, K = p.K;
+    const int64_t M = p.M, N = p.N;
+    int64_t K = p.K;
+    if constexpr (MODE == 4) {
+        // this workgroup's K range; the operands start at its first k
+        const int64_t k0 = split * p.kchunk;
+        K = min(p.K - k0, p.kchunk);
+        A += AK ? k0 : k0 * p.lda;
+        B += BKM ? k0 : k0 * p.ldb;
+    }
 
     f32x16_t acc[TM][TN];
 #pragma unroll
@@ -149,7 +198,7 @@ __global__ __launch_bounds__(NT) void dense16_kernel(DenseArgs p, int tiles_m, i
         DmaSrc<BN, BKM> srcB;
         srcA.init(A, p.lda, m0, M, K, lane);
         srcB.init(B, p.ldb, n0, N, K, lane);
-        if constexpr (MODE >= 2)
+        if constexpr (MODE == 2 || MODE == 3)
             mainloop_dma<BM, BN, DT, AK, BKM, false>(acc, smem0, smem1, srcA, srcB, nk, lane, wm, wn, wave);
         else if ((m0 + BM <= M) && (n0 + BN <= N) && (K % KSTEP == 0))
             mainloop_dma<BM, BN, DT, AK, BKM, false>(acc, smem0, smem1, srcA, srcB, nk, lane, wm, wn, wave);
@@ -165,7 +214,10 @@ __global__ __launch_bounds__(NT) void dense16_kernel(DenseArgs p, int tiles_m, i
 
     // Epilogue: for each (i, j, q) a lane holds row m = m0 + wm*WM + 32 i + l%32 and
     // the 4 columns n .. n+3, n = n0 + wn*WN + 32 j + 8 q + 4 (l/32).
-    if constexpr (MODE >= 2) {
+    if constexpr (MODE == 4) {
+        const int64_t NB = p.nb0 * p.nb1;
+        store_partial<BM, BN>(p, acc, p.ws + ((int64_t)split * NB + z) * M * N, m0, n0, lane, wm, wn);
+    } else if constexpr (MODE >= 2) {
         static_assert(BM == 256 && BN == 256, "four 32 KiB wave blocks in the two stage buffers");
         __syncthreads();  // every wave is done reading the last stage
         // full tile, no bounds checks; the results leave through LDS as whole
@@ -182,10 +234,26 @@ __global__ __launch_bounds__(NT) void dense16_kernel(DenseArgs p, int tiles_m, i
         epilogue16<BM, BN, DT, VEC>(p, acc, Y, m0, n0, lane, wm, wn);
 }
 
+// Split-K reduction: Y = alpha * sum_s ws[s] + beta * C, the partial sums
+// added in split order (deterministic), one output element per thread.
+template <int DT>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(DenseArgs p) {
+    const int64_t MN = p.M * p.N, NB = p.nb0 * p.nb1;
+    const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (f >= NB * MN) return;
+    const int64_t z = f / MN, mn = f - z * MN, m = mn / p.N, n = mn - m * p.N;
+    float acc = 0.0f;
+    for (int s = 0; s < p.splits; ++s) acc += p.ws[(s * NB + z) * MN + mn];
+    float v = p.alpha * acc;
+    if (p.C) v += p.beta * from_bits<DT>(((const uint16_t*)p.C)[m * p.c_sm + n * p.c_sn]);
+    const int64_t z0 = z / p.nb1, z1 = z - z0 * p.nb1;
+    ((uint16_t*)p.Y)[z0 * p.y_bs0 + z1 * p.y_bs1 + m * p.ldy + n] = to_bits<DT>(v);
+}
+
 template <int BM, int BN, int DT, bool AK, bool BKM, int MODE>
 hipError_t launch_cfg(const DenseArgs& a, hipStream_t s) {
     const int64_t tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
-    const int64_t total = tiles_m * tiles_n * a.nb0 * a.nb1;
+    const int64_t total = tiles_m * tiles_n * a.nb0 * a.nb1 * (MODE == 4 ? a.splits : 1);
     if (total <= 0) return hipSuccess;
     if (total > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL((dense16_kernel<BM, BN, DT, AK, BKM, MODE>), dim3((unsigned)total), dim3(NT), 0, s, a,
@@ -223,6 +291,31 @@ hipError_t launch_dt(const DenseArgs& a, hipStream_t s) {
         if (full && !a.C) return launch_layout<256, 256, DT, 2>(a, s);
         if (full && a.c_sm == 0 && a.c_sn == 1 && ((uintptr_t)a.C & 7) == 0) return launch_layout<256, 256, DT, 3>(a, s);
         return launch_layout<256, 256, DT, 1>(a, s);
+    }
+    // Few output tiles and a long K: split K over several workgroups per tile
+    // so that the whole chip streams the operands, then reduce.
+    const int64_t NB = a.nb0 * a.nb1;
+    const int64_t t128 = ((a.M + 127) / 128) * ((a.N + 127) / 128) * NB;
+    if (vec && t128 < 128 && a.K >= 2048) {
+        int64_t S = std::min<int64_t>(std::min<int64_t>(512 / t128, a.K / 512), 32);
+        if (S >= 2) {
+            const int64_t kchunk = ((a.K + S - 1) / S + KSTEP - 1) / KSTEP * KSTEP;
+            S = (a.K + kchunk - 1) / kchunk;
+            const int64_t elems = NB * a.M * a.N;
+            DenseArgs b = a;
+            b.kchunk = kchunk;
+            b.splits = (int)S;
+            hipError_t e = hipMallocAsync((void**)&b.ws, (size_t)(S * elems) * sizeof(float), s);
+            if (e != hipSuccess) return e;
+            e = launch_layout<128, 128, DT, 4>(b, s);
+            if (e == hipSuccess) {
+                hipLaunchKernelGGL(splitk_reduce_kernel<DT>, dim3((unsigned)((elems + 255) / 256)), dim3(256), 0, s,
+                                   b);
+                e = hipGetLastError();
+            }
+            const hipError_t f = hipFreeAsync(b.ws, s);
+            return e != hipSuccess ? e : f;
+        }
     }
     if (vec) return launch_layout<128, 128, DT, 1>(a, s);
     return launch_layout<128, 128, DT, 0>(a, s);

@@ -24,6 +24,11 @@ struct DenseArgs {
     float alpha, beta;
     int a_kmajor;           // 1: A stored (M,K) with k contiguous; 0: stored (K,M)
     int b_kmajor;           // 1: B stored (N,K) with k contiguous; 0: stored (K,N)
+    // split-K (set by the launcher): partial products of K range
+    // [s*kchunk, (s+1)*kchunk) go to ws[s][batch][M][N] (fp32)
+    float* ws;
+    int64_t kchunk;
+    int splits;
 };
 
 // Quantised product.  Parameter offsets follow the same two batch levels plus

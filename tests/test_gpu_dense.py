@@ -198,3 +198,44 @@ def test_full_tile_modes_exact(dt, tA, tB, cform):
     got = host_f64(Y).ravel()[sel]
     assert np.array_equal(got, y), np.argwhere(got != y)[:5]
     assert torch.isfinite(Y.float()).all()
+
+
+SPLITK = [  # (A shape, B shape, transA, transB): few output tiles, long K -> split-K path
+    ((64, 8192), (8192, 4096), 0, 0), ((64, 8192), (4096, 8192), 0, 1), ((8192, 96), (8192, 1024), 1, 0),
+    ((200, 4104), (4104, 320), 0, 0), ((1, 6144), (6144, 2048), 0, 0),
+]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("sa,sb,tA,tB", SPLITK)
+def test_gemm_split_k(dt, sa, sb, tA, tB):
+    """Long-K, few-tile shapes: partial products over K ranges, reduced in a
+    second kernel with the alpha / beta / C epilogue (ragged last K range for
+    K = 4104)."""
+    rng = np.random.default_rng(sum(sa) + sum(sb) + tA + tB)
+    A = synth.store(synth.normal(rng, sa, 0.05), dt)
+    B = synth.store(synth.normal(rng, sb, 0.05), dt)
+    N = sb[0] if tB else sb[1]
+    C = synth.store(synth.uniform(rng, (N,), -0.1, 0.1), dt)
+    Y = om.gemm(dev(A, dt), dev(B, dt), dev(C, dt), 0.5, -1.5, tA, tB)
+    torch.cuda.synchronize()
+    M = Y.shape[0]
+    sel = sample_indices(M * N, 20000, 8)
+    y, t = oracle.gemm(A, B, C, 0.5, -1.5, tA, tB, dt=dt, sel=sel)
+    c64 = C.astype(np.float64) if dt == "f16" else synth.bf16_to_f32(C).astype(np.float64)
+    Cb = np.broadcast_to(c64, (M, N)).ravel()[sel]
+    check_close(host_f64(Y).ravel()[sel], y, 0.5 * t + 1.5 * np.abs(Cb), dt, "split-K %s %s x %s" % (dt, sa, sb))
+
+
+def test_matmul_split_k_decode_batch_exact():
+    """A batch of single-token rows against one weight matrix (batch folds into
+    M = 8): split-K, small integers, fp16 output exact."""
+    rng = np.random.default_rng(901)
+    A = synth.store(synth.small_ints(rng, (8, 1, 8192), -1, 1), "f16")
+    B = synth.store(synth.small_ints(rng, (8192, 3072), -1, 1), "f16")
+    Y = om.matmul(dev(A, "f16"), dev(B, "f16"))
+    torch.cuda.synchronize()
+    y, _ = oracle.matmul(A, B, dt="f16")
+    assert tuple(Y.shape) == (8, 1, 3072)
+    assert np.abs(y).max() < 2048
+    assert np.array_equal(host_f64(Y), y)
