@@ -303,12 +303,19 @@ __global__ __launch_bounds__(256) void grouped16_kernel(GroupedArgs a, const cha
     __shared__ __attribute__((aligned(1024))) char s0[(GBM + GBN) * core16::KSTEP * 2];
     __shared__ __attribute__((aligned(1024))) char s1[(GBM + GBN) * core16::KSTEP * 2];
     __shared__ int orow_s[GBM];
-    const int total = max_mtiles * tiles_n;
-    const int w = xcd_remap((int)blockIdx.x, total);
-    int tm, tn;
-    grouped_order(w, max_mtiles, tiles_n, 4, tm, tn);
+    // The grid is sized for the most row tiles any routing can produce; the
+    // routed count is known only here.  Workgroup b runs on XCD b % 8, so the
+    // routed tiles are split evenly over the 8 XCDs (each takes one contiguous
+    // run of the tile order) and the surplus workgroups of every XCD exit.
+    (void)max_mtiles;
     const int ntiles = ((const int*)ws)[0];
-    if (tm >= ntiles) return;
+    const int total = ntiles * tiles_n;
+    const int b = (int)blockIdx.x, x = b & 7, l = b >> 3;
+    const int per = total >> 3, extra = total & 7;
+    if (l >= per + (x < extra ? 1 : 0)) return;
+    const int w = x * per + min(x, extra) + l;
+    int tm, tn;
+    grouped_order(w, ntiles, tiles_n, 4, tm, tn);
     grouped_body<DT, VEC>(a, ws, tm, tn, s0, s1, orow_s);
 }
 
