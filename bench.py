@@ -10,7 +10,9 @@ on one stream (all inputs resident in HBM before timing starts):
 `value` is the step's algorithmic operations (2*M*N*K per product; int8
 multiply-adds counted like flops) divided by the step time.  Each workload is
 also timed on its own (median of HIP-event intervals around its call) and
-reported against the MI355X dense MFMA peak of its type under `per_config`.
+reported against the MI355X dense MFMA peak of its type under `per_config`;
+`cold_ms` there is the median of calls issued right after a 512 MiB write that
+evicts the last-level cache (operands start in HBM only).
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--only NAME]
        python bench.py --copy-calibration      (1 GiB device-to-device copies, for
@@ -115,6 +117,23 @@ def time_each(torch, fn, reps):
     return ms[len(ms) // 2], ms
 
 
+def time_cold(torch, fn, reps, flush):
+    """Median of HIP-event intervals around single calls, each issued right after a
+    write of `flush` (larger than the 256 MB last-level cache), so the call starts
+    with none of its operands cached."""
+    ms = []
+    for i in range(reps):
+        flush.fill_(i & 0xFF)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        torch.cuda.synchronize()
+        ms.append(s.elapsed_time(e))
+    ms.sort()
+    return ms[len(ms) // 2]
+
+
 def kernel_source_hash():
     """sha256 over the kernel sources (csrc/*.hip, *.hpp): identifies the build the counters describe."""
     d = os.path.join(ROOT, "onnx_matmul_family_amd", "csrc")
@@ -202,6 +221,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--reps", type=int, default=30, help="timed calls per workload for the per-config medians")
+    ap.add_argument("--cold-reps", type=int, default=5,
+                    help="calls per workload timed right after a 512 MiB cache-flush write (0: skip)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the baseline")
     ap.add_argument("--only", default=None, help="comma-separated workload names")
@@ -251,6 +272,7 @@ def main():
     log("step %.3f ms" % (step_s * 1e3))
 
     per = []
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if args.cold_reps > 0 else None
     for n, fn in runs.items():
         med, _ = time_each(torch, fn, args.reps)
         w = W[n]
@@ -258,6 +280,8 @@ def main():
         per.append(dict(workload=n, dtype=w["dtype"], ms=round(med, 4), tflops=round(rate, 2),
                         frac_peak=round(rate / PEAK[w["dtype"]], 4),
                         hbm_gbs=round(w["bytes"] / (med * 1e-3) / 1e9, 1)))
+        if flush is not None:
+            per[-1]["cold_ms"] = round(time_cold(torch, fn, args.cold_reps, flush), 4)
         log("%-20s %9.4f ms  %8.1f T/s  %5.1f%% of %s peak" % (n, med, rate, 100 * rate / PEAK[w["dtype"]],
                                                                w["dtype"]))
 
