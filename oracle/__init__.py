@@ -61,6 +61,10 @@ def lib():
                                          vp, ci, ci, i64p, vp, ci, vp, ci, i64p,
                                          vp, ci, vp, ci, cl, i64p, vp, vp, ci]
         L.orc_grouped_matmul.argtypes = [vp, vp, vp, ci, vp, ci, cl, cl, cl, cl, cl, cl, i64p, dp, dp, ci]
+        L.orc_grouped_matmul_dq.argtypes = [vp, vp, ci, vp, vp, cl, vp, ci, vp, ci, cl, cl, cl, cl, cl, cl, i64p,
+                                            dp, dp, ci]
+        L.orc_round.argtypes = [ci, ctypes.c_double]
+        L.orc_round.restype = ctypes.c_double
         L.orc_decode.argtypes = [ci, vp, cl]
         L.orc_decode.restype = ctypes.c_double
         _lib = L
@@ -213,6 +217,46 @@ def grouped_matmul(inp, weights, group_indices, bias=None, dt=None, sel=None, nt
     if s is None:
         return y.reshape(M, S, N), t.reshape(M, S, N)
     return y, t
+
+
+def grouped_matmul_dequant(inp, qweights, scale, zero_point, block_size, group_indices, bias=None, dt=None,
+                           sel=None, nthreads=None):
+    """GroupedMatMul over DequantizeLinear weights (blocked along K, per column).
+
+    qweights (G, K, N) int8/uint8; scale (G, ceil(K/bs), N) of the float type;
+    zero_point None or like scale with qweights' dtype.  Returns (y, t) in
+    float64, shape (M, S, N)."""
+    inp, qw = np.ascontiguousarray(inp), np.ascontiguousarray(qweights)
+    scale = np.ascontiguousarray(scale)
+    idx = np.ascontiguousarray(group_indices)
+    zp = None if zero_point is None else np.ascontiguousarray(zero_point)
+    if bias is not None:
+        bias = np.ascontiguousarray(bias)
+    M, K = inp.shape
+    G, K2, N = qw.shape
+    M2, S = idx.shape
+    nkb = (K + block_size - 1) // block_size if block_size > 0 else -1
+    if (K2 != K or M2 != M or scale.shape != (G, nkb, N) or (zp is not None and zp.shape != scale.shape)
+            or (zp is not None and zp.dtype != qw.dtype) or (bias is not None and bias.shape != (G, N))):
+        raise OracleError(-1)
+    s, ns, sp = _sel(sel)
+    cnt = ns if s is not None else M * S * N
+    y = np.empty(cnt, np.float64)
+    t = np.empty(cnt, np.float64)
+    r = lib().orc_grouped_matmul_dq(_ptr(inp), _ptr(qw), _code(qw, None), _ptr(scale), _ptr(zp), block_size,
+                                    _ptr(idx), _code(idx, None), _ptr(bias), _code(inp, dt), M, K, G, N, S, ns, sp,
+                                    _ptr(y), _ptr(t), nthreads or threads())
+    if r:
+        raise OracleError(r)
+    if s is None:
+        return y.reshape(M, S, N), t.reshape(M, S, N)
+    return y, t
+
+
+def round_to(values, dt):
+    """The oracle's own rounding of real values to float type dt (nearest, ties to even)."""
+    L = lib()
+    return np.array([L.orc_round(_CODES[dt], float(v)) for v in np.ravel(values)])
 
 
 def decode(arr, dt):

@@ -26,7 +26,10 @@
  *    point per tensor, per row of a or per column of b.
  *  - GroupedMatMul - 29, Summary:
  *    output[m, i] = input[m] @ weights[group_indices[m, i]] (+ bias[g]),
- *    indices outside [0, G) are invalid.
+ *    indices outside [0, G) are invalid; weight-only quantised experts are
+ *    DequantizeLinear of quantised weights fed to GroupedMatMul (the page
+ *    names the composition; the affine map used is the QLinearMatMul
+ *    page's (q - zero_point) * scale).
  */
 #include <math.h>
 #include <stdint.h>
@@ -415,6 +418,91 @@ int orc_grouped_matmul(const void* input, const void* weights, const void* idx, 
     }
     return bad ? ORC_EINDEX : ORC_OK;
 }
+
+/* ---- GroupedMatMul over DequantizeLinear weights ------------------------ */
+
+/*
+ * Round a real value to the nearest value of float type dt, ties to even,
+ * with IEEE gradual underflow and overflow to infinity: p significand bits,
+ * emin the exponent of the smallest normal number, maxf the largest finite
+ * value.  The value's leading-digit exponent fixes the spacing of the
+ * representable numbers around it (fixed below emin: subnormals).
+ */
+static double orc_round_to(double v, int dt) {
+    int p, emin;
+    double maxf;
+    switch (dt) {
+    case ORC_F64: return v;
+    case ORC_F32: p = 24; emin = -126; maxf = ldexp(2.0 - ldexp(1.0, -23), 127); break;
+    case ORC_BF16: p = 8; emin = -126; maxf = ldexp(2.0 - ldexp(1.0, -7), 127); break;
+    case ORC_F16: p = 11; emin = -14; maxf = 65504.0; break;
+    default: return NAN;
+    }
+    if (v == 0.0 || isnan(v) || isinf(v)) return v;
+    int e;
+    frexp(v, &e);  /* |v| in [2^(e-1), 2^e) */
+    int ue = e - 1;
+    if (ue < emin) ue = emin;
+    double ulp = ldexp(1.0, ue - (p - 1));
+    double r = nearbyint(v / ulp) * ulp;  /* default rounding mode: to nearest, ties to even */
+    if (fabs(r) > maxf) return v > 0 ? INFINITY : -INFINITY;
+    return r;
+}
+
+/*
+ * Weight-only quantised experts, as the GroupedMatMul page describes them:
+ * DequantizeLinear applied to quantised weights, its result fed to
+ * GroupedMatMul.  The dequantised weight is the affine map the QLinearMatMul
+ * page uses for its operands, (q - zero_point) * scale, held in the scale's
+ * type T (so rounded once to T), with one scale and zero point per block of
+ * block_size consecutive k and per column n of each group:
+ *   w[g, k, n] = round_T((q[g, k, n] - zp[g, k / bs, n]) * scale[g, k / bs, n])
+ *   output[m, i, n] = sum_k input[m, k] * w[g, k, n] (+ bias[g, n]),  g = group_indices[m, i]
+ * scale and zp have shape (G, ceil(K / bs), N); zp NULL means 0.  q and zp are
+ * int8 or uint8 (q_dt), scale, input, bias and the result of type dt.
+ */
+int orc_grouped_matmul_dq(const void* input, const void* qw, int q_dt, const void* scale, const void* zp,
+                          int64_t bs, const void* idx, int idx_dt, const void* bias, int dt, int64_t M, int64_t K,
+                          int64_t G, int64_t N, int64_t S, int64_t n_sel, const int64_t* sel, double* y, double* t,
+                          int nthreads) {
+    if (!orc_is_float(dt)) return ORC_EDTYPE;
+    if (q_dt != ORC_I8 && q_dt != ORC_U8) return ORC_EDTYPE;
+    if (idx_dt != ORC_I32 && idx_dt != ORC_I64) return ORC_EDTYPE;
+    if (bs < 1) return ORC_ESHAPE;
+    int64_t nkb = (K + bs - 1) / bs;
+    int64_t cnt = sel ? n_sel : M * S * N;
+    int bad = 0;
+#pragma omp parallel for schedule(static) num_threads(nthreads) reduction(| : bad)
+    for (int64_t j = 0; j < cnt; j++) {
+        int64_t f = sel ? sel[j] : j;
+        int64_t n = f % N, mi = f / N;
+        int64_t m = mi / S;
+        int64_t grp = orc_ldi(idx, idx_dt, mi);
+        if (grp < 0 || grp >= G) {
+            bad = 1;
+            y[j] = NAN;
+            if (t) t[j] = NAN;
+            continue;
+        }
+        double s = 0.0, sa = 0.0;
+        for (int64_t k = 0; k < K; k++) {
+            int64_t po = (grp * nkb + k / bs) * N + n;
+            double q = (double)orc_ldi(qw, q_dt, (grp * K + k) * N + n);
+            double z = zp ? (double)orc_ldi(zp, q_dt, po) : 0.0;
+            double w = orc_round_to((q - z) * orc_ldf(scale, dt, po), dt);
+            double p = orc_ldf(input, dt, m * K + k) * w;
+            s += p;
+            sa += fabs(p);
+        }
+        if (bias) s += orc_ldf(bias, dt, grp * N + n);
+        y[j] = s;
+        if (t) t[j] = sa;
+    }
+    return bad ? ORC_EINDEX : ORC_OK;
+}
+
+/* Exposed so a test can compare the rounding against library conversions. */
+double orc_round(int dt, double v) { return orc_round_to(v, dt); }
 
 /* Exposed so a test can compare the decoders against library conversions. */
 double orc_decode(int dt, const void* p, int64_t i) { return orc_ldf(p, dt, i); }

@@ -16,7 +16,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
-PINS = ["tests/test_oracle_examples.py", "tests/test_oracle_properties.py"]
+PINS = ["tests/test_oracle_examples.py", "tests/test_oracle_properties.py", "tests/test_oracle_dequant.py"]
 
 MUTANTS = {
     # MatMul
@@ -44,22 +44,51 @@ MUTANTS = {
     "qlinear_requant_in_double": ("float x = xf * mult;", "float x = (float)((double)acc_w * sa * sb / sy);"),
     "qlinear_requant_other_order": ("float mult = prod / sy;", "float mult = sa * (sb / sy);"),
     # GroupedMatMul
-    "grouped_bias_dropped": ("if (bias) s += orc_ldf(bias", "if (0) s += orc_ldf(bias"),
-    "grouped_first_selection_only": ("orc_ldi(idx, idx_dt, mi)", "orc_ldi(idx, idx_dt, m * S)"),
-    "grouped_weights_transposed": ("(grp * K + k) * N + n", "(grp * N + n) * K + k"),
-    "grouped_bias_of_group_zero": ("orc_ldf(bias, dt, grp * N + n)", "orc_ldf(bias, dt, n)"),
+    "grouped_bias_dropped": ("if (bias) s += orc_ldf(bias", "if (0) s += orc_ldf(bias", "int orc_grouped_matmul(const void* input"),
+    "grouped_first_selection_only": ("orc_ldi(idx, idx_dt, mi)", "orc_ldi(idx, idx_dt, m * S)", "int orc_grouped_matmul(const void* input"),
+    "grouped_weights_transposed": ("(grp * K + k) * N + n", "(grp * N + n) * K + k", "int orc_grouped_matmul(const void* input"),
+    "grouped_bias_of_group_zero": ("orc_ldf(bias, dt, grp * N + n)", "orc_ldf(bias, dt, n)", "int orc_grouped_matmul(const void* input"),
+    # GroupedMatMul over DequantizeLinear weights
+    "dq_bias_dropped": ("if (bias) s += orc_ldf(bias", "if (0) s += orc_ldf(bias", "int orc_grouped_matmul_dq("),
+    "dq_first_selection_only": ("orc_ldi(idx, idx_dt, mi)", "orc_ldi(idx, idx_dt, m * S)", "int orc_grouped_matmul_dq("),
+    "dq_zero_point_dropped": ("double z = zp ? (double)orc_ldi(zp, q_dt, po) : 0.0;", "double z = 0.0;"),
+    "dq_zero_point_added": ("orc_round_to((q - z) *", "orc_round_to((q + z) *"),
+    "dq_block_index_wraps": ("int64_t po = (grp * nkb + k / bs) * N + n;", "int64_t po = (grp * nkb + k % nkb) * N + n;"),
+    "dq_scale_n_major": ("int64_t po = (grp * nkb + k / bs) * N + n;", "int64_t po = (grp * N + n) * nkb + k / bs;"),
+    "dq_weights_transposed": ("orc_ldi(qw, q_dt, (grp * K + k) * N + n)", "orc_ldi(qw, q_dt, (grp * N + n) * K + k)"),
+    "dq_weight_not_rounded": ("double w = orc_round_to((q - z) * orc_ldf(scale, dt, po), dt);",
+                              "double w = (q - z) * orc_ldf(scale, dt, po);"),
+    "round_ties_away": ("nearbyint(v / ulp)", "round(v / ulp)"),
+    "round_no_subnormal_spacing": ("if (ue < emin) ue = emin;", ""),
+    "round_no_overflow": ("if (fabs(r) > maxf) return v > 0 ? INFINITY : -INFINITY;", ""),
+    "round_bf16_one_bit_more": ("case ORC_BF16: p = 8;", "case ORC_BF16: p = 9;"),
     # element decoding
     "bf16_decode_shift": ("(uint32_t)h << 16", "(uint32_t)h << 15"),
     "fp16_subnormal_scale": ("ldexp((double)f, -24)", "ldexp((double)f, -25)"),
 }
 
 
+def _site(name):
+    """(old, new, start): the mutation replaces the first `old` at or after the
+    first occurrence of `start` (a marker naming the function it belongs to)."""
+    m = MUTANTS[name]
+    return m if len(m) == 3 else (m[0], m[1], None)
+
+
+def _mutate(src, name):
+    old, new, start = _site(name)
+    base = 0 if start is None else src.index(start)
+    at = src.index(old, base)
+    if start is None:
+        assert src.count(old) == 1, "mutation site for %s not found exactly once" % name
+    return src[:at] + new + src[at + len(old):]
+
+
 def _run_mutant(name, old, new, tmp):
     src = open(SRC).read()
-    assert src.count(old) == 1, "mutation site for %s not found exactly once" % name
     path = os.path.join(tmp, name + ".c")
     with open(path, "w") as f:
-        f.write(src.replace(old, new))
+        f.write(_mutate(src, name))
     lib = os.path.join(tmp, "lib_" + name + ".so")
     subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC",
                            "-shared", "-w", "-o", lib, path, "-lm"])
@@ -72,7 +101,7 @@ def _run_mutant(name, old, new, tmp):
 
 def test_every_mutant_is_caught():
     with tempfile.TemporaryDirectory() as tmp, cf.ThreadPoolExecutor(max_workers=4) as ex:
-        futs = {name: ex.submit(_run_mutant, name, old, new, tmp) for name, (old, new) in MUTANTS.items()}
+        futs = {name: ex.submit(_run_mutant, name, None, None, tmp) for name in MUTANTS}
         survivors = []
         for name, fut in futs.items():
             rc, failed = fut.result()
@@ -83,5 +112,5 @@ def test_every_mutant_is_caught():
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutation_site_present(name):
-    old, _ = MUTANTS[name]
-    assert open(SRC).read().count(old) == 1
+    src = open(SRC).read()
+    assert _mutate(src, name) != src
