@@ -10,6 +10,8 @@
  *                        32-bit accumulation and a round-half-even requantisation.
  *   omm_grouped_matmul   GroupedMatMul (version 29):
  *                        output[m, i] = input[m] @ weights[group_indices[m, i]] (+ bias[g]).
+ *   omm_grouped_matmul_dequant  the same over int8/uint8 weights with block
+ *                        scales (DequantizeLinear fused into the weight load).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -161,6 +163,34 @@ int omm_grouped_matmul_output_shape(const omm_tensor* input, const omm_tensor* w
 int omm_grouped_matmul(const omm_tensor* input, const omm_tensor* weights, const omm_tensor* group_indices,
                        const omm_tensor* bias, omm_tensor* output, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/* ------------------------------------------------------------------------
+ * GroupedMatMul over weight-only quantised experts (GroupedMatMul version 29,
+ * Summary: quantised weights passed through DequantizeLinear and then to
+ * GroupedMatMul, a composition runtimes may fuse so the dequantised
+ * (G, K, N) weights are never materialised).  Computes exactly
+ *     w[g, k, n] = T( (q[g, k, n] - zp[g, k / block_size, n]) * scale[g, k / block_size, n] )
+ *     output[m, i, :] = input[m, :] @ w[g] (+ bias[g, :]),  g = group_indices[m, i]
+ * i.e. DequantizeLinear blocked along K (its output in the scale's type T,
+ * rounded once, nearest-even; (q - zp) * scale is exact before that rounding
+ * for 16-bit T) followed by omm_grouped_matmul.  The dequantised weights are
+ * formed in registers as each weight tile is staged.
+ *   input (M, K) of T; qweights (G, K, N) OMM_I8 or OMM_U8; w_scale
+ *   (G, ceil(K / block_size), N) of T; w_zero_point NULL (zero) or like
+ *   w_scale with qweights' dtype; block_size >= 1 (block_size >= K: one scale
+ *   per group and column); group_indices, bias, output, workspace, stream and
+ *   invalid indices as omm_grouped_matmul.  T: OMM_BF16, OMM_F16 or OMM_F32.
+ *   The fast path needs 16-byte aligned input / 8-byte aligned q, zp, bias and
+ *   output / 16-byte aligned scales, K and N multiples of 8 and block_size a
+ *   multiple of 64; other layouts use an element-wise path.
+ * Errors: OMM_ERR_NULL, OMM_ERR_DTYPE, OMM_ERR_SHAPE (also block_size < 1 or
+ * a scale / zero-point shape that is not (G, ceil(K / block_size), N)),
+ * OMM_ERR_WORKSPACE.
+ */
+int omm_grouped_matmul_dequant(const omm_tensor* input, const omm_tensor* qweights, const omm_tensor* w_scale,
+                               const omm_tensor* w_zero_point, int64_t block_size, const omm_tensor* group_indices,
+                               const omm_tensor* bias, omm_tensor* output, void* workspace, size_t workspace_bytes,
+                               void* stream);
 
 /* Waits for `stream`, then reports how many (m, i) pairs of the last
  * omm_grouped_matmul that used `workspace` had an index outside [0, G).

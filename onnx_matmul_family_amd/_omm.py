@@ -59,6 +59,7 @@ def lib():
         L.omm_grouped_matmul_output_shape.argtypes = [P, P, P, i32p, i64p]
         L.omm_grouped_matmul.argtypes = [P, P, P, P, P, vp, ctypes.c_size_t, vp]
         L.omm_grouped_matmul_check.argtypes = [vp, vp, i64p]
+        L.omm_grouped_matmul_dequant.argtypes = [P, P, P, P, ctypes.c_int64, P, P, P, vp, ctypes.c_size_t, vp]
         _lib = L
     return _lib
 
@@ -167,6 +168,30 @@ def grouped_matmul(input, weights, group_indices, bias=None, output=None, worksp
     _check(L.omm_grouped_matmul(ctypes.byref(ti), ctypes.byref(tw), ctypes.byref(tx), pb, ctypes.byref(to),
                                 ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream)),
            "omm_grouped_matmul")
+    return output, workspace
+
+
+def grouped_matmul_dequant(input, qweights, w_scale, w_zero_point, block_size, group_indices, bias=None,
+                           output=None, workspace=None, stream=None):
+    """GroupedMatMul over DequantizeLinear(qweights, w_scale, w_zero_point) blocked along K:
+    w[g, k, n] = T((q - zp) * scale) with the scale / zero point of block k // block_size.
+    Returns (output, workspace)."""
+    L = lib()
+    ti, tq, tx, ts = describe(input), describe(qweights), describe(group_indices), describe(w_scale)
+    if output is None:
+        output = torch.empty(_shape(L.omm_grouped_matmul_output_shape, ctypes.byref(ti), ctypes.byref(tq),
+                                    ctypes.byref(tx)), dtype=input.dtype, device=input.device)
+    to = describe(output)
+    M, S, G = group_indices.shape[0], group_indices.shape[1], qweights.shape[0]
+    need = grouped_matmul_workspace_size(M, S, G)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=input.device)
+    pz = ctypes.byref(describe(w_zero_point)) if w_zero_point is not None else None
+    pb = ctypes.byref(describe(bias)) if bias is not None else None
+    _check(L.omm_grouped_matmul_dequant(ctypes.byref(ti), ctypes.byref(tq), ctypes.byref(ts), pz, int(block_size),
+                                        ctypes.byref(tx), pb, ctypes.byref(to), ctypes.c_void_p(workspace.data_ptr()),
+                                        workspace.numel(), _stream(stream)),
+           "omm_grouped_matmul_dequant")
     return output, workspace
 
 

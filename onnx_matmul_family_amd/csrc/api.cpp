@@ -531,6 +531,59 @@ int omm_grouped_matmul(const omm_tensor* input, const omm_tensor* weights, const
     return hip_status(omm::launch_grouped(a, kd, workspace, (hipStream_t)stream));
 }
 
+int omm_grouped_matmul_dequant(const omm_tensor* input, const omm_tensor* qweights, const omm_tensor* w_scale,
+                               const omm_tensor* w_zero_point, int64_t block_size, const omm_tensor* group_indices,
+                               const omm_tensor* bias, omm_tensor* output, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    int rc;
+    if ((rc = check_tensor(output)) || (rc = check_tensor(w_scale))) return rc;
+    if (bias && (rc = check_tensor(bias))) return rc;
+    if (w_zero_point && (rc = check_tensor(w_zero_point))) return rc;
+    int32_t nd;
+    int64_t osh[3];
+    if ((rc = omm_grouped_matmul_output_shape(input, qweights, group_indices, &nd, osh))) return rc;
+    const int dt = input->dtype;
+    if (qweights->dtype != OMM_I8 && qweights->dtype != OMM_U8) return OMM_ERR_DTYPE;
+    if (w_scale->dtype != dt || output->dtype != dt || (bias && bias->dtype != dt)) return OMM_ERR_DTYPE;
+    if (w_zero_point && w_zero_point->dtype != qweights->dtype) return OMM_ERR_DTYPE;
+    if (elem_size(dt) == 0 || dt == OMM_I8 || dt == OMM_U8 || dt == OMM_I32 || dt == OMM_I64) return OMM_ERR_DTYPE;
+    if (!is_dense_float(dt)) return OMM_ERR_UNSUPPORTED;
+    if (group_indices->dtype != OMM_I32 && group_indices->dtype != OMM_I64) return OMM_ERR_DTYPE;
+    const int64_t M = osh[0], S = osh[1], N = osh[2], K = input->shape[1], G = qweights->shape[0];
+    if (block_size < 1) return OMM_ERR_SHAPE;
+    const int64_t nkb = (K + block_size - 1) / block_size;
+    if (w_scale->ndim != 3 || w_scale->shape[0] != G || w_scale->shape[1] != nkb || w_scale->shape[2] != N)
+        return OMM_ERR_SHAPE;
+    if (w_zero_point && (w_zero_point->ndim != 3 || w_zero_point->shape[0] != G || w_zero_point->shape[1] != nkb ||
+                         w_zero_point->shape[2] != N))
+        return OMM_ERR_SHAPE;
+    if (bias && (bias->ndim != 2 || bias->shape[0] != G || bias->shape[1] != N)) return OMM_ERR_SHAPE;
+    if ((rc = check_out(output, 3, osh))) return rc;
+    if (!workspace || workspace_bytes < omm::grouped_workspace_bytes(M, S, G) || ((uintptr_t)workspace & 255))
+        return OMM_ERR_WORKSPACE;
+    if (G > 8192 || M * S > 0x7fffffffLL) return OMM_ERR_UNSUPPORTED;
+    GroupedArgs a;
+    memset(&a, 0, sizeof a);
+    a.input = input->data;
+    a.weights = qweights->data;
+    a.idx = group_indices->data;
+    a.bias = bias ? bias->data : nullptr;
+    a.output = output->data;
+    a.M = M;
+    a.K = K;
+    a.N = N;
+    a.G = G;
+    a.S = S;
+    a.idx64 = group_indices->dtype == OMM_I64;
+    a.wscale = w_scale->data;
+    a.wzp = w_zero_point ? w_zero_point->data : nullptr;
+    a.bs = block_size;
+    a.nkb = nkb;
+    a.q_kind = qweights->dtype == OMM_U8 ? 2 : 1;
+    const int kd = dt == OMM_BF16 ? 0 : dt == OMM_F16 ? 1 : 2;
+    return hip_status(omm::launch_grouped_dq(a, kd, workspace, (hipStream_t)stream));
+}
+
 int omm_grouped_matmul_check(const void* workspace, void* stream, int64_t* invalid_count) {
     if (!workspace || !invalid_count) return OMM_ERR_NULL;
     return hip_status(omm::grouped_invalid_count(workspace, (hipStream_t)stream, invalid_count));

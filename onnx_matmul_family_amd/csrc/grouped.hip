@@ -152,6 +152,94 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(const void* idx, int
     }
 }
 
+// Epilogue of one grouped tile: + bias[g], one rounding to T, each row to
+// output[pair].  VEC: output and bias 8-byte aligned and N % 8 == 0 (4-value
+// stores; whole 256-column tiles of a 16-byte aligned output go through LDS as
+// whole row segments, orow_s holding the tile's output rows, filled before
+// the K loop's barriers).
+template <int DT, bool VEC>
+__device__ __forceinline__ void grouped_epilogue(const f32x16_t (&acc)[4][4], const GroupedArgs& a, int g, int rows,
+                                                 int start, const int* sorted, int64_t n0, int lane, int wave,
+                                                 char* s0, char* s1, const int* orow_s) {
+    using namespace core16;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t N = a.N;
+    if constexpr (VEC) {
+        if (n0 + GBN <= N && N % 8 == 0 && ((uintptr_t)a.output & 15) == 0) {
+            __syncthreads();  // every wave is done reading the last stage
+            char* stage = (wave < 2 ? s0 : s1) + (wave & 1) * (GBM * KSTEP * 2);
+            const int64_t col0 = n0 + wn * (GBN / 2);
+            uint16_t* out = (uint16_t*)a.output + col0;
+            const int* orow_w = orow_s + wm * (GBM / 2);
+            auto rowp = [&](int r) -> uint16_t* {
+                const int o = orow_w[r];
+                return o >= 0 ? out + (int64_t)o * N : nullptr;
+            };
+            if (a.bias)
+                wave_epilogue_lds<DT, true>(acc, 1.0f, (const uint16_t*)a.bias + (int64_t)g * N + col0, 1.0f, stage,
+                                            lane, rowp);
+            else
+                wave_epilogue_lds<DT, false>(acc, 1.0f, nullptr, 1.0f, stage, lane, rowp);
+            return;
+        }
+    }
+    const uint16_t* __restrict__ bias = a.bias ? (const uint16_t*)a.bias + (int64_t)g * N : nullptr;
+    uint16_t* __restrict__ out = (uint16_t*)a.output;
+    const bool vec_store = VEC && (N % 4 == 0);
+    const int64_t nl = n0 + wn * 128 + 4 * (lane >> 5);
+    int orow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = wm * 128 + 32 * i + (lane & 31);
+        orow[i] = r < rows ? sorted[start + r] : -1;
+    }
+    // one 32-column block at a time, so only its 16 bias values are live
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float bv[4][4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t n = nl + 32 * j + 8 * q;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bv[q][e] = 0.0f;
+            if (bias && vec_store && n < N) {
+                const u32x2_t b2 = *(const u32x2_t*)(bias + n);
+                bv[q][0] = from_bits<DT>((uint16_t)b2.x);
+                bv[q][1] = from_bits<DT>((uint16_t)(b2.x >> 16));
+                bv[q][2] = from_bits<DT>((uint16_t)b2.y);
+                bv[q][3] = from_bits<DT>((uint16_t)(b2.y >> 16));
+            } else if (bias) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < N) bv[q][e] = from_bits<DT>(bias[n + e]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (orow[i] < 0) continue;
+            uint16_t* __restrict__ yr = out + (int64_t)orow[i] * N;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t n = nl + 32 * j + 8 * q;
+                if (n >= N) continue;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e] + bv[q][e];
+                if (vec_store) {
+                    u32x2_t o;
+                    o.x = pack2<DT>(v[0], v[1]);
+                    o.y = pack2<DT>(v[2], v[3]);
+                    *(u32x2_t*)(yr + n) = o;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) yr[n + e] = to_bits<DT>(v[e]);
+                }
+            }
+        }
+    }
+}
+
 // One 256x256 tile of the grouped product.  VEC: DMA path (CHECKED pads ragged
 // rows / columns / K with zeros); otherwise element-wise register-staged loads.
 template <int DT, bool VEC>
@@ -218,84 +306,7 @@ __device__ __forceinline__ void grouped_body(const GroupedArgs& a, const char* w
         mainloop<GBM, GBN, DT, true, false, 2>(acc, s0, s1, srcA, srcB, nk, t, lane, wm, wn);
     }
 
-    // Epilogue: + bias[g], one rounding, each row to output[pair].
-    if constexpr (VEC) {
-        // whole 256-column tile with 16-byte aligned rows: through LDS as
-        // whole row segments (orow_s was filled before the K loop's barriers)
-        if (n0 + GBN <= N && N % 8 == 0 && ((uintptr_t)a.output & 15) == 0) {
-            __syncthreads();  // every wave is done reading the last stage
-            char* stage = (wave < 2 ? s0 : s1) + (wave & 1) * (GBM * KSTEP * 2);
-            const int64_t col0 = n0 + wn * (GBN / 2);
-            uint16_t* out = (uint16_t*)a.output + col0;
-            const int* orow_w = orow_s + wm * (GBM / 2);
-            auto rowp = [&](int r) -> uint16_t* {
-                const int o = orow_w[r];
-                return o >= 0 ? out + (int64_t)o * N : nullptr;
-            };
-            if (a.bias)
-                wave_epilogue_lds<DT, true>(acc, 1.0f, (const uint16_t*)a.bias + (int64_t)g * N + col0, 1.0f, stage,
-                                            lane, rowp);
-            else
-                wave_epilogue_lds<DT, false>(acc, 1.0f, nullptr, 1.0f, stage, lane, rowp);
-            return;
-        }
-    }
-    const uint16_t* __restrict__ bias = a.bias ? (const uint16_t*)a.bias + (int64_t)g * N : nullptr;
-    uint16_t* __restrict__ out = (uint16_t*)a.output;
-    const bool vec_store = VEC && (N % 4 == 0);
-    const int64_t nl = n0 + wn * 128 + 4 * (lane >> 5);
-    float bv[4][4][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int64_t n = nl + 32 * j + 8 * q;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) bv[j][q][e] = 0.0f;
-            if (bias && vec_store && n < N) {
-                const u32x2_t b2 = *(const u32x2_t*)(bias + n);
-                bv[j][q][0] = from_bits<DT>((uint16_t)b2.x);
-                bv[j][q][1] = from_bits<DT>((uint16_t)(b2.x >> 16));
-                bv[j][q][2] = from_bits<DT>((uint16_t)b2.y);
-                bv[j][q][3] = from_bits<DT>((uint16_t)(b2.y >> 16));
-            } else if (bias) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (n + e < N) bv[j][q][e] = from_bits<DT>(bias[n + e]);
-            }
-        }
-    int orow[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = wm * 128 + 32 * i + (lane & 31);
-        orow[i] = r < rows ? sorted[start + r] : -1;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (orow[i] < 0) continue;
-        uint16_t* __restrict__ yr = out + (int64_t)orow[i] * N;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t n = nl + 32 * j + 8 * q;
-                if (n >= N) continue;
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e] + bv[j][q][e];
-                if (vec_store) {
-                    u32x2_t o;
-                    o.x = pack2<DT>(v[0], v[1]);
-                    o.y = pack2<DT>(v[2], v[3]);
-                    *(u32x2_t*)(yr + n) = o;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (n + e < N) yr[n + e] = to_bits<DT>(v[e]);
-                }
-            }
-        }
-    }
+    grouped_epilogue<DT, VEC>(acc, a, g, rows, start, sorted, n0, lane, wave, s0, s1, orow_s);
 }
 
 template <int DT, bool VEC>
@@ -317,6 +328,335 @@ __global__ __launch_bounds__(256) void grouped16_kernel(GroupedArgs a, const cha
     int tm, tn;
     grouped_order(w, ntiles, tiles_n, 4, tm, tn);
     grouped_body<DT, VEC>(a, ws, tm, tn, s0, s1, orow_s);
+}
+
+// ---------------------------------------------------------------------------
+// Weight-only quantised experts: the weights arrive as int8 / uint8 q (G, K, N)
+// with scales (G, nkb, N) of T and optional zero points (G, nkb, N) of q's
+// type, one per block of bs consecutive k and per column; the weight the
+// product uses is w = T((q - zp) * scale) (DequantizeLinear, its output in the
+// scale's type), formed in registers as each tile is staged: the dequantised
+// (G, K, N) tensor never exists.
+
+// Register-staged source of one dequantised 256-column weight tile, in the
+// MN-major chunks of Chunks<GBN, false> (8 columns of one k row per chunk;
+// chunk i of thread t is row t/32 + 8 i of the stage, columns (t%32)*8 ..).
+//  FAST: N % 8 == 0, q rows 8-byte and scale rows 16-byte aligned, bs a
+//        multiple of the 64-deep stage (a stage lies in one block): load()
+//        issues 8-byte loads of the int8 bytes and one scale / zero-point
+//        chunk per stage; convert() dequantises when the stage is stored, so
+//        the loads have the whole stage of MFMAs to land.
+//  else: element loads with element range checks, dequantised in load().
+// (q - zp) * scale is exact in fp32 (|q - zp| <= 255, 8- or 11-bit scale
+// significand), so the one rounding is the conversion to T.
+template <int DT, bool QU8, bool FAST>
+struct DeqSrc {
+    static constexpr int NC = core16::Chunks<GBN, false>::NC;
+    const uint8_t* q;    // this group's q, (K, N)
+    const uint16_t* sc;  // this group's scales, (nkb, N)
+    const uint8_t* zp;   // this group's zero points, or nullptr
+    int64_t N, K, bs, n;
+    int r0;
+    u32x2_t raw[NC];
+    u32x4_t sraw;
+    u32x2_t zraw;
+    u32x4_t out[NC];
+
+    __device__ void init(const GroupedArgs& a, int g, int64_t n0, int t) {
+        const int64_t nkb = a.nkb;
+        q = (const uint8_t*)a.weights + (int64_t)g * a.K * a.N;
+        sc = (const uint16_t*)a.wscale + (int64_t)g * nkb * a.N;
+        zp = a.wzp ? (const uint8_t*)a.wzp + (int64_t)g * nkb * a.N : nullptr;
+        N = a.N;
+        K = a.K;
+        bs = a.bs;
+        int lmn, lk;
+        core16::Chunks<GBN, false>::coords(t, 0, lmn, lk);
+        n = n0 + lmn;
+        r0 = lk;
+    }
+
+    __device__ static float elem(uint32_t qb, uint32_t zb, float s) {
+        const int qi = QU8 ? (int)qb : (int)(int8_t)qb, zi = QU8 ? (int)zb : (int)(int8_t)zb;
+        return (float)(qi - zi) * s;
+    }
+
+    __device__ __forceinline__ void load(int kt) {
+        const int64_t k0 = (int64_t)kt * core16::KSTEP + r0;
+        if constexpr (FAST) {
+            const bool nok = n < N;
+            const int64_t kb = (int64_t)kt * core16::KSTEP / bs;
+            sraw = u32x4_t{0u, 0u, 0u, 0u};
+            zraw = u32x2_t{0u, 0u};
+            if (nok) {
+                sraw = *(const u32x4_t*)(sc + kb * N + n);
+                if (zp) zraw = *(const u32x2_t*)(zp + kb * N + n);
+            }
+#pragma unroll
+            for (int i = 0; i < NC; ++i) {
+                const int64_t k = k0 + 8 * i;
+                u32x2_t v = {0u, 0u};
+                if (nok && k < K) v = *(const u32x2_t*)(q + k * N + n);
+                raw[i] = v;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NC; ++i) {
+                const int64_t k = k0 + 8 * i;
+                float w[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) w[e] = 0.0f;
+                if (k < K) {
+                    const int64_t kb = k / bs;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        if (n + e < N) {
+                            const uint32_t qb = q[k * N + n + e];
+                            const uint32_t zb = zp ? zp[kb * N + n + e] : 0u;
+                            w[e] = elem(qb, zb, from_bits<DT>(sc[kb * N + n + e]));
+                        }
+                    }
+                }
+                out[i] = u32x4_t{pack2<DT>(w[0], w[1]), pack2<DT>(w[2], w[3]), pack2<DT>(w[4], w[5]),
+                                 pack2<DT>(w[6], w[7])};
+            }
+        }
+    }
+
+    __device__ __forceinline__ void convert(u32x4_t (&reg)[NC], int kt) const {
+        if constexpr (FAST) {
+            // int8 bytes are shifted to q + 128 (one xor per 4 bytes) so that
+            // every byte converts as unsigned; the shift moves into the offset:
+            // w = (q + 128) * s - (zp + 128) * s, both products exact
+            float sf[8], cf[8];
+            const uint32_t sw[4] = {sraw.x, sraw.y, sraw.z, sraw.w}, zw[2] = {zraw.x, zraw.y};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                sf[e] = from_bits<DT>((uint16_t)(sw[e >> 1] >> (16 * (e & 1))));
+                const uint32_t zb = (zw[e >> 2] >> (8 * (e & 3))) & 0xffu;
+                const int zs = QU8 ? (int)zb : (int)(int8_t)zb + 128;
+                cf[e] = -(float)zs * sf[e];
+            }
+            const int64_t k0 = (int64_t)kt * core16::KSTEP + r0;
+#pragma unroll
+            for (int i = 0; i < NC; ++i) {
+                uint32_t u[2] = {raw[i].x, raw[i].y};
+                if constexpr (!QU8) {
+                    u[0] ^= 0x80808080u;
+                    u[1] ^= 0x80808080u;
+                }
+                float w[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) w[e] = __builtin_fmaf((float)((u[e >> 2] >> (8 * (e & 3))) & 0xffu), sf[e], cf[e]);
+                u32x4_t v = {pack2<DT>(w[0], w[1]), pack2<DT>(w[2], w[3]), pack2<DT>(w[4], w[5]), pack2<DT>(w[6], w[7])};
+                // rows past K (and columns past N, whose scales are 0) hold zeros
+                if (!(k0 + 8 * i < K)) v = u32x4_t{0u, 0u, 0u, 0u};
+                reg[i] = v;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NC; ++i) reg[i] = out[i];
+        }
+    }
+};
+
+// Register-staged K loop with a dequantising B source: stage kt+1's loads are
+// issued before stage kt's MFMAs and dequantised + stored after them.
+template <int DT, int MODE, class SA, class SB>
+__device__ __forceinline__ void mainloop_deq(f32x16_t (&acc)[4][4], char* smem0, char* smem1, const SA& srcA, SB& srcB,
+                                             int nk, int t, int lane, int wm, int wn) {
+    using namespace core16;
+    constexpr int A_BYTES = GBM * KSTEP * 2;
+    u32x4_t ra[Chunks<GBM, true>::NC], rb[Chunks<GBN, false>::NC];
+    if (nk > 0) {
+        srcA.template load<MODE>(ra, 0);
+        srcB.load(0);
+        srcB.convert(rb, 0);
+        store_tile<GBM, true>(smem0, ra, t);
+        store_tile<GBN, false>(smem0 + A_BYTES, rb, t);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) {
+            srcA.template load<MODE>(ra, kt + 1);
+            srcB.load(kt + 1);
+        }
+        const char* sa = buf ? smem1 : smem0;
+        const char* sb = sa + A_BYTES;
+#pragma unroll
+        for (int s = 0; s < KSTEP / 16; ++s) {
+            u32x4_t af[4], bfr[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) af[i] = read_frag<GBM, true>(sa, wm * 128 + 32 * i, s, lane);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bfr[j] = read_frag<GBN, false>(sb, wn * 128 + 32 * j, s, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16<DT>(bfr[j], af[i], acc[i][j]);
+        }
+        if (kt + 1 < nk) {
+            char* so = buf ? smem0 : smem1;
+            srcB.convert(rb, kt + 1);
+            store_tile<GBM, true>(so, ra, t);
+            store_tile<GBN, false>(so + A_BYTES, rb, t);
+        }
+        __syncthreads();
+    }
+}
+
+// FAST variant: the gathered input rows go global -> LDS by DMA (as in
+// grouped16_kernel), the dequantised weights through registers.  Stage kt+1's
+// DMA and weight loads are issued before stage kt's MFMAs; its weights are
+// dequantised and stored after them; one wait + barrier per stage.
+template <int DT, class SB>
+__device__ __forceinline__ void mainloop_deq_dma(f32x16_t (&acc)[4][4], char* s0, char* s1,
+                                                 const core16::GatherDma<GBM>& srcA, SB& srcB, int nk, int t,
+                                                 int lane, int wm, int wn, int wave) {
+    using namespace core16;
+    constexpr int A_BYTES = GBM * KSTEP * 2;
+    u32x4_t rb[Chunks<GBN, false>::NC];
+    if (nk > 0) {
+        srcA.template issue<true>(s0, 0, wave);
+        srcB.load(0);
+        srcB.convert(rb, 0);
+        store_tile<GBN, false>(s0 + A_BYTES, rb, t);
+    }
+    wait_vm<0>();
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        const char* sa = buf ? s1 : s0;
+        char* so = buf ? s0 : s1;
+        // so held stage kt-1, whose reads ended before the last barrier
+        if (kt + 1 < nk) {
+            srcA.template issue<true>(so, kt + 1, wave);
+            srcB.load(kt + 1);
+        }
+        const char* sb = sa + A_BYTES;
+#pragma unroll
+        for (int s = 0; s < KSTEP / 16; ++s) {
+            u32x4_t af[4], bfr[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) af[i] = read_frag<GBM, true>(sa, wm * 128 + 32 * i, s, lane);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bfr[j] = read_frag<GBN, false>(sb, wn * 128 + 32 * j, s, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16<DT>(bfr[j], af[i], acc[i][j]);
+        }
+        if (kt + 1 < nk) {
+            srcB.convert(rb, kt + 1);
+            store_tile<GBN, false>(so + A_BYTES, rb, t);
+        }
+        wait_vm<0>();  // this wave's DMA of stage kt+1 has landed
+        __syncthreads();
+    }
+}
+
+template <int DT, bool QU8, bool FAST>
+__global__ __launch_bounds__(256) void grouped16_dq_kernel(GroupedArgs a, const char* ws, int tiles_n) {
+    __shared__ __attribute__((aligned(1024))) char s0[(GBM + GBN) * core16::KSTEP * 2];
+    __shared__ __attribute__((aligned(1024))) char s1[(GBM + GBN) * core16::KSTEP * 2];
+    __shared__ int orow_s[GBM];
+    using namespace core16;
+    // routed tiles split evenly over the 8 XCDs, as in grouped16_kernel
+    const int ntiles = ((const int*)ws)[0];
+    const int total = ntiles * tiles_n;
+    const int b = (int)blockIdx.x, x = b & 7, l = b >> 3;
+    const int per = total >> 3, extra = total & 7;
+    if (l >= per + (x < extra ? 1 : 0)) return;
+    int tm, tn;
+    grouped_order(x * per + min(x, extra) + l, ntiles, tiles_n, 4, tm, tn);
+
+    const int4 te = ((const int4*)(ws + off_tiles(a.G)))[tm];
+    const int g = te.x, start = te.y, rows = te.z;
+    const int* sorted = (const int*)(ws + off_sorted(a.M * a.S, a.G));
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t K = a.K, S = a.S;
+    const int64_t n0 = (int64_t)tn * GBN;
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    const int nk = (int)((K + KSTEP - 1) / KSTEP);
+    if (t < GBM) orow_s[t] = t < rows ? sorted[start + t] : -1;
+
+    DeqSrc<DT, QU8, FAST> srcB;
+    srcB.init(a, g, n0, t);
+    if constexpr (FAST) {
+        GatherDma<GBM> srcA;
+        srcA.base = (const char*)a.input;
+        srcA.K = K;
+        srcA.lane = lane;
+#pragma unroll
+        for (int j = 0; j < GatherDma<GBM>::PER_WAVE; ++j) {
+            const int r = GatherDma<GBM>::row_of(wave, j, lane);
+            srcA.roff[j] = r < rows ? (uint32_t)((int64_t)(sorted[start + r] / S) * K * 2) +
+                                          (GatherDma<GBM>::chunk(j, lane) << 4)
+                                    : DMA_OOB;
+        }
+        mainloop_deq_dma<DT>(acc, s0, s1, srcA, srcB, nk, t, lane, wm, wn, wave);
+    } else {
+        GatherSrc<GBM> srcA;
+        srcA.base = (const uint16_t*)a.input;
+        srcA.K = K;
+        int r0, lk;
+        Chunks<GBM, true>::coords(t, 0, r0, lk);
+        srcA.lk = lk;
+        srcA.valid = 0;
+#pragma unroll
+        for (int i = 0; i < GatherSrc<GBM>::NC; ++i) {
+            const int r = r0 + 32 * i;
+            int64_t off = 0;
+            if (r < rows) {
+                srcA.valid |= 1u << i;
+                off = (int64_t)(sorted[start + r] / S) * K;
+            }
+            srcA.roff[i] = off + srcA.lk;
+        }
+        mainloop_deq<DT, 2>(acc, s0, s1, srcA, srcB, nk, t, lane, wm, wn);
+    }
+    grouped_epilogue<DT, FAST>(acc, a, g, rows, start, sorted, n0, lane, wave, s0, s1, orow_s);
+}
+
+// fp32 with quantised weights: one workgroup per (pair, 256 columns); each
+// weight dequantised with one fp32 rounding of (q - zp) * scale.
+__global__ __launch_bounds__(256) void grouped_dq_f32_kernel(GroupedArgs a, int qu8) {
+    __shared__ float row[1024];
+    const int64_t p = blockIdx.x;
+    const int64_t n = (int64_t)blockIdx.y * 256 + threadIdx.x;
+    const int64_t g = load_idx(a.idx, p, a.idx64);
+    if (g < 0 || g >= a.G) return;
+    const float* in = (const float*)a.input + (p / a.S) * a.K;
+    const uint8_t* qg = (const uint8_t*)a.weights + g * a.K * a.N;
+    const float* sg = (const float*)a.wscale + g * a.nkb * a.N;
+    const uint8_t* zg = a.wzp ? (const uint8_t*)a.wzp + g * a.nkb * a.N : nullptr;
+    float acc = 0.0f;
+    for (int64_t k0 = 0; k0 < a.K; k0 += 1024) {
+        __syncthreads();
+        for (int k = threadIdx.x; k < 1024; k += 256) row[k] = (k0 + k < a.K) ? in[k0 + k] : 0.0f;
+        __syncthreads();
+        if (n < a.N) {
+            const int64_t kend = min((int64_t)1024, a.K - k0);
+            for (int64_t k = 0; k < kend; ++k) {
+                const int64_t kk = k0 + k, po = (kk / a.bs) * a.N + n;
+                const uint32_t qb = qg[kk * a.N + n], zb = zg ? zg[po] : 0u;
+                const int qi = qu8 ? (int)qb : (int)(int8_t)qb, zi = qu8 ? (int)zb : (int)(int8_t)zb;
+                acc += row[k] * ((float)(qi - zi) * sg[po]);
+            }
+        }
+    }
+    if (n < a.N) {
+        if (a.bias) acc += ((const float*)a.bias)[g * a.N + n];
+        ((float*)a.output)[p * a.N + n] = acc;
+    }
 }
 
 // fp32: one workgroup per (pair, 256 columns); plain fp32 dot products.
@@ -351,9 +691,10 @@ size_t grouped_workspace_bytes(int64_t M, int64_t S, int64_t G) {
     return (size_t)(off_sorted(P, G) + 4 * P + 255) / 256 * 256;
 }
 
-hipError_t launch_grouped(const GroupedArgs& a, int dt, void* ws, hipStream_t s) {
+namespace {
+// Routing kernels: counts, tile table and the pairs sorted by group in `ws`.
+hipError_t launch_routing(const GroupedArgs& a, void* ws, hipStream_t s) {
     const int64_t P = a.M * a.S;
-    if (a.G > MAX_G || P > 0x7fffffff) return hipErrorInvalidValue;
     char* w = (char*)ws;
     const unsigned nchunk = (unsigned)((P + ROUTE_CHUNK - 1) / ROUTE_CHUNK);
     hipLaunchKernelGGL(route_zero_kernel, dim3(1), dim3(256), 0, s, w, (int)a.G);
@@ -364,7 +705,50 @@ hipError_t launch_grouped(const GroupedArgs& a, int dt, void* ws, hipStream_t s)
     if (nchunk) {
         hipLaunchKernelGGL(route_scatter_kernel, dim3(nchunk), dim3(256), 0, s, a.idx, a.idx64, P, (int)a.G, w);
     }
-    hipError_t e = hipGetLastError();
+    return hipGetLastError();
+}
+bool al(const void* q, uintptr_t n) { return ((uintptr_t)q & (n - 1)) == 0; }
+}  // namespace
+
+hipError_t launch_grouped_dq(const GroupedArgs& a, int dt, void* ws, hipStream_t s) {
+    const int64_t P = a.M * a.S;
+    if (a.G > MAX_G || P > 0x7fffffff || a.bs < 1) return hipErrorInvalidValue;
+    hipError_t e = launch_routing(a, ws, s);
+    if (e != hipSuccess) return e;
+    if (P == 0 || a.N == 0) return hipSuccess;
+    const int qu8 = a.q_kind == 2;
+    if (dt == 2) {
+        const int64_t nb = (a.N + 255) / 256;
+        if (nb > 65535) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(grouped_dq_f32_kernel, dim3((unsigned)P, (unsigned)nb), dim3(256), 0, s, a, qu8);
+        return hipGetLastError();
+    }
+    const int64_t max_mtiles = P / GBM + a.G;
+    const int64_t tiles_n = (a.N + GBN - 1) / GBN;
+    if (max_mtiles * tiles_n > 0x7fffffff) return hipErrorInvalidValue;
+    // the gathered input goes by DMA (32-bit offsets: it must span < 2 GiB)
+    const bool fast = al(a.input, 16) && a.K % 8 == 0 && a.M * a.K * 2 < (1LL << 31) && a.N % 8 == 0 &&
+                      al(a.weights, 8) && al(a.wscale, 16) && (!a.wzp || al(a.wzp, 8)) &&
+                      a.bs % core16::KSTEP == 0 && al(a.output, 8) && (!a.bias || al(a.bias, 8));
+    dim3 grid((unsigned)(max_mtiles * tiles_n));
+    const char* wsc = (const char*)ws;
+    const int tn = (int)tiles_n;
+#define OMM_DQ(D, U, F) hipLaunchKernelGGL((grouped16_dq_kernel<D, U, F>), grid, dim3(256), 0, s, a, wsc, tn)
+    if (dt == 0) {
+        if (qu8) { if (fast) OMM_DQ(0, true, true); else OMM_DQ(0, true, false); }
+        else { if (fast) OMM_DQ(0, false, true); else OMM_DQ(0, false, false); }
+    } else {
+        if (qu8) { if (fast) OMM_DQ(1, true, true); else OMM_DQ(1, true, false); }
+        else { if (fast) OMM_DQ(1, false, true); else OMM_DQ(1, false, false); }
+    }
+#undef OMM_DQ
+    return hipGetLastError();
+}
+
+hipError_t launch_grouped(const GroupedArgs& a, int dt, void* ws, hipStream_t s) {
+    const int64_t P = a.M * a.S;
+    if (a.G > MAX_G || P > 0x7fffffff) return hipErrorInvalidValue;
+    hipError_t e = launch_routing(a, ws, s);
     if (e != hipSuccess) return e;
     if (P == 0 || a.N == 0) return hipSuccess;
     if (dt == 2) {
@@ -376,10 +760,9 @@ hipError_t launch_grouped(const GroupedArgs& a, int dt, void* ws, hipStream_t s)
     const int64_t max_mtiles = P / GBM + a.G;
     const int64_t tiles_n = (a.N + GBN - 1) / GBN;
     if (max_mtiles * tiles_n > 0x7fffffff) return hipErrorInvalidValue;
-    auto al16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
     // DMA offsets are 32-bit: the gathered input and one k-stage of a group's weights must span < 2 GiB
-    const bool vec = al16(a.input) && al16(a.weights) && ((uintptr_t)a.output & 7) == 0 && a.K % 8 == 0 &&
-                     a.N % 8 == 0 && a.M * a.K * 2 < (1LL << 31) && 64 * a.N * 2 < (1LL << 31);
+    const bool vec = al(a.input, 16) && al(a.weights, 16) && al(a.output, 8) && (!a.bias || al(a.bias, 8)) &&
+                     a.K % 8 == 0 && a.N % 8 == 0 && a.M * a.K * 2 < (1LL << 31) && 64 * a.N * 2 < (1LL << 31);
     dim3 grid((unsigned)(max_mtiles * tiles_n));
     const char* wsc = (const char*)ws;
     if (dt == 0) {

@@ -60,6 +60,12 @@ struct GroupedArgs {
     void* output;           // (M, S, N)
     int64_t M, K, N, G, S;
     int idx64;
+    // weight-only quantised weights (launch_grouped_dq): weights are int8 /
+    // uint8 q (G, K, N), w = T((q - zp) * scale) per block of bs k and column
+    const void* wscale;  // (G, nkb, N) of T
+    const void* wzp;     // (G, nkb, N) of q's type, or nullptr (zero)
+    int64_t bs, nkb;
+    int q_kind;          // 1 = int8, 2 = uint8
 };
 
 // dt: 0 = bf16, 1 = fp16
@@ -69,6 +75,7 @@ hipError_t launch_qlinear(const QArgs& a, hipStream_t s);
 // dt: 0 = bf16, 1 = fp16, 2 = fp32
 size_t grouped_workspace_bytes(int64_t M, int64_t S, int64_t G);
 hipError_t launch_grouped(const GroupedArgs& a, int dt, void* ws, hipStream_t s);
+hipError_t launch_grouped_dq(const GroupedArgs& a, int dt, void* ws, hipStream_t s);
 hipError_t grouped_invalid_count(const void* ws, hipStream_t s, int64_t* count);
 
 }  // namespace omm

@@ -123,3 +123,24 @@ def grouped_bf16_moe(seed=4, M=16384, K=4096, N=2048, G=64, S=8):
     bias = store(uniform(rng, (G, N), -0.1, 0.1), "bf16")
     idx = distinct_groups(rng, M, S, G, np.int32)
     return dict(input=inp, weights=weights, group_indices=idx, bias=bias, dt="bf16")
+
+
+# Weight-only quantised experts (GroupedMatMul fed by DequantizeLinear): the
+# grouped workload's shapes with int8 weights, one bf16 scale and int8 zero
+# point per 128 k and column (scales U(1e-4, 3e-4): dequantised weights of
+# about the same spread as the bf16 workload's N(0, 0.02)).
+GROUPED_DQ_WORKLOAD = ("GroupedMatMul over int8 weights (DequantizeLinear blocked along K, block 128), bf16, "
+                       "M=16384 K=4096 N=2048 G=64 S=8, q U[-128,127], zp U[-8,8], scale U(1e-4,3e-4), seed 5")
+
+
+def grouped_dq_int8_moe(seed=5, M=16384, K=4096, N=2048, G=64, S=8, bs=128):
+    rng = np.random.default_rng(seed)
+    nkb = -(-K // bs)
+    inp = store(normal(rng, (M, K)), "bf16")
+    q = rng.integers(-128, 127, size=(G, K, N), dtype=np.int8, endpoint=True)
+    scale = store(uniform(rng, (G, nkb, N), 1e-4, 3e-4), "bf16")
+    zp = rng.integers(-8, 8, size=(G, nkb, N), dtype=np.int8, endpoint=True)
+    bias = store(uniform(rng, (G, N), -0.1, 0.1), "bf16")
+    idx = distinct_groups(rng, M, S, G, np.int32)
+    return dict(input=inp, qweights=q, scale=scale, zero_point=zp, block_size=bs, group_indices=idx, bias=bias,
+                dt="bf16")

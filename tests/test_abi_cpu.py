@@ -162,6 +162,30 @@ def test_grouped_argument_errors():
     assert L.omm_grouped_matmul_check(None, None, ctypes.byref(ctypes.c_int64())) == -1
 
 
+def test_grouped_dequant_argument_errors():
+    L = om.lib()
+    inp, q, idx, out = T((6, 8), BF16), T((3, 8, 5), I8), T((6, 2), I32), T((6, 2, 5), BF16)
+    sc, zp = T((3, 2, 5), BF16), T((3, 2, 5), I8)  # block_size 4 -> 2 blocks along K = 8
+    ws = L.omm_grouped_matmul_workspace_size(6, 2, 3)
+    call = lambda **kw: L.omm_grouped_matmul_dequant(
+        ctypes.byref(kw.get("inp", inp)), ctypes.byref(kw.get("q", q)), ctypes.byref(kw.get("sc", sc)),
+        kw.get("zp", ctypes.byref(zp)), kw.get("bs", 4), ctypes.byref(kw.get("idx", idx)), kw.get("bias", None),
+        ctypes.byref(kw.get("out", out)), kw.get("ws", FAKE), kw.get("wsb", ws), None)
+    assert call(q=T((3, 8, 5), BF16)) == -2          # weights must be int8 / uint8
+    assert call(sc=T((3, 2, 5), F16)) == -2          # scale of the input's type
+    assert call(zp=ctypes.byref(T((3, 2, 5), U8))) == -2  # zero point of the weights' type
+    assert call(out=T((6, 2, 5), F16)) == -2
+    assert call(bs=0) == -3
+    assert call(bs=3) == -3                          # ceil(8 / 3) = 3 blocks, scale has 2
+    assert call(sc=T((3, 1, 5), BF16)) == -3
+    assert call(zp=ctypes.byref(T((3, 2, 4), I8))) == -3
+    assert call(q=T((3, 7, 5), I8)) == -3
+    assert call(bias=ctypes.byref(T((3, 4), BF16))) == -3
+    assert call(inp=T((6, 8), I8), q=T((3, 8, 5), I8)) == -2
+    assert call(ws=None) == -6
+    assert call(sc=T((3, 2, 5), F64), inp=T((6, 8), F64), out=T((6, 2, 5), F64)) == -5
+
+
 def test_binding_rejects_host_tensors():
     import torch
     with pytest.raises(ValueError):
