@@ -12,7 +12,9 @@ multiply-adds counted like flops) divided by the step time.  Each workload is
 also timed on its own (median of HIP-event intervals around its call) and
 reported against the MI355X dense MFMA peak of its type under `per_config`;
 `cold_ms` there is the median of calls issued right after a 512 MiB write that
-evicts the last-level cache (operands start in HBM only).
+evicts the last-level cache (operands start in HBM only).  `next_rows` times
+workloads outside the step the same way (GroupedMatMul over int8 weights with
+the dequantisation fused); they are not part of `value`.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--only NAME]
        python bench.py --copy-calibration      (1 GiB device-to-device copies, for
@@ -115,6 +117,33 @@ def time_each(torch, fn, reps):
     torch.cuda.synchronize()
     ms = sorted(s.elapsed_time(e) for s, e in evs)
     return ms[len(ms) // 2], ms
+
+
+def next_rows(torch, om, synth, dev, reps):
+    """Workloads beyond the five-workload step, timed the same way but not part
+    of `value`: GroupedMatMul over int8 weights with the dequantisation fused
+    (the grouped workload's shapes, block 128)."""
+    c = synth.grouped_dq_int8_moe()
+    M, S = c["group_indices"].shape
+    G, K, N = c["qweights"].shape
+    d = dict(input=dev(c["input"], "bf16"), q=dev(c["qweights"]), scale=dev(c["scale"], "bf16"),
+             zp=dev(c["zero_point"]), idx=dev(c["group_indices"]), bias=dev(c["bias"], "bf16"))
+    out = torch.empty((M, S, N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(om.grouped_matmul_workspace_size(M, S, G), dtype=torch.uint8, device="cuda")
+    fn = lambda: om.grouped_matmul_dequant(d["input"], d["q"], d["scale"], d["zp"], c["block_size"], d["idx"],
+                                           d["bias"], out, ws)
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    med, _ = time_each(torch, fn, reps)
+    ops = 2 * M * S * K * N
+    byts = M * K * 2 + G * K * N + c["scale"].size * 2 + c["zero_point"].size + G * N * 2 + M * S * N * 2 + M * S * 4
+    rate = ops / (med * 1e-3) / 1e12
+    log("%-20s %9.4f ms  %8.1f T/s  %5.1f%% of bf16 peak (not in the step)" % ("grouped_dq_int8_moe", med, rate,
+                                                                               100 * rate / PEAK["bf16"]))
+    return [dict(workload="grouped_dq_int8_moe", desc=synth.GROUPED_DQ_WORKLOAD, dtype="bf16 x int8-dequant",
+                 ms=round(med, 4), tflops=round(rate, 2), frac_peak=round(rate / PEAK["bf16"], 4),
+                 hbm_gbs=round(byts / (med * 1e-3) / 1e9, 1))]
 
 
 def time_cold(torch, fn, reps, flush):
@@ -224,6 +253,8 @@ def main():
     ap.add_argument("--cold-reps", type=int, default=5,
                     help="calls per workload timed right after a 512 MiB cache-flush write (0: skip)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the workloads outside the step (quantised experts), reported under next_rows")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the baseline")
     ap.add_argument("--only", default=None, help="comma-separated workload names")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -301,6 +332,8 @@ def main():
                    "ops_per_step": total_ops},
         "roofline": roof, "per_config": per,
     }
+    if not args.no_next and only is None:
+        out["next_rows"] = next_rows(torch, om, synth, dev, args.reps)
     if not args.no_cpu:
         log("timing the CPU oracle baseline ...")
         out["cpu_baseline"] = cpu_baseline(W, args.cpu_budget)
