@@ -124,14 +124,16 @@ int omm_gemm(const omm_tensor* A, const omm_tensor* B, const omm_tensor* C, floa
  *     mult = fp32( fp32(a_scale * b_scale) / y_scale )         each op rounded to nearest even
  *     x    = fp32( fp32(acc) * mult )
  *     y    = saturate( round_half_even(x) + y_zero_point )     to T3's range
- *   Scales are fp32 (OMM_F32) device tensors.  Scale and zero point of one
+ *   Scales are fp32 (OMM_F32) or fp16 (OMM_F16) device tensors, all three of
+ *   one dtype (fp16 values are taken exactly as fp32; the page's examples use
+ *   both).  Scale and zero point of one
  *   operand have the same shape: a single element (per tensor), or per row of
  *   a -- (M), or (..., M, 1) broadcastable to a's batch dims -- or per column
  *   of b -- (N), or (..., 1, N) broadcastable to b's batch dims.  The zero
  *   point's dtype equals its operand's.  y_scale and y_zero_point hold one
  *   element each.
- * Errors: OMM_ERR_NULL, OMM_ERR_DTYPE, OMM_ERR_SHAPE, OMM_ERR_BROADCAST;
- * fp16 scales return OMM_ERR_UNSUPPORTED.  Non-positive or non-finite scales
+ * Errors: OMM_ERR_NULL, OMM_ERR_DTYPE (also scales of mixed or other dtypes),
+ * OMM_ERR_SHAPE, OMM_ERR_BROADCAST.  Non-positive or non-finite scales
  * are outside the operator's domain; the result is then unspecified.
  */
 int omm_qlinear_matmul_output_shape(const omm_tensor* a, const omm_tensor* b, int32_t* ndim, int64_t* shape);

@@ -400,10 +400,10 @@ int omm_qlinear_matmul(const omm_tensor* a, const omm_tensor* a_scale, const omm
     if (!is8(a->dtype) || !is8(b->dtype) || !is8(y_zero_point->dtype)) return OMM_ERR_DTYPE;
     if (a_zero_point->dtype != a->dtype || b_zero_point->dtype != b->dtype || y->dtype != y_zero_point->dtype)
         return OMM_ERR_DTYPE;
-    for (const omm_tensor* sc : {a_scale, b_scale, y_scale}) {
-        if (sc->dtype == OMM_F16) return OMM_ERR_UNSUPPORTED;
-        if (sc->dtype != OMM_F32) return OMM_ERR_DTYPE;
-    }
+    // scales: fp32, or fp16 (upcast exactly); the three alike
+    if (a_scale->dtype != OMM_F32 && a_scale->dtype != OMM_F16) return OMM_ERR_DTYPE;
+    if (b_scale->dtype != a_scale->dtype || y_scale->dtype != a_scale->dtype) return OMM_ERR_DTYPE;
+    const int64_t ses = elem_size(a_scale->dtype);
     if (!same_shape(a_scale, a_zero_point) || !same_shape(b_scale, b_zero_point)) return OMM_ERR_BROADCAST;
     int64_t n;
     numel(y_scale, &n);
@@ -445,11 +445,12 @@ int omm_qlinear_matmul(const omm_tensor* a, const omm_tensor* a_scale, const omm
         q.a = (const char*)a->data + off[0];
         q.b = (const char*)b->data + off[1];
         q.y = (char*)y->data + off[2];
-        q.a_scale = (const float*)a_scale->data + off[3];
+        q.a_scale = (const char*)a_scale->data + off[3] * ses;
         q.a_zp = (const char*)a_zero_point->data + off[3];
-        q.b_scale = (const float*)b_scale->data + off[4];
+        q.b_scale = (const char*)b_scale->data + off[4] * ses;
         q.b_zp = (const char*)b_zero_point->data + off[4];
-        q.y_scale = (const float*)y_scale->data;
+        q.y_scale = y_scale->data;
+        q.scale_f16 = a_scale->dtype == OMM_F16;
         q.y_zp = y_zero_point->data;
         q.M = g.M;
         q.N = g.N;

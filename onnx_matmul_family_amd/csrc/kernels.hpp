@@ -37,11 +37,11 @@ struct QArgs {
     const void* a;
     const void* b;
     void* y;
-    const float* a_scale;
+    const void* a_scale;   // fp32, or fp16 when scale_f16 (all three scales alike)
     const void* a_zp;
-    const float* b_scale;
+    const void* b_scale;
     const void* b_zp;
-    const float* y_scale;
+    const void* y_scale;
     const void* y_zp;
     int64_t M, N, K;
     int64_t lda, ldb, ldy;
@@ -50,6 +50,7 @@ struct QArgs {
     int64_t ap_sm, bp_sn;                    // parameter stride along m / n
     int64_t nb0, nb1;
     int a_u8, b_u8, y_u8;                    // 1 = uint8
+    int scale_f16;                           // 1 = the scales are fp16 (upcast exactly)
 };
 
 struct GroupedArgs {

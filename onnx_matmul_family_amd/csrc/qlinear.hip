@@ -527,7 +527,11 @@ __global__ __launch_bounds__(NT) void qlinear_kernel(QArgs p, int tiles_m, int t
     int* ZB = (int*)smem + 1536;
     float* SB = (float*)smem + 1792;
     const uint32_t Ku = (uint32_t)K;
-    const float sy = p.y_scale[0];
+    // fp16 scales are exactly representable in fp32
+    auto ldscale = [&](const void* q, int64_t i) {
+        return p.scale_f16 ? from_bits<1>(((const uint16_t*)q)[i]) : ((const float*)q)[i];
+    };
+    const float sy = ldscale(p.y_scale, 0);
     // scales inside [2^-30, 2^30] (or zero) keep the fast division exact
     auto tame = [](float v) {
         const float av = __builtin_fabsf(v);
@@ -541,12 +545,12 @@ __global__ __launch_bounds__(NT) void qlinear_kernel(QArgs p, int tiles_m, int t
         if (m < M) {
             const int64_t apo = z0 * p.ap_bs0 + z1 * p.ap_bs1 + m * p.ap_sm;
             za = ldzp(p.a_zp, apo, AU8);
-            sa = p.a_scale[apo];
+            sa = ldscale(p.a_scale, apo);
         }
         if (n < N) {
             const int64_t bpo = z0 * p.bp_bs0 + z1 * p.bp_bs1 + n * p.bp_sn;
             zb = ldzp(p.b_zp, bpo, BU8);
-            sb = p.b_scale[bpo];
+            sb = ldscale(p.b_scale, bpo);
         }
         U[t] = (uint32_t)rowsum[t] - Ku * (uint32_t)za;
         ZA[t] = za;

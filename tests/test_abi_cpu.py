@@ -130,7 +130,8 @@ def test_qlinear_argument_errors():
     assert L.omm_qlinear_matmul(*args(a=T((4, 8), F32)), None) == -2          # a not 8-bit
     assert L.omm_qlinear_matmul(*args(az=T((), U8)), None) == -2             # zp dtype != a dtype
     assert L.omm_qlinear_matmul(*args(y=T((4, 5), U8)), None) == -2          # y dtype != y_zp dtype
-    assert L.omm_qlinear_matmul(*args(as_=T((), F16)), None) == -5           # fp16 scales: not implemented
+    assert L.omm_qlinear_matmul(*args(as_=T((), F16)), None) == -2           # scales of mixed dtypes
+    assert L.omm_qlinear_matmul(*args(as_=T((), BF16), bs=T((), BF16), ys=T((), BF16)), None) == -2
     assert L.omm_qlinear_matmul(*args(as_=T((4,), F32)), None) == -4         # scale / zp shapes differ
     assert L.omm_qlinear_matmul(*args(as_=T((5,), F32), az=T((5,), I8)), None) == -4   # not M
     assert L.omm_qlinear_matmul(*args(bs=T((1, 4), F32), bz=T((1, 4), I8)), None) == -4  # not N

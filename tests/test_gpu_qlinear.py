@@ -25,7 +25,9 @@ def _gpu():
 
 
 def run(a, asc, az, b, bsc, bz, ys, yz):
-    asc, bsc, ys = (np.asarray(x, np.float32) for x in (asc, bsc, ys))
+    # fp16 scales go to the library as fp16; anything else as fp32
+    f16 = np.asarray(asc).dtype == np.float16
+    asc, bsc, ys = (np.asarray(x, np.float16 if f16 else np.float32) for x in (asc, bsc, ys))
     y = om.qlinear_matmul(dev(a), dev(asc), dev(az), dev(b), dev(bsc), dev(bz), dev(ys), dev(yz))
     torch.cuda.synchronize()
     ref, _ = oracle.qlinear_matmul(a, asc, az, b, bsc, bz, ys, yz)
@@ -33,16 +35,34 @@ def run(a, asc, az, b, bsc, bz, ys, yz):
 
 
 def test_printed_examples(golden):
+    """Every printed example, its scales passed as printed (fp32 or fp16)."""
     from tests.test_oracle_examples import arr
+    seen = set()
     for ex in golden("qlinearmatmul"):
         i = ex["inputs"]
-        # fp16 scales are exactly representable in fp32: pass them as fp32
-        f32 = lambda k: arr(i[k]).astype(np.float32)
-        got, ref = run(arr(i["a"]), f32("a_scale"), arr(i["a_zero_point"]), arr(i["b"]), f32("b_scale"),
-                       arr(i["b_zero_point"]), f32("y_scale"), arr(i["y_zero_point"]))
+        sc = lambda k: arr(i[k])
+        seen.add(sc("a_scale").dtype)
+        got, ref = run(arr(i["a"]), sc("a_scale"), arr(i["a_zero_point"]), arr(i["b"]), sc("b_scale"),
+                       arr(i["b_zero_point"]), sc("y_scale"), arr(i["y_zero_point"]))
         exp = arr(ex["outputs"]["y"])
         assert np.array_equal(got, exp), (ex["cite"], got, exp)
         assert np.array_equal(got, ref), ex["cite"]
+    assert np.dtype(np.float16) in seen and np.dtype(np.float32) in seen
+
+
+@pytest.mark.parametrize("M,K,N", [(300, 272, 208), (512, 512, 512)])
+def test_fp16_scales_per_row_and_column(M, K, N):
+    """fp16 scales (upcast exactly) against the oracle, per row / per column, full and ragged tiles."""
+    rng = np.random.default_rng(M + N)
+    a = rng.integers(-128, 128, (M, K)).astype(np.int8)
+    b = rng.integers(-128, 128, (K, N)).astype(np.int8)
+    asc = rng.uniform(0.002, 0.01, (M, 1)).astype(np.float16)
+    bsc = rng.uniform(0.002, 0.01, (1, N)).astype(np.float16)
+    az = rng.integers(-16, 17, (M, 1)).astype(np.int8)
+    bz = rng.integers(-16, 17, (1, N)).astype(np.int8)
+    ys, yz = np.array(0.05, np.float16), np.array(3, np.int8)
+    got, ref = run(a, asc, az, b, bsc, bz, ys, yz)
+    assert np.array_equal(got, ref)
 
 
 TYPES = [(np.int8, np.int8, np.int8), (np.uint8, np.int8, np.uint8), (np.int8, np.uint8, np.int8),
