@@ -360,13 +360,14 @@ struct DmaSrc {
     }
 };
 
-// 8-bit MN-major tile (int8 b, n contiguous): 128 k rows of R bytes, 16-byte
-// chunk c of row k stored at chunk c ^ mswz8(k).  LDS block b = rows 4b..4b+3
-// (R = 256); lane p -> row p / 16, physical chunk p % 16.
-template <int R>
+// 8-bit MN-major tile (int8 b, n contiguous): KR k rows of R bytes per stage,
+// 16-byte chunk c of row k stored at chunk c ^ mswz8(k).  LDS block b = rows
+// 4b..4b+3 (R = 256); lane p -> row p / 16, physical chunk p % 16.
+template <int R, int KR = 128>
 struct DmaSrcMN8 {
     static_assert(R == 256, "256-byte rows");
-    static constexpr int PER_WAVE = 8;  // 32 blocks per stage
+    static constexpr int PER_WAVE = KR / 16;  // KR / 4 blocks per stage
+    static_assert(PER_WAVE % 2 == 0, "block phase == parity of the wave-local block index");
     const char* base;
     int64_t step;
     uint32_t ldb;
@@ -385,7 +386,7 @@ struct DmaSrcMN8 {
         mn0 = mn0_;
         ldb = (uint32_t)ld;
         base = (const char*)b + mn0;
-        step = 128 * ld;
+        step = (int64_t)KR * ld;
 #pragma unroll
         for (int q = 0; q < 2; ++q) lane_off[q] = (uint32_t)(lane >> 4) * ldb + (chunk(q) << 4);
     }
@@ -403,7 +404,7 @@ struct DmaSrcMN8 {
         const int b = wave * PER_WAVE + j;
         uint32_t voff = lane_off[j & 1] + (uint32_t)(b * 4) * ldb;
         if (CHECKED) {
-            const int64_t k = (int64_t)kt * 128 + b * 4 + (lane >> 4);
+            const int64_t k = (int64_t)kt * KR + b * 4 + (lane >> 4);
             const int64_t mn = mn0 + 16 * (int64_t)chunk(j & 1);
             if (!(k < K && mn < MN)) voff = DMA_OOB;
         }

@@ -556,6 +556,245 @@ __device__ __forceinline__ void mainloop_deq_dma(f32x16_t (&acc)[4][4], char* s0
     }
 }
 
+// ---- DMA variant: the int8 weight tile itself goes global -> LDS by DMA (64
+// k rows x 256 bytes per stage, the 8-bit MN-major layout) and each lane
+// dequantises its MFMA operand after the transposing read: ds_read_b64_tr_b8
+// gives lane l the 8 k-values k = 16 s + 8 (l/32) + 0..7 of column
+// colb + l%32, exactly the bf16 operand layout, so one scale and one zero
+// point (of that column and the stage's block) serve all 8.  LDS holds half
+// the weight bytes of the bf16 kernel and the weights never pass through
+// registers on their way in.
+
+template <int DT, bool QU8>
+__device__ __forceinline__ u32x4_t dq8(u32x2_t raw, float sf, float cf) {
+    uint32_t u[2] = {raw.x, raw.y};
+    if constexpr (!QU8) {
+        u[0] ^= 0x80808080u;  // q + 128 in every byte
+        u[1] ^= 0x80808080u;
+    }
+    float w[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = __builtin_fmaf((float)((u[e >> 2] >> (8 * (e & 3))) & 0xffu), sf, cf);
+    return u32x4_t{pack2<DT>(w[0], w[1]), pack2<DT>(w[2], w[3]), pack2<DT>(w[4], w[5]), pack2<DT>(w[6], w[7])};
+}
+
+__device__ __forceinline__ u32x2_t read_frag_q8(const char* lds, int colb, int s, int lane) {
+    const int g = lane >> 4, i = lane & 15;
+    const int krow = 16 * s + 8 * (g >> 1) + (i >> 1);
+    const int ncol = colb + 16 * (g & 1) + 8 * (i & 1);
+    const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(OMM_LDS(i32x2_t, lds + mmaj8_off<GBN>(krow, ncol)));
+    return __builtin_bit_cast(u32x2_t, v);
+}
+
+struct FragsDQ {
+    u32x4_t a[4], b[4];
+    u32x2_t braw[4];
+};
+
+// read r of a k-block (frag_order: B0 A0 B1 B2 B3 A1 A2 A3) goes out after
+// MFMA 2r; weight fragment j is converted 4 MFMAs after its read
+constexpr int dq_read_pos(int f) {
+    for (int r = 0; r < 8; ++r)
+        if (core16::frag_order(4, 4, r) == f) return r;
+    return -1;
+}
+constexpr int dq_conv_slot(int j) { return 2 * dq_read_pos(4 + j) + 4; }
+
+// per-stage dequantisation constants of this lane's 4 columns: w = fma(q', sf, cf)
+struct DqScales {
+    float sf[4], cf[4];
+};
+
+template <int DT, bool QU8, int X>
+__device__ __forceinline__ void dq_slot_reads(FragsDQ& nxt, const char* lds, int s, int lane, int wm, int wn,
+                                              const DqScales& sc) {
+    using namespace core16;
+    constexpr int A_BYTES = GBM * KSTEP * 2;
+    if constexpr (X % 2 == 0 && X / 2 < 8) {
+        constexpr int f = frag_order(4, 4, X / 2);
+        if constexpr (f < 4)
+            nxt.a[f] = read_frag<GBM, true>(lds, wm * 128 + 32 * f, s, lane);
+        else
+            nxt.braw[f - 4] = read_frag_q8(lds + A_BYTES, wn * 128 + 32 * (f - 4), s, lane);
+    }
+    static_for<0, 4>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        if constexpr (dq_conv_slot(j) == X) nxt.b[j] = dq8<DT, QU8>(nxt.braw[j], sc.sf[j], sc.cf[j]);
+    });
+}
+
+// One k-block of MFMAs on `cur`, the reads (and conversions) of k-block s of
+// `lds` into `nxt`, and this wave's DMA instructions D0 .. D1-1 of stage kt
+// into buffer Xb spread between the MFMAs (none when D0 == D1).
+template <int DT, bool QU8, int D0, int D1, class SA, class SB>
+__device__ __forceinline__ void kblock_dq(f32x16_t (&acc)[4][4], const FragsDQ& cur, FragsDQ& nxt, const char* lds,
+                                          int s, char* Xb, const SA& srcA, const SB& srcB, int kt, bool live,
+                                          int lane, int wm, int wn, int wave, const DqScales& sc) {
+    using namespace core16;
+    constexpr int A_BYTES = GBM * KSTEP * 2;
+    constexpr int NM = 16, ND = D1 - D0, LA = SA::PER_WAVE;
+    DmaCtx ca{}, cb{};
+    if constexpr (ND > 0) {
+        ca = srcA.ctx(Xb, kt, live);
+        cb = srcB.ctx(Xb + A_BYTES, kt, live);
+    }
+    static_for<0, NM>([&](auto xc) {
+        constexpr int x = decltype(xc)::value;
+        acc[x / 4][x % 4] = mfma32x32x16<DT>(cur.b[x % 4], cur.a[x / 4], acc[x / 4][x % 4]);
+        if constexpr (ND > 0)
+            static_for<D0 + (x * ND + NM - 1) / NM, D0 + ((x + 1) * ND + NM - 1) / NM>(
+                [&](auto dc) { dma_one<true, LA, decltype(dc)::value>(srcA, srcB, ca, cb, kt, wave); });
+        dq_slot_reads<DT, QU8, x>(nxt, lds, s, lane, wm, wn, sc);
+        fence_sched();
+    });
+}
+
+// One stage's scales and zero points (the block of the stage's k, the tile's
+// 256 columns) go to the stage's LDS buffer by DMA next to the tiles: wave 0
+// loads the 512 bytes of scales, wave 1 the 256 bytes of zero points (no zero
+// points, or columns past N: zeros).  After the stage's barrier each lane
+// reads the 4 values of its columns from LDS.
+constexpr int DQ_SC_OFF = GBM * core16::KSTEP * 2 + GBN * core16::KSTEP;  // after the A and int8 B tiles
+struct DqParams {
+    const char* sc;  // this group's scales (N per block, 2 bytes each)
+    const char* zp;  // this group's zero points, or nullptr
+    int64_t N, bs, n0;
+    __device__ __forceinline__ void issue(char* buf, int kt, bool live, int wave, int lane) const {
+        using namespace core16;
+        const int w = __builtin_amdgcn_readfirstlane(wave);  // uniform: the buffer resource lives in SGPRs
+        if (w >= 2) return;
+        const bool isz = w == 1;
+        const char* base = isz ? zp : sc;
+        const int es = isz ? 1 : 2;
+        const bool lv = __builtin_amdgcn_readfirstlane((int)(live && base != nullptr)) != 0;
+        const int64_t kb = lv ? (int64_t)kt * KSTEP / bs : 0;
+        const i32x4_t r = make_rsrc(lv ? base + (kb * N + n0) * es : sc, lv);
+        const int nl = isz ? 16 : 32;  // lanes with data: 16 bytes = 8 scales or 16 zero points each
+        const uint32_t voff = (lane < nl && n0 + (int64_t)lane * (16 / es) < N) ? (uint32_t)lane * 16u : DMA_OOB;
+        dma16u(r, lds_addr(buf + DQ_SC_OFF + (isz ? 1024 : 0)), voff);
+    }
+    // this lane's columns: wn * 128 + 32 j + lane % 32
+    template <int DT, bool QU8>
+    __device__ __forceinline__ void to_scales(const char* buf, int wn, int lane, DqScales& o) const {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = wn * 128 + 32 * j + (lane & 31);
+            o.sf[j] = from_bits<DT>(*(const uint16_t*)(buf + DQ_SC_OFF + 2 * c));
+            const uint32_t zb = *(const uint8_t*)(buf + DQ_SC_OFF + 1024 + c);
+            const int zs = QU8 ? (int)zb : (int)(int8_t)zb + 128;
+            o.cf[j] = -(float)zs * o.sf[j];
+        }
+    }
+};
+
+template <int DT, bool QU8, class SA, class SB>
+__device__ __forceinline__ void dq_stage(f32x16_t (&acc)[4][4], FragsDQ& fc, FragsDQ& fn, char* X, char* Y,
+                                         const SA& srcA, const SB& srcB, DqParams& prm, DqScales& sc, int kt, int nk,
+                                         int lane, int wm, int wn, int wave) {
+    using namespace core16;
+    constexpr int LD = SA::PER_WAVE + SB::PER_WAVE, H = LD / 2;
+    fence_sched();
+    prm.issue(Y, kt + 1, kt + 1 < nk, wave, lane);
+    kblock_dq<DT, QU8, H, LD>(acc, fc, fn, X, 1, Y, srcA, srcB, kt + 1, kt + 1 < nk, lane, wm, wn, wave, sc);
+    kblock_dq<DT, QU8, 0, 0>(acc, fn, fc, X, 2, Y, srcA, srcB, kt, false, lane, wm, wn, wave, sc);
+    kblock_dq<DT, QU8, 0, 0>(acc, fc, fn, X, 3, Y, srcA, srcB, kt, false, lane, wm, wn, wave, sc);
+    wait_vm<0>();     // stage kt+1 (tiles and scales) has landed
+    __syncthreads();  // ... for every wave; every read of X is done
+    prm.template to_scales<DT, QU8>(Y, wn, lane, sc);
+    fence_sched();
+    kblock_dq<DT, QU8, 0, H>(acc, fn, fc, Y, 0, X, srcA, srcB, kt + 2, kt + 2 < nk, lane, wm, wn, wave, sc);
+}
+
+template <int DT, bool QU8, class SA, class SB>
+__device__ __forceinline__ void mainloop_dq_dma(f32x16_t (&acc)[4][4], char* __restrict__ s0, char* __restrict__ s1,
+                                                const SA& srcA, const SB& srcB, DqParams& prm, int nk, int lane,
+                                                int wm, int wn, int wave) {
+    using namespace core16;
+    constexpr int A_BYTES = GBM * KSTEP * 2;
+    constexpr int LA = SA::PER_WAVE, LD = SA::PER_WAVE + SB::PER_WAVE, H = LD / 2;
+    if (nk <= 0) return;
+    prm.issue(s0, 0, true, wave, lane);
+    {
+        const DmaCtx a0 = srcA.ctx(s0, 0, true), b0 = srcB.ctx(s0 + A_BYTES, 0, true);
+        static_for<0, LD>([&](auto dc) { dma_one<true, LA, decltype(dc)::value>(srcA, srcB, a0, b0, 0, wave); });
+        const DmaCtx a1 = srcA.ctx(s1, 1, nk > 1), b1 = srcB.ctx(s1 + A_BYTES, 1, nk > 1);
+        static_for<0, H>([&](auto dc) { dma_one<true, LA, decltype(dc)::value>(srcA, srcB, a1, b1, 1, wave); });
+    }
+    wait_vm<H>();
+    __syncthreads();
+    DqScales sc;
+    prm.template to_scales<DT, QU8>(s0, wn, lane, sc);
+    fence_sched();
+    FragsDQ fc, fn;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fc.a[i] = read_frag<GBM, true>(s0, wm * 128 + 32 * i, 0, lane);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        fc.b[j] = dq8<DT, QU8>(read_frag_q8(s0 + A_BYTES, wn * 128 + 32 * j, 0, lane), sc.sf[j], sc.cf[j]);
+    for (int kt = 0; kt < nk; kt += 2) {
+        dq_stage<DT, QU8>(acc, fc, fn, s0, s1, srcA, srcB, prm, sc, kt, nk, lane, wm, wn, wave);
+        dq_stage<DT, QU8>(acc, fc, fn, s1, s0, srcA, srcB, prm, sc, kt + 1, nk, lane, wm, wn, wave);
+    }
+    wait_vm<0>();
+}
+
+// Weights by DMA: K % 64 == 0, N % 16 == 0, 16-byte aligned q, scale and
+// zero-point rows (16-byte aligned bases), block size a multiple of 64 (one
+// block per stage).
+template <int DT, bool QU8>
+__global__ __launch_bounds__(256) void grouped16_dq_dma_kernel(GroupedArgs a, const char* ws, int tiles_n) {
+    __shared__ __attribute__((aligned(1024))) char s0[(GBM + GBN) * core16::KSTEP * 2];
+    __shared__ __attribute__((aligned(1024))) char s1[(GBM + GBN) * core16::KSTEP * 2];
+    __shared__ int orow_s[GBM];
+    using namespace core16;
+    const int ntiles = ((const int*)ws)[0];
+    const int total = ntiles * tiles_n;
+    const int b = (int)blockIdx.x, x = b & 7, l = b >> 3;
+    const int per = total >> 3, extra = total & 7;
+    if (l >= per + (x < extra ? 1 : 0)) return;
+    int tm, tn;
+    grouped_order(x * per + min(x, extra) + l, ntiles, tiles_n, 4, tm, tn);
+
+    const int4 te = ((const int4*)(ws + off_tiles(a.G)))[tm];
+    const int g = te.x, start = te.y, rows = te.z;
+    const int* sorted = (const int*)(ws + off_sorted(a.M * a.S, a.G));
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t K = a.K, N = a.N, S = a.S;
+    const int64_t n0 = (int64_t)tn * GBN;
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    const int nk = (int)(K / KSTEP);
+    if (t < GBM) orow_s[t] = t < rows ? sorted[start + t] : -1;
+
+    GatherDma<GBM> srcA;
+    srcA.base = (const char*)a.input;
+    srcA.K = K;
+    srcA.lane = lane;
+#pragma unroll
+    for (int j = 0; j < GatherDma<GBM>::PER_WAVE; ++j) {
+        const int r = GatherDma<GBM>::row_of(wave, j, lane);
+        srcA.roff[j] = r < rows ? (uint32_t)((int64_t)(sorted[start + r] / S) * K * 2) +
+                                      (GatherDma<GBM>::chunk(j, lane) << 4)
+                                : DMA_OOB;
+    }
+    DmaSrcMN8<GBN, KSTEP> srcB;
+    srcB.init((const uint8_t*)a.weights + (int64_t)g * K * N, N, n0, N, K, lane);
+    DqParams prm;
+    prm.sc = (const char*)a.wscale + (int64_t)g * a.nkb * N * 2;
+    prm.zp = a.wzp ? (const char*)a.wzp + (int64_t)g * a.nkb * N : nullptr;
+    prm.N = N;
+    prm.bs = a.bs;
+    prm.n0 = n0;
+    mainloop_dq_dma<DT, QU8>(acc, s0, s1, srcA, srcB, prm, nk, lane, wm, wn, wave);
+    grouped_epilogue<DT, true>(acc, a, g, rows, start, sorted, n0, lane, wave, s0, s1, orow_s);
+}
+
 template <int DT, bool QU8, bool FAST>
 __global__ __launch_bounds__(256) void grouped16_dq_kernel(GroupedArgs a, const char* ws, int tiles_n) {
     __shared__ __attribute__((aligned(1024))) char s0[(GBM + GBN) * core16::KSTEP * 2];
@@ -733,6 +972,20 @@ hipError_t launch_grouped_dq(const GroupedArgs& a, int dt, void* ws, hipStream_t
     dim3 grid((unsigned)(max_mtiles * tiles_n));
     const char* wsc = (const char*)ws;
     const int tn = (int)tiles_n;
+    // weights by DMA as well: whole stages (K % 64 == 0), 16-byte weight rows
+    const bool dma = fast && a.K % core16::KSTEP == 0 && a.N % 16 == 0 && al(a.weights, 16) &&
+                     (!a.wzp || al(a.wzp, 16)) && core16::KSTEP * a.N < (1LL << 31) &&
+                     a.nkb * a.N * 2 < (1LL << 31);
+    if (dma) {
+        if (dt == 0) {
+            if (qu8) hipLaunchKernelGGL((grouped16_dq_dma_kernel<0, true>), grid, dim3(256), 0, s, a, wsc, tn);
+            else hipLaunchKernelGGL((grouped16_dq_dma_kernel<0, false>), grid, dim3(256), 0, s, a, wsc, tn);
+        } else {
+            if (qu8) hipLaunchKernelGGL((grouped16_dq_dma_kernel<1, true>), grid, dim3(256), 0, s, a, wsc, tn);
+            else hipLaunchKernelGGL((grouped16_dq_dma_kernel<1, false>), grid, dim3(256), 0, s, a, wsc, tn);
+        }
+        return hipGetLastError();
+    }
 #define OMM_DQ(D, U, F) hipLaunchKernelGGL((grouped16_dq_kernel<D, U, F>), grid, dim3(256), 0, s, a, wsc, tn)
     if (dt == 0) {
         if (qu8) { if (fast) OMM_DQ(0, true, true); else OMM_DQ(0, true, false); }

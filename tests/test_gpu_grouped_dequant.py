@@ -1,9 +1,9 @@
 """GPU parity of GroupedMatMul over DequantizeLinear weights against the CPU oracle.
 
 Covers bf16 / fp16 / fp32, int8 and uint8 weights, zero points present and
-absent, block sizes that are multiples of the 64-deep stage (the fast path:
-input by DMA, weights dequantised in registers) and others (element-wise
-path), one block per group and column (block_size >= K), ragged M / N / K,
+absent, the three 16-bit kernels (int8 weight tile by DMA and dequantised
+after the transposing LDS read; weights register-staged and dequantised
+before the LDS store; element-wise for other block sizes and layouts), one block per group and column (block_size >= K), ragged M / N / K,
 the rounding of each dequantised weight to T, exact small-integer results,
 invalid indices, and the full-size workload on sampled outputs."""
 import numpy as np
@@ -45,10 +45,11 @@ def make(rng, M, K, N, G, S, bs, qdt, with_zp, dt, with_bias=True, srange=(0.002
 
 
 CASES = [  # M, K, N, G, S, block_size
-    (300, 256, 264, 7, 3, 128),    # fast; ragged last column tile
-    (1000, 512, 512, 16, 4, 64),   # fast; several row tiles per group
-    (150, 200, 256, 5, 2, 64),     # fast; K tail inside the last stage
-    (257, 192, 256, 3, 2, 192),    # fast; one block per group and column (block_size == K)
+    (300, 256, 272, 7, 3, 128),    # weights by DMA; ragged last column tile
+    (300, 256, 264, 7, 3, 128),    # register-staged fast path (N % 16 != 0); ragged last column tile
+    (1000, 512, 512, 16, 4, 64),   # weights by DMA; several row tiles per group
+    (150, 200, 256, 5, 2, 64),     # register-staged fast path; K tail inside the last stage
+    (257, 192, 256, 3, 2, 192),    # weights by DMA; one block per group and column (block_size == K), odd stage count
     (513, 200, 300, 5, 5, 40),     # element-wise: block 40, N % 8 != 0
     (64, 136, 64, 1, 1, 136),      # element-wise: one block, block % 64 != 0
     (100, 100, 72, 4, 2, 1000),    # element-wise: block_size > K
@@ -93,7 +94,7 @@ def test_exact_small_integers_f16(bs, qdt):
 def test_dequantised_weight_rounded_to_bf16(bs):
     """(127 + 128) * 1.0078125 = 256.9921875 is held in bf16 as 256; a second
     weight that is exact makes the difference visible in the sum."""
-    K, N = 64, 8
+    K, N = 64, 16  # bs 64: the weights-by-DMA kernel; bs 1: the element-wise path
     nkb = K // bs
     q = np.zeros((1, K, N), np.int8)
     zp = np.zeros((1, nkb, N), np.int8)
