@@ -14,7 +14,7 @@ reported against the MI355X dense MFMA peak of its type under `per_config`;
 `cold_ms` there is the median of calls issued right after a 512 MiB write that
 evicts the last-level cache (operands start in HBM only).  `next_rows` times
 workloads outside the step the same way (GroupedMatMul over int8 weights with
-the dequantisation fused); they are not part of `value`.
+the dequantisation fused, an fp64 Gemm); they are not part of `value`.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--only NAME]
        python bench.py --copy-calibration      (1 GiB device-to-device copies, for
@@ -39,7 +39,7 @@ sys.path.insert(0, ROOT)
 METRIC = "TFLOP/s (int8: TOPS) per config and % of MI355X dense MFMA peak, 1 GPU"
 UNIT = "TFLOP/s (int8: TOPS)"
 # MI355X datasheet dense peaks (TFLOP/s or TOPS) and HBM bandwidth (GB/s)
-PEAK = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "int8": 5033.2}
+PEAK = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "int8": 5033.2, "f64": 78.6}
 HBM_GBS = 8000.0
 
 
@@ -141,9 +141,28 @@ def next_rows(torch, om, synth, dev, reps):
     rate = ops / (med * 1e-3) / 1e12
     log("%-20s %9.4f ms  %8.1f T/s  %5.1f%% of bf16 peak (not in the step)" % ("grouped_dq_int8_moe", med, rate,
                                                                                100 * rate / PEAK["bf16"]))
-    return [dict(workload="grouped_dq_int8_moe", desc=synth.GROUPED_DQ_WORKLOAD, dtype="bf16 x int8-dequant",
+    rows = [dict(workload="grouped_dq_int8_moe", desc=synth.GROUPED_DQ_WORKLOAD, dtype="bf16 x int8-dequant",
                  ms=round(med, 4), tflops=round(rate, 2), frac_peak=round(rate / PEAK["bf16"], 4),
                  hbm_gbs=round(byts / (med * 1e-3) / 1e9, 1))]
+    del d, out, ws
+    # fp64 Gemm (MFMA f64), 4096^3, N(0,1) operands, C[4096], alpha=beta=1
+    n = 4096
+    rng = np.random.default_rng(6)
+    A64 = torch.from_numpy(rng.standard_normal((n, n))).cuda()
+    B64 = torch.from_numpy(rng.standard_normal((n, n))).cuda()
+    C64 = torch.from_numpy(rng.standard_normal(n)).cuda()
+    Y64 = torch.empty((n, n), dtype=torch.float64, device="cuda")
+    fn = lambda: om.gemm(A64, B64, C64, 1.0, 1.0, 0, 1, Y64)
+    fn()
+    torch.cuda.synchronize()
+    med, _ = time_each(torch, fn, max(5, reps // 3))
+    rate = 2 * n ** 3 / (med * 1e-3) / 1e12
+    log("%-20s %9.4f ms  %8.1f T/s  %5.1f%% of f64 peak (not in the step)" % ("gemm_f64_4096", med, rate,
+                                                                              100 * rate / PEAK["f64"]))
+    rows.append(dict(workload="gemm_f64_4096", desc="Gemm fp64 4096^3, transB=1, C[4096], alpha=beta=1, N(0,1), seed 6",
+                     dtype="f64", ms=round(med, 4), tflops=round(rate, 2), frac_peak=round(rate / PEAK["f64"], 4),
+                     hbm_gbs=round((3 * n * n + n) * 8 / (med * 1e-3) / 1e9, 1)))
+    return rows
 
 
 def time_cold(torch, fn, reps, flush):

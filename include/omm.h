@@ -87,9 +87,10 @@ int omm_version(void);
  *     is removed from Y (so 1-D x 1-D gives a 0-d Y).
  *   - Dims before the last two are batch dims: right-aligned, each pair equal
  *     or one of them 1 (broadcast); Y's batch dims are the broadcast shape.
- *   - T: OMM_BF16, OMM_F16 or OMM_F32 (A, B and Y all the same).  bf16/fp16
- *     accumulate in fp32 and round once (nearest-even) to T.  Other types the
- *     page allows (double, int32/64, uint32/64) return OMM_ERR_UNSUPPORTED.
+ *   - T: OMM_BF16, OMM_F16, OMM_F32 or OMM_F64 (A, B and Y all the same).
+ *     bf16/fp16 accumulate in fp32 and round once (nearest-even) to T; fp64
+ *     accumulates in fp64.  The integer types the page allows (int32/64,
+ *     uint32/64) return OMM_ERR_UNSUPPORTED.
  * Errors: OMM_ERR_NULL, OMM_ERR_DTYPE, OMM_ERR_SHAPE (ndim 0, inner dims
  * differ, or Y's shape is not the computed one), OMM_ERR_BROADCAST.
  */
@@ -106,8 +107,9 @@ int omm_matmul(const omm_tensor* A, const omm_tensor* B, omm_tensor* Y, void* st
  *     (M, 1) or (M, N) (and the equivalents with extents 1).
  *   - alpha and beta are the operator's float attributes; the ONNX defaults
  *     are alpha = 1, beta = 1, transA = transB = 0 and are the caller's to pass.
- *   - T: OMM_BF16, OMM_F16 or OMM_F32 for A, B, C and Y alike.  The epilogue is
- *     computed in fp32 from the fp32 accumulator and rounded once to T.
+ *   - T: OMM_BF16, OMM_F16, OMM_F32 or OMM_F64 for A, B, C and Y alike.  The
+ *     epilogue is computed in fp32 from the fp32 accumulator and rounded once
+ *     to T (fp64: in fp64, alpha and beta taken exactly).
  * Errors: as omm_matmul, plus OMM_ERR_BROADCAST for a C that does not fit.
  */
 int omm_gemm_output_shape(const omm_tensor* A, const omm_tensor* B, int transA, int transB,
@@ -146,8 +148,9 @@ int omm_qlinear_matmul(const omm_tensor* a, const omm_tensor* a_scale, const omm
  *   input (M, K), weights (G, K, N), group_indices (M, S) of OMM_I32 or
  *   OMM_I64, optional bias (G, N) (NULL = absent), output (M, S, N):
  *     output[m, i, :] = input[m, :] @ weights[g] (+ bias[g, :]), g = group_indices[m, i]
- *   T: OMM_BF16, OMM_F16 or OMM_F32 (input, weights, bias, output alike);
- *   fp32 accumulation, one rounding to T of (accumulator + bias).
+ *   T: OMM_BF16, OMM_F16, OMM_F32 or OMM_F64 (input, weights, bias, output
+ *   alike); fp32 accumulation (fp64 for OMM_F64), one rounding to T of
+ *   (accumulator + bias).
  *   The (m, i) pairs are counting-sorted by group on the device and each
  *   group's rows run as one GEMM against weights[g]; the gathered
  *   (M*S, K, N) weights are never formed.
@@ -181,7 +184,8 @@ int omm_grouped_matmul(const omm_tensor* input, const omm_tensor* weights, const
  *   (G, ceil(K / block_size), N) of T; w_zero_point NULL (zero) or like
  *   w_scale with qweights' dtype; block_size >= 1 (block_size >= K: one scale
  *   per group and column); group_indices, bias, output, workspace, stream and
- *   invalid indices as omm_grouped_matmul.  T: OMM_BF16, OMM_F16 or OMM_F32.
+ *   invalid indices as omm_grouped_matmul.  T: OMM_BF16, OMM_F16 or OMM_F32
+ *   (OMM_F64 returns OMM_ERR_UNSUPPORTED).
  *   The fast path needs 16-byte aligned input / 8-byte aligned q, zp, bias and
  *   output / 16-byte aligned scales, K and N multiples of 8 and block_size a
  *   multiple of 64; other layouts use an element-wise path.

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libomm.so")
 BUILD = os.path.join(HERE, "_build")
 
-SOURCES = ["api.cpp", "dense16.hip", "dense_f32.hip", "qlinear.hip", "grouped.hip"]
+SOURCES = ["api.cpp", "dense16.hip", "dense_f32.hip", "dense_f64.hip", "qlinear.hip", "grouped.hip"]
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", os.path.join(HERE, "..", "include")]

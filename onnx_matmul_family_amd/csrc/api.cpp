@@ -169,10 +169,11 @@ int for_each_outer(const Batch& b, F&& launch) {
     return OMM_OK;
 }
 
-bool is_dense_float(int dt) { return dt == OMM_BF16 || dt == OMM_F16 || dt == OMM_F32; }
+bool is_dense_float(int dt) { return dt == OMM_BF16 || dt == OMM_F16 || dt == OMM_F32 || dt == OMM_F64; }
 
 hipError_t launch_dense(const DenseArgs& a, int dt, hipStream_t s) {
     if (dt == OMM_F32) return omm::launch_dense_f32(a, s);
+    if (dt == OMM_F64) return omm::launch_dense_f64(a, s);
     return omm::launch_dense16(a, dt == OMM_BF16 ? 0 : 1, s);
 }
 
@@ -528,7 +529,7 @@ int omm_grouped_matmul(const omm_tensor* input, const omm_tensor* weights, const
     a.G = G;
     a.S = S;
     a.idx64 = group_indices->dtype == OMM_I64;
-    const int kd = dt == OMM_BF16 ? 0 : dt == OMM_F16 ? 1 : 2;
+    const int kd = dt == OMM_BF16 ? 0 : dt == OMM_F16 ? 1 : dt == OMM_F32 ? 2 : 3;
     return hip_status(omm::launch_grouped(a, kd, workspace, (hipStream_t)stream));
 }
 
@@ -548,7 +549,7 @@ int omm_grouped_matmul_dequant(const omm_tensor* input, const omm_tensor* qweigh
     if (w_scale->dtype != dt || output->dtype != dt || (bias && bias->dtype != dt)) return OMM_ERR_DTYPE;
     if (w_zero_point && w_zero_point->dtype != qweights->dtype) return OMM_ERR_DTYPE;
     if (elem_size(dt) == 0 || dt == OMM_I8 || dt == OMM_U8 || dt == OMM_I32 || dt == OMM_I64) return OMM_ERR_DTYPE;
-    if (!is_dense_float(dt)) return OMM_ERR_UNSUPPORTED;
+    if (!is_dense_float(dt) || dt == OMM_F64) return OMM_ERR_UNSUPPORTED;
     if (group_indices->dtype != OMM_I32 && group_indices->dtype != OMM_I64) return OMM_ERR_DTYPE;
     const int64_t M = osh[0], S = osh[1], N = osh[2], K = input->shape[1], G = qweights->shape[0];
     if (block_size < 1) return OMM_ERR_SHAPE;

@@ -898,19 +898,21 @@ __global__ __launch_bounds__(256) void grouped_dq_f32_kernel(GroupedArgs a, int 
     }
 }
 
-// fp32: one workgroup per (pair, 256 columns); plain fp32 dot products.
-__global__ __launch_bounds__(256) void grouped_f32_kernel(GroupedArgs a) {
-    __shared__ float row[1024];
+// fp32 / fp64: one workgroup per (pair, 256 columns); plain dot products in
+// the tensors' own type.
+template <class F>
+__global__ __launch_bounds__(256) void grouped_fp_kernel(GroupedArgs a) {
+    __shared__ F row[1024];
     const int64_t p = blockIdx.x;
     const int64_t n = (int64_t)blockIdx.y * 256 + threadIdx.x;
     const int64_t g = load_idx(a.idx, p, a.idx64);
-    if (g < 0 || g >= a.G) return;
-    const float* in = (const float*)a.input + (p / a.S) * a.K;
-    const float* wg = (const float*)a.weights + g * a.K * a.N;
-    float acc = 0.0f;
+    if (g < 0 || g >= a.G) return;  // the whole workgroup has the same pair
+    const F* in = (const F*)a.input + (p / a.S) * a.K;
+    const F* wg = (const F*)a.weights + g * a.K * a.N;
+    F acc = 0;
     for (int64_t k0 = 0; k0 < a.K; k0 += 1024) {
         __syncthreads();
-        for (int k = threadIdx.x; k < 1024; k += 256) row[k] = (k0 + k < a.K) ? in[k0 + k] : 0.0f;
+        for (int k = threadIdx.x; k < 1024; k += 256) row[k] = (k0 + k < a.K) ? in[k0 + k] : (F)0;
         __syncthreads();
         if (n < a.N) {
             const int64_t kend = min((int64_t)1024, a.K - k0);
@@ -918,8 +920,8 @@ __global__ __launch_bounds__(256) void grouped_f32_kernel(GroupedArgs a) {
         }
     }
     if (n < a.N) {
-        if (a.bias) acc += ((const float*)a.bias)[g * a.N + n];
-        ((float*)a.output)[p * a.N + n] = acc;
+        if (a.bias) acc += ((const F*)a.bias)[g * a.N + n];
+        ((F*)a.output)[p * a.N + n] = acc;
     }
 }
 
@@ -1004,10 +1006,11 @@ hipError_t launch_grouped(const GroupedArgs& a, int dt, void* ws, hipStream_t s)
     hipError_t e = launch_routing(a, ws, s);
     if (e != hipSuccess) return e;
     if (P == 0 || a.N == 0) return hipSuccess;
-    if (dt == 2) {
+    if (dt >= 2) {
         const int64_t nb = (a.N + 255) / 256;
         if (nb > 65535) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(grouped_f32_kernel, dim3((unsigned)P, (unsigned)nb), dim3(256), 0, s, a);
+        if (dt == 2) hipLaunchKernelGGL(grouped_fp_kernel<float>, dim3((unsigned)P, (unsigned)nb), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL(grouped_fp_kernel<double>, dim3((unsigned)P, (unsigned)nb), dim3(256), 0, s, a);
         return hipGetLastError();
     }
     const int64_t max_mtiles = P / GBM + a.G;

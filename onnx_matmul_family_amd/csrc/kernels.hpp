@@ -72,8 +72,9 @@ struct GroupedArgs {
 // dt: 0 = bf16, 1 = fp16
 hipError_t launch_dense16(const DenseArgs& a, int dt, hipStream_t s);
 hipError_t launch_dense_f32(const DenseArgs& a, hipStream_t s);
+hipError_t launch_dense_f64(const DenseArgs& a, hipStream_t s);
 hipError_t launch_qlinear(const QArgs& a, hipStream_t s);
-// dt: 0 = bf16, 1 = fp16, 2 = fp32
+// dt: 0 = bf16, 1 = fp16, 2 = fp32, 3 = fp64
 size_t grouped_workspace_bytes(int64_t M, int64_t S, int64_t G);
 hipError_t launch_grouped(const GroupedArgs& a, int dt, void* ws, hipStream_t s);
 hipError_t launch_grouped_dq(const GroupedArgs& a, int dt, void* ws, hipStream_t s);

@@ -13,8 +13,11 @@ import torch
 
 from onnx_matmul_family_amd import synth
 
-TOL = {"f32": (1e-5, 1e-6), "bf16": (1e-2, 1e-3), "f16": (1e-2, 1e-3)}
-TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+# fp64 (no stated bound): the GPU sums the same products in another order, each
+# fp64 operation off by at most 2^-53 relative, so |err| <= K * 2^-53 * t, under
+# 1e-12 * t for every K tested (K <= 4096)
+TOL = {"f32": (1e-5, 1e-6), "bf16": (1e-2, 1e-3), "f16": (1e-2, 1e-3), "f64": (1e-12, 1e-300)}
+TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "f64": torch.float64}
 
 
 def dev(arr, dt=None):
@@ -26,7 +29,7 @@ def dev(arr, dt=None):
 
 
 def host_f64(t):
-    """GPU tensor -> float64 numpy (exact for bf16 / fp16 / fp32)."""
+    """GPU tensor -> float64 numpy (exact for bf16 / fp16 / fp32 / fp64)."""
     t = t.detach()
     if t.dtype == torch.bfloat16:
         bits = t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)

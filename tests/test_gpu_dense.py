@@ -1,4 +1,4 @@
-"""GPU parity of MatMul and Gemm (bf16 / fp16 / fp32) against the CPU oracle,
+"""GPU parity of MatMul and Gemm (bf16 / fp16 / fp32 / fp64) against the CPU oracle,
 through the C ABI.  Shapes span several tiles with ragged tails in every dim,
 all four transpose combinations, every C broadcast form, 1-D promotion and
 batch broadcasting, plus bit-exact small-integer cases."""
@@ -30,7 +30,7 @@ def draw(rng, shape, dt, kind="normal"):
 GEMM_SHAPES = [(1, 1, 1), (7, 5, 3), (64, 32, 48), (300, 520, 200), (257, 129, 199), (130, 264, 136), (33, 17, 0)]
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32", "f64"])
 @pytest.mark.parametrize("tA,tB", [(0, 0), (0, 1), (1, 0), (1, 1)])
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
 def test_gemm_shapes(dt, tA, tB, M, N, K):
@@ -47,7 +47,7 @@ def test_gemm_shapes(dt, tA, tB, M, N, K):
                 "gemm %s %dx%dx%d tA=%d tB=%d" % (dt, M, N, K, tA, tB))
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("dt", ["bf16", "f32", "f64"])
 @pytest.mark.parametrize("cshape", [None, (), (1,), (90,), (1, 90), (70, 1), (70, 90), (1, 1)])
 def test_gemm_c_forms(dt, cshape):
     rng = np.random.default_rng(101)
@@ -61,7 +61,7 @@ def test_gemm_c_forms(dt, cshape):
     check_close(host_f64(Y), y, 1.5 * t + cm, dt, "gemm C %s" % (cshape,))
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f64"])
 @pytest.mark.parametrize("tA,tB", [(0, 0), (0, 1), (1, 0), (1, 1)])
 def test_gemm_small_integers_exact(dt, tA, tB):
     """Entries in {-2..2} with K = 64: every partial sum is an integer of
@@ -102,7 +102,7 @@ MATMUL_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32", "f64"])
 @pytest.mark.parametrize("sa,sb", MATMUL_SHAPES)
 def test_matmul_broadcast(dt, sa, sb):
     rng = np.random.default_rng(abs(hash((sa, sb))) % 2**31)

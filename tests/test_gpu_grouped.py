@@ -1,6 +1,6 @@
 """GPU parity of GroupedMatMul against the CPU oracle (and the page's examples).
 
-Covers bf16 / fp16 / fp32, int32 and int64 indices, bias present and absent,
+Covers bf16 / fp16 / fp32 / fp64, int32 and int64 indices, bias present and absent,
 ragged M/N/K and group sizes (several tiles per group, unused and empty
 groups), zero tokens / zero selections, and invalid indices (counted, their
 rows untouched, everything else still correct)."""
@@ -34,24 +34,23 @@ def test_page_examples(golden):
     from tests.test_oracle_examples import _grouped_inputs
     for ex in golden("groupedmatmul"):
         for T in ex.get("T_values", [None]):
-            if T == "float64":
-                continue  # fp64 is not implemented on the GPU path
             for Tind in ex.get("Tind_values", [None]):
                 inp, w, idx, bias = _grouped_inputs(ex, T, Tind)
-                dt = {"float16": "f16", None: "f32", "float32": "f32"}[T]
+                dt = {"float16": "f16", None: "f32", "float32": "f32", "float64": "f64"}[T]
                 out, bad = run(inp, w, idx, bias, dt)
                 y, t = oracle.grouped_matmul(inp, w, idx, bias)
                 assert bad == 0 and tuple(out.shape) == y.shape, ex["cite"]
                 check_close(host_f64(out), y, t, dt, ex["cite"])
 
 
-def test_fp64_is_reported_unsupported():
-    x = torch.zeros((2, 2), dtype=torch.float64, device="cuda")
-    w = torch.zeros((1, 2, 2), dtype=torch.float64, device="cuda")
-    i = torch.zeros((2, 1), dtype=torch.int64, device="cuda")
-    with pytest.raises(om.OmmError) as e:
-        om.grouped_matmul(x, w, i)
-    assert e.value.code == -5
+def test_fp64_page_values_exact():
+    """fp64 GroupedMatMul: integer-valued inputs give exact results."""
+    x = torch.tensor([[1.0, 2.0], [3.0, -4.0]], dtype=torch.float64, device="cuda")
+    w = torch.tensor([[[1.0, 0.0], [0.0, 1.0]], [[0.0, 1.0], [1.0, 0.0]]], dtype=torch.float64, device="cuda")
+    i = torch.tensor([[1, 0], [0, 1]], dtype=torch.int64, device="cuda")
+    out, ws = om.grouped_matmul(x, w, i)
+    assert om.grouped_matmul_check(ws) == 0
+    assert out.cpu().tolist() == [[[2.0, 1.0], [1.0, 2.0]], [[3.0, -4.0], [-4.0, 3.0]]]
 
 
 CASES = [  # M, K, N, G, S
@@ -59,7 +58,7 @@ CASES = [  # M, K, N, G, S
 ]
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32", "f64"])
 @pytest.mark.parametrize("M,K,N,G,S", CASES)
 @pytest.mark.parametrize("with_bias", [True, False])
 def test_random(dt, M, K, N, G, S, with_bias):
