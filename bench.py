@@ -14,7 +14,8 @@ reported against the MI355X dense MFMA peak of its type under `per_config`;
 `cold_ms` there is the median of calls issued right after a 512 MiB write that
 evicts the last-level cache (operands start in HBM only).  `next_rows` times
 workloads outside the step the same way (GroupedMatMul over int8 weights with
-the dequantisation fused, an fp64 Gemm); they are not part of `value`.
+the dequantisation fused, an fp64 Gemm, decode-like skinny Gemms against the
+HBM peak); they are not part of `value`.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--only NAME]
        python bench.py --copy-calibration      (1 GiB device-to-device copies, for
@@ -162,6 +163,26 @@ def next_rows(torch, om, synth, dev, reps):
     rows.append(dict(workload="gemm_f64_4096", desc="Gemm fp64 4096^3, transB=1, C[4096], alpha=beta=1, N(0,1), seed 6",
                      dtype="f64", ms=round(med, 4), tflops=round(rate, 2), frac_peak=round(rate / PEAK["f64"], 4),
                      hbm_gbs=round((3 * n * n + n) * 8 / (med * 1e-3) / 1e9, 1)))
+    del A64, B64, C64, Y64
+    # decode-like skinny Gemm (split-K path): HBM-bound, reported against the HBM peak
+    for M in (1, 16):
+        N = K = 8192
+        A = torch.from_numpy(synth.store(synth.normal(rng, (M, K)), "bf16").view(np.int16)).cuda().view(torch.bfloat16)
+        B = torch.from_numpy(synth.store(synth.normal(rng, (N, K), 0.02), "bf16").view(np.int16)).cuda().view(
+            torch.bfloat16)
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        fn = lambda: om.gemm(A, B, None, 1.0, 0.0, 0, 1, Y)
+        fn()
+        torch.cuda.synchronize()
+        med, _ = time_each(torch, fn, reps)
+        byts = 2 * (M * K + N * K + M * N)
+        gbs = byts / (med * 1e-3) / 1e9
+        log("%-20s %9.4f ms  %8.1f GB/s  %5.1f%% of HBM peak (not in the step)" % ("gemm_bf16_skinny_m%d" % M, med,
+                                                                                    gbs, 100 * gbs / HBM_GBS))
+        rows.append(dict(workload="gemm_bf16_skinny_m%d" % M,
+                         desc="Gemm bf16 M=%d N=K=8192, transB=1, no C (split-K path), seed 6" % M, dtype="bf16",
+                         ms=round(med, 4), tflops=round(2 * M * N * K / (med * 1e-3) / 1e12, 2),
+                         hbm_gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_GBS, 4)))
     return rows
 
 

@@ -101,6 +101,34 @@ def test_random(ta, tb, ty, M, N, K, mode):
     assert np.array_equal(got, ref), (np.argwhere(got != ref)[:5], M, N, K)
 
 
+@pytest.mark.parametrize("ta,tb,ty", [(np.uint8, np.uint8, np.uint8), (np.uint8, np.int8, np.int8),
+                                      (np.int8, np.uint8, np.uint8)])
+def test_mixed_types_at_scale(ta, tb, ty):
+    """uint8 / mixed operands on the full-tile fast path at a larger size
+    (K a multiple of 256 for uint8 a), every output compared."""
+    rng = np.random.default_rng(90 + (ta == np.uint8) + 2 * (tb == np.uint8))
+    M, K, N = 1024, 2048, 1536
+    a, b = rint(rng, (M, K), ta), rint(rng, (K, N), tb)
+    zl = lambda d: (100, 150) if d == np.uint8 else (-16, 16)
+    az, bz = rint(rng, (M, 1), ta, *zl(ta)), rint(rng, (1, N), tb, *zl(tb))
+    asc, bsc = synth.uniform(rng, (M, 1), 0.002, 0.01), synth.uniform(rng, (1, N), 0.002, 0.01)
+    yz = np.array(128 if ty == np.uint8 else 0, ty)
+    got, ref = run(a, asc, az, b, bsc, bz, 0.05, yz)
+    assert got.dtype == ty
+    assert np.array_equal(got, ref), np.argwhere(got != ref)[:5]
+
+
+def test_batched_params_larger():
+    """3-D batch with per-row / per-column parameters per batch entry, full 256x256 tiles."""
+    rng = np.random.default_rng(79)
+    D, M, K, N = 4, 512, 512, 512
+    a, b = rint(rng, (D, M, K), np.int8), rint(rng, (D, K, N), np.uint8)
+    az, bz = rint(rng, (D, M, 1), np.int8, -16, 16), rint(rng, (D, 1, N), np.uint8, 100, 150)
+    asc, bsc = synth.uniform(rng, (D, M, 1), 0.002, 0.01), synth.uniform(rng, (D, 1, N), 0.002, 0.01)
+    got, ref = run(a, asc, az, b, bsc, bz, 0.04, np.array(-5, np.int8))
+    assert np.array_equal(got, ref)
+
+
 def test_batched_params():
     rng = np.random.default_rng(77)
     D, M, K, N = 3, 130, 96, 70
