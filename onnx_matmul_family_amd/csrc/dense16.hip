@@ -250,6 +250,184 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(DenseArgs p) {
     ((uint16_t*)p.Y)[z0 * p.y_bs0 + z1 * p.y_bs1 + m * p.ldy + n] = to_bits<DT>(v);
 }
 
+// ---------------------------------------------------------------------------
+// Skinny products (M <= 16 rows, A and B both k-contiguous: a decode-like
+// activation block against weights stored (N, K)).  The work is one read of
+// B, so the kernel is built to stream B from HBM: each wave owns 16 columns
+// and loads its B operand straight from global memory in the
+// v_mfma_f32_16x16x32 operand layout (lane l: column l%16, 8 consecutive k at
+// 8 (l/16)), 8 k-steps of 32 in flight ahead of the MFMAs; A (16 rows, zero
+// past M) sits in LDS for the workgroup's K range and is shared by its 4
+// waves.  K is split over gridDim.y ranges so that every CU streams; the fp32
+// partial products go to the split-K workspace and splitk_reduce_kernel adds
+// them in a fixed order and applies the epilogue.
+constexpr int SK_COLS = 64;      // columns per workgroup (4 waves x 16)
+constexpr int SK_U = 16;         // k-steps of 32 per batch of loads
+constexpr int SK_KMAX = 2048;    // k per workgroup (A rows in LDS: 16 x 2048 x 2 bytes)
+constexpr int SK_ROWB = SK_KMAX * 2 + 64;  // LDS row pitch of A (bytes)
+
+template <int DT>
+__device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
+    if constexpr (DT == 0)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                      c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b),
+                                                     c, 0, 0, 0);
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void skinny_kernel(DenseArgs p) {
+    __shared__ __attribute__((aligned(16))) char As[16 * SK_ROWB];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int64_t z = blockIdx.z, z0 = z / p.nb1, z1 = z - z0 * p.nb1;
+    const int split = blockIdx.y;
+    const int64_t M = p.M, N = p.N, K = p.K, NB = p.nb0 * p.nb1;
+    const int64_t k0 = (int64_t)split * p.kchunk;
+    const int64_t kn = min(p.kchunk, K - k0);  // > 0: the launcher sizes the splits
+    const uint16_t* __restrict__ A = (const uint16_t*)p.A + z0 * p.a_bs0 + z1 * p.a_bs1 + k0;
+    const uint16_t* __restrict__ B = (const uint16_t*)p.B + z0 * p.b_bs0 + z1 * p.b_bs1 + k0;
+    const int64_t n = (int64_t)blockIdx.x * SK_COLS + 16 * wave + (lane & 15);
+    const int kl = 8 * (lane >> 4);  // this lane's k offset inside a k-step
+    const bool nok = n < N;
+    const uint16_t* __restrict__ Bn = B + n * p.ldb + kl;
+    const int nsteps = (int)((kn + 31) / 32);
+
+    // B of one batch of k-steps (zeros past K or N); 16-byte loads, K % 8 == 0
+    auto load_b = [&](u32x4_t (&r)[SK_U], int j0) {
+#pragma unroll
+        for (int u = 0; u < SK_U; ++u) {
+            const int64_t k = 32 * (int64_t)(j0 + u) + kl;
+            u32x4_t v = {0u, 0u, 0u, 0u};
+            if (nok && k < kn) v = *(const u32x4_t*)(Bn + 32 * (j0 + u));
+            r[u] = v;
+        }
+    };
+    u32x4_t bcur[SK_U], bnxt[SK_U];
+    load_b(bcur, 0);
+
+    // A rows 0..15 of this K range into LDS (rows past M and k past kn: zeros)
+    const int kc = (int)((kn + 7) / 8);  // 16-byte chunks per row
+    for (int c = t; c < 16 * kc; c += 256) {
+        const int m = c / kc, q = c - m * kc;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (m < M) v = *(const u32x4_t*)(A + m * p.lda + 8 * q);
+        *(u32x4_t*)(As + m * SK_ROWB + 16 * q) = v;
+    }
+    __syncthreads();
+
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    const char* Arow = As + (lane & 15) * SK_ROWB + 2 * kl;
+    // batch j0 of MFMAs on buffer r (A fragment: row l%16, k = 32 j + 8 (l/16)
+    // .. +7; k past kn reads zeros: LDS there was never written, B is zero too)
+    auto mma = [&](const u32x4_t (&r)[SK_U], int j0) {
+#pragma unroll
+        for (int u = 0; u < SK_U; ++u) {
+            const int j = j0 + u;
+            u32x4_t av = {0u, 0u, 0u, 0u};
+            if (32 * j + kl < kn) av = *(const u32x4_t*)(Arow + 64 * j);
+            acc = mfma16x16x32<DT>(av, r[u], acc);
+        }
+    };
+    // two buffers in turn (no register copies, which would wait for the loads):
+    // one batch of loads in flight while the other batch multiplies
+    for (int j0 = 0; j0 < nsteps; j0 += 2 * SK_U) {
+        if (j0 + SK_U < nsteps) load_b(bnxt, j0 + SK_U);
+        mma(bcur, j0);
+        if (j0 + SK_U >= nsteps) break;
+        if (j0 + 2 * SK_U < nsteps) load_b(bcur, j0 + 2 * SK_U);
+        mma(bnxt, j0 + SK_U);
+    }
+
+    // result register r of lane l: row 4 (l/16) + r, column l%16
+    if (!nok) return;
+    float* __restrict__ ws = p.ws + ((int64_t)split * NB + z) * M * N;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int64_t m = 4 * (lane >> 4) + r;
+        if (m < M) ws[m * N + n] = acc[r];
+    }
+}
+
+// Single-pass variant for enough columns (N/16 workgroups fill the chip): a
+// workgroup owns 16 columns and its 4 waves split K in 4 contiguous ranges;
+// A fragments come straight from global memory too (the A rows, at most 16,
+// are small and stay in L2); the 4 partial 16x16 tiles are added in LDS in a
+// fixed order and wave 0 applies alpha * acc + beta * C and stores Y.  No
+// workspace and no second kernel.
+constexpr int SK1_U = 8;  // k-steps per batch of loads
+
+template <int DT>
+__global__ __launch_bounds__(256) void skinny1_kernel(DenseArgs p) {
+    __shared__ float red[3][64][4];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int64_t z = blockIdx.y, z0 = z / p.nb1, z1 = z - z0 * p.nb1;
+    const int64_t M = p.M, N = p.N, K = p.K;
+    // this wave's K range: steps of 32, split as evenly as whole steps allow
+    const int64_t steps = (K + 31) / 32;
+    const int64_t s0 = steps * wave / 4, s1 = steps * (wave + 1) / 4;
+    const int nst = (int)(s1 - s0);
+    const int64_t kbase = 32 * s0;
+    const int64_t n = (int64_t)blockIdx.x * 16 + (lane & 15);
+    const int64_t m = lane & 15;
+    const int kl = 8 * (lane >> 4);
+    const bool nok = n < N, mok = m < M;
+    const uint16_t* __restrict__ Bn = (const uint16_t*)p.B + z0 * p.b_bs0 + z1 * p.b_bs1 + n * p.ldb + kbase + kl;
+    const uint16_t* __restrict__ Am = (const uint16_t*)p.A + z0 * p.a_bs0 + z1 * p.a_bs1 + m * p.lda + kbase + kl;
+    const int64_t kn = K - kbase;  // k past this are beyond K (K % 8 == 0)
+
+    auto load = [&](u32x4_t (&rb)[SK1_U], u32x4_t (&ra)[SK1_U], int j0) {
+#pragma unroll
+        for (int u = 0; u < SK1_U; ++u) {
+            const int j = j0 + u;
+            const bool kok = j < nst && 32 * (int64_t)j + kl < kn;
+            u32x4_t vb = {0u, 0u, 0u, 0u}, va = {0u, 0u, 0u, 0u};
+            if (nok && kok) vb = *(const u32x4_t*)(Bn + 32 * j);
+            if (mok && kok) va = *(const u32x4_t*)(Am + 32 * j);
+            rb[u] = vb;
+            ra[u] = va;
+        }
+    };
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto mma = [&](const u32x4_t (&rb)[SK1_U], const u32x4_t (&ra)[SK1_U]) {
+#pragma unroll
+        for (int u = 0; u < SK1_U; ++u) acc = mfma16x16x32<DT>(ra[u], rb[u], acc);
+    };
+    u32x4_t b0[SK1_U], a0[SK1_U], b1[SK1_U], a1[SK1_U];
+    load(b0, a0, 0);
+    for (int j0 = 0; j0 < nst; j0 += 2 * SK1_U) {
+        if (j0 + SK1_U < nst) load(b1, a1, j0 + SK1_U);
+        mma(b0, a0);
+        if (j0 + SK1_U >= nst) break;
+        if (j0 + 2 * SK1_U < nst) load(b0, a0, j0 + 2 * SK1_U);
+        mma(b1, a1);
+    }
+    // waves 1..3 hand their tiles to wave 0, which adds them in wave order
+    if (wave > 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave - 1][lane][r] = acc[r];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 0; w < 3; ++w)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] += red[w][lane][r];
+    // result register r of lane l: row 4 (l/16) + r, column l%16
+    if (!nok) return;
+    uint16_t* __restrict__ Y = (uint16_t*)p.Y + z0 * p.y_bs0 + z1 * p.y_bs1;
+    const uint16_t* Cp = (const uint16_t*)p.C;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int64_t mm = 4 * (lane >> 4) + r;
+        if (mm < M) {
+            float v = p.alpha * acc[r];
+            if (Cp) v += p.beta * from_bits<DT>(Cp[mm * p.c_sm + n * p.c_sn]);
+            Y[mm * p.ldy + n] = to_bits<DT>(v);
+        }
+    }
+}
+
 template <int BM, int BN, int DT, bool AK, bool BKM, int MODE>
 hipError_t launch_cfg(const DenseArgs& a, hipStream_t s) {
     const int64_t tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
@@ -292,9 +470,39 @@ hipError_t launch_dt(const DenseArgs& a, hipStream_t s) {
         if (full && a.c_sm == 0 && a.c_sn == 1 && ((uintptr_t)a.C & 7) == 0) return launch_layout<256, 256, DT, 3>(a, s);
         return launch_layout<256, 256, DT, 1>(a, s);
     }
+    const int64_t NB = a.nb0 * a.nb1;
+    // Skinny (M <= 16) with both operands k-contiguous: stream B, split K.
+    if (vec && a.M <= 16 && a.a_kmajor && a.b_kmajor && a.K >= 1024 && NB <= 65535 &&
+        (a.N + 15) / 16 * NB >= 512 && (a.N + 15) / 16 <= 0x7fffffff) {
+        hipLaunchKernelGGL(skinny1_kernel<DT>, dim3((unsigned)((a.N + 15) / 16), (unsigned)NB), dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
+    if (vec && a.M <= 16 && a.a_kmajor && a.b_kmajor && a.K >= 1024 && NB <= 65535) {
+        const int64_t groups = (a.N + SK_COLS - 1) / SK_COLS;
+        int64_t S = std::max<int64_t>((512 + groups * NB - 1) / (groups * NB), (a.K + SK_KMAX - 1) / SK_KMAX);
+        S = std::min<int64_t>(S, (a.K + 255) / 256);
+        const int64_t kchunk = std::min<int64_t>(((a.K + S - 1) / S + 255) / 256 * 256, SK_KMAX);
+        S = (a.K + kchunk - 1) / kchunk;
+        if (groups <= 0x7fffffff && S <= 65535) {
+            const int64_t elems = NB * a.M * a.N;
+            DenseArgs b = a;
+            b.kchunk = kchunk;
+            b.splits = (int)S;
+            hipError_t e = hipMallocAsync((void**)&b.ws, (size_t)(S * elems) * sizeof(float), s);
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(skinny_kernel<DT>, dim3((unsigned)groups, (unsigned)S, (unsigned)NB), dim3(256), 0, s, b);
+            e = hipGetLastError();
+            if (e == hipSuccess) {
+                hipLaunchKernelGGL(splitk_reduce_kernel<DT>, dim3((unsigned)((elems + 255) / 256)), dim3(256), 0, s,
+                                   b);
+                e = hipGetLastError();
+            }
+            const hipError_t f = hipFreeAsync(b.ws, s);
+            return e != hipSuccess ? e : f;
+        }
+    }
     // Few output tiles and a long K: split K over several workgroups per tile
     // so that the whole chip streams the operands, then reduce.
-    const int64_t NB = a.nb0 * a.nb1;
     const int64_t t128 = ((a.M + 127) / 128) * ((a.N + 127) / 128) * NB;
     if (vec && t128 < 128 && a.K >= 2048) {
         int64_t S = std::min<int64_t>(std::min<int64_t>(512 / t128, a.K / 512), 32);

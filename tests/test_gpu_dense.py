@@ -227,6 +227,43 @@ def test_gemm_split_k(dt, sa, sb, tA, tB):
     check_close(host_f64(Y).ravel()[sel], y, 0.5 * t + 1.5 * np.abs(Cb), dt, "split-K %s %s x %s" % (dt, sa, sb))
 
 
+SKINNY = [  # M, N, K: M <= 16 rows against B stored (N, K) -> the B-streaming skinny kernels
+    (1, 8192, 8192), (5, 8200, 3000), (16, 8192, 1024),                        # single pass (>= 512 x 16 columns)
+    (16, 4096, 4104), (3, 100, 1000), (7, 4100, 2056), (16, 64, 1024), (1, 1, 20000),  # K split over workgroups
+]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("M,N,K", SKINNY)
+def test_gemm_skinny_stream(dt, M, N, K):
+    """Decode-like Gemm, transB=1: B streamed in the MFMA operand layout, K split
+    over workgroups (ragged last range, N tails, a single column), reduced with
+    the alpha / beta / C epilogue."""
+    rng = np.random.default_rng(M * 131 + N + K)
+    A = synth.store(synth.normal(rng, (M, K)), dt)
+    B = synth.store(synth.normal(rng, (N, K), 0.02), dt)
+    C = synth.store(synth.uniform(rng, (M, N), -0.1, 0.1), dt)
+    Y = om.gemm(dev(A, dt), dev(B, dt), dev(C, dt), 0.75, 1.25, 0, 1)
+    torch.cuda.synchronize()
+    sel = sample_indices(M * N, 20000, 9)
+    y, t = oracle.gemm(A, B, C, 0.75, 1.25, 0, 1, dt=dt, sel=sel)
+    cabs = np.abs(oracle.decode(C, dt)).ravel()[sel]
+    check_close(host_f64(Y).ravel()[sel], y, 0.75 * t + 1.25 * cabs, dt, "skinny %s M=%d N=%d K=%d" % (dt, M, N, K))
+
+
+@pytest.mark.parametrize("M", [1, 5, 16])
+def test_gemm_skinny_exact(M):
+    """Small integers (entries in {-1, 0, 1}, |partial sums| <= 256): bit-exact."""
+    rng = np.random.default_rng(M)
+    K, N = 2048, 320
+    A = synth.store(rng.integers(-1, 2, (M, K)).astype(np.float32) * (np.arange(K) % 8 == 0), "bf16")
+    B = synth.store(rng.integers(-1, 2, (N, K)).astype(np.float32), "bf16")
+    Y = om.gemm(dev(A, "bf16"), dev(B, "bf16"), None, 1.0, 0.0, 0, 1)
+    torch.cuda.synchronize()
+    y, _ = oracle.gemm(A, B, None, 1.0, 0.0, 0, 1, dt="bf16")
+    assert np.array_equal(host_f64(Y), y)
+
+
 def test_matmul_split_k_decode_batch_exact():
     """A batch of single-token rows against one weight matrix (batch folds into
     M = 8): split-K, small integers, fp16 output exact."""
