@@ -165,22 +165,23 @@ def next_rows(torch, om, synth, dev, reps):
                      hbm_gbs=round((3 * n * n + n) * 8 / (med * 1e-3) / 1e9, 1)))
     del A64, B64, C64, Y64
     # decode-like skinny Gemm (split-K path): HBM-bound, reported against the HBM peak
-    for M in (1, 16):
+    for M, tB in ((1, 1), (16, 1), (1, 0)):
         N = K = 8192
         A = torch.from_numpy(synth.store(synth.normal(rng, (M, K)), "bf16").view(np.int16)).cuda().view(torch.bfloat16)
         B = torch.from_numpy(synth.store(synth.normal(rng, (N, K), 0.02), "bf16").view(np.int16)).cuda().view(
             torch.bfloat16)
         Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-        fn = lambda: om.gemm(A, B, None, 1.0, 0.0, 0, 1, Y)
+        fn = lambda: om.gemm(A, B, None, 1.0, 0.0, 0, tB, Y)
         fn()
         torch.cuda.synchronize()
         med, _ = time_each(torch, fn, reps)
         byts = 2 * (M * K + N * K + M * N)
         gbs = byts / (med * 1e-3) / 1e9
-        log("%-20s %9.4f ms  %8.1f GB/s  %5.1f%% of HBM peak (not in the step)" % ("gemm_bf16_skinny_m%d" % M, med,
-                                                                                    gbs, 100 * gbs / HBM_GBS))
-        rows.append(dict(workload="gemm_bf16_skinny_m%d" % M,
-                         desc="Gemm bf16 M=%d N=K=8192, transB=1, no C (split-K path), seed 6" % M, dtype="bf16",
+        name = "gemm_bf16_skinny_m%d_%s" % (M, "nk" if tB else "kn")
+        log("%-20s %9.4f ms  %8.1f GB/s  %5.1f%% of HBM peak (not in the step)" % (name, med, gbs, 100 * gbs / HBM_GBS))
+        rows.append(dict(workload=name,
+                         desc="Gemm bf16 M=%d N=K=8192, B stored %s (transB=%d), no C, seed 6"
+                         % (M, "(N, K)" if tB else "(K, N)", tB), dtype="bf16",
                          ms=round(med, 4), tflops=round(2 * M * N * K / (med * 1e-3) / 1e12, 2),
                          hbm_gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_GBS, 4)))
     return rows

@@ -266,6 +266,18 @@ constexpr int SK_U = 16;         // k-steps of 32 per batch of loads
 constexpr int SK_KMAX = 2048;    // k per workgroup (A rows in LDS: 16 x 2048 x 2 bytes)
 constexpr int SK_ROWB = SK_KMAX * 2 + 64;  // LDS row pitch of A (bytes)
 
+// Branch-free 16-byte loads for the streaming kernels: through a buffer
+// resource, an offset at or past 2^31 reads zeros, so masked lanes need no
+// branch (a branch around a load makes the compiler wait for every load in
+// flight before the next use) and the loads of a batch stay in flight together.
+constexpr uint32_t SK_OOB = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sk_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t sk_load(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+}
+
 template <int DT>
 __device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
     if constexpr (DT == 0)
@@ -290,7 +302,8 @@ __global__ __launch_bounds__(256) void skinny_kernel(DenseArgs p) {
     const int64_t n = (int64_t)blockIdx.x * SK_COLS + 16 * wave + (lane & 15);
     const int kl = 8 * (lane >> 4);  // this lane's k offset inside a k-step
     const bool nok = n < N;
-    const uint16_t* __restrict__ Bn = B + n * p.ldb + kl;
+    const __amdgpu_buffer_rsrc_t rb = sk_rsrc(B);
+    const uint32_t boff = (uint32_t)((n * p.ldb + kl) * 2);
     const int nsteps = (int)((kn + 31) / 32);
 
     // B of one batch of k-steps (zeros past K or N); 16-byte loads, K % 8 == 0
@@ -298,21 +311,30 @@ __global__ __launch_bounds__(256) void skinny_kernel(DenseArgs p) {
 #pragma unroll
         for (int u = 0; u < SK_U; ++u) {
             const int64_t k = 32 * (int64_t)(j0 + u) + kl;
-            u32x4_t v = {0u, 0u, 0u, 0u};
-            if (nok && k < kn) v = *(const u32x4_t*)(Bn + 32 * (j0 + u));
-            r[u] = v;
+            r[u] = sk_load(rb, nok && k < kn ? boff + 64u * (uint32_t)(j0 + u) : SK_OOB);
         }
     };
     u32x4_t bcur[SK_U], bnxt[SK_U];
     load_b(bcur, 0);
 
-    // A rows 0..15 of this K range into LDS (rows past M and k past kn: zeros)
-    const int kc = (int)((kn + 7) / 8);  // 16-byte chunks per row
-    for (int c = t; c < 16 * kc; c += 256) {
-        const int m = c / kc, q = c - m * kc;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (m < M) v = *(const u32x4_t*)(A + m * p.lda + 8 * q);
-        *(u32x4_t*)(As + m * SK_ROWB + 16 * q) = v;
+    // A rows 0..15 of this K range into LDS (rows past M: zeros), 4 loads in
+    // flight per thread
+    {
+        const int kc = (int)((kn + 7) / 8);  // 16-byte chunks per row
+        const __amdgpu_buffer_rsrc_t rsa = sk_rsrc(A);
+        for (int c0 = 0; c0 < 16 * kc; c0 += 1024) {
+            u32x4_t v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c = c0 + t + 256 * u, m = c / kc, q = c - m * kc;
+                v[u] = sk_load(rsa, c < 16 * kc && m < M ? (uint32_t)((m * p.lda + 8 * q) * 2) : SK_OOB);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c = c0 + t + 256 * u, m = c / kc, q = c - m * kc;
+                if (c < 16 * kc) *(u32x4_t*)(As + m * SK_ROWB + 16 * q) = v[u];
+            }
+        }
     }
     __syncthreads();
 
@@ -332,10 +354,9 @@ __global__ __launch_bounds__(256) void skinny_kernel(DenseArgs p) {
     // two buffers in turn (no register copies, which would wait for the loads):
     // one batch of loads in flight while the other batch multiplies
     for (int j0 = 0; j0 < nsteps; j0 += 2 * SK_U) {
-        if (j0 + SK_U < nsteps) load_b(bnxt, j0 + SK_U);
+        load_b(bnxt, j0 + SK_U);
         mma(bcur, j0);
-        if (j0 + SK_U >= nsteps) break;
-        if (j0 + 2 * SK_U < nsteps) load_b(bcur, j0 + 2 * SK_U);
+        load_b(bcur, j0 + 2 * SK_U);
         mma(bnxt, j0 + SK_U);
     }
 
@@ -372,8 +393,9 @@ __global__ __launch_bounds__(256) void skinny1_kernel(DenseArgs p) {
     const int64_t m = lane & 15;
     const int kl = 8 * (lane >> 4);
     const bool nok = n < N, mok = m < M;
-    const uint16_t* __restrict__ Bn = (const uint16_t*)p.B + z0 * p.b_bs0 + z1 * p.b_bs1 + n * p.ldb + kbase + kl;
-    const uint16_t* __restrict__ Am = (const uint16_t*)p.A + z0 * p.a_bs0 + z1 * p.a_bs1 + m * p.lda + kbase + kl;
+    const __amdgpu_buffer_rsrc_t rsb = sk_rsrc((const uint16_t*)p.B + z0 * p.b_bs0 + z1 * p.b_bs1);
+    const __amdgpu_buffer_rsrc_t rsa = sk_rsrc((const uint16_t*)p.A + z0 * p.a_bs0 + z1 * p.a_bs1);
+    const uint32_t boff = (uint32_t)((n * p.ldb + kbase + kl) * 2), aoff = (uint32_t)((m * p.lda + kbase + kl) * 2);
     const int64_t kn = K - kbase;  // k past this are beyond K (K % 8 == 0)
 
     auto load = [&](u32x4_t (&rb)[SK1_U], u32x4_t (&ra)[SK1_U], int j0) {
@@ -381,11 +403,8 @@ __global__ __launch_bounds__(256) void skinny1_kernel(DenseArgs p) {
         for (int u = 0; u < SK1_U; ++u) {
             const int j = j0 + u;
             const bool kok = j < nst && 32 * (int64_t)j + kl < kn;
-            u32x4_t vb = {0u, 0u, 0u, 0u}, va = {0u, 0u, 0u, 0u};
-            if (nok && kok) vb = *(const u32x4_t*)(Bn + 32 * j);
-            if (mok && kok) va = *(const u32x4_t*)(Am + 32 * j);
-            rb[u] = vb;
-            ra[u] = va;
+            rb[u] = sk_load(rsb, nok && kok ? boff + 64u * (uint32_t)j : SK_OOB);
+            ra[u] = sk_load(rsa, mok && kok ? aoff + 64u * (uint32_t)j : SK_OOB);
         }
     };
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -395,11 +414,11 @@ __global__ __launch_bounds__(256) void skinny1_kernel(DenseArgs p) {
     };
     u32x4_t b0[SK1_U], a0[SK1_U], b1[SK1_U], a1[SK1_U];
     load(b0, a0, 0);
+    // straight-line ping-pong (steps past the range load zeros)
     for (int j0 = 0; j0 < nst; j0 += 2 * SK1_U) {
-        if (j0 + SK1_U < nst) load(b1, a1, j0 + SK1_U);
+        load(b1, a1, j0 + SK1_U);
         mma(b0, a0);
-        if (j0 + SK1_U >= nst) break;
-        if (j0 + 2 * SK1_U < nst) load(b0, a0, j0 + 2 * SK1_U);
+        load(b0, a0, j0 + 2 * SK1_U);
         mma(b1, a1);
     }
     // waves 1..3 hand their tiles to wave 0, which adds them in wave order
@@ -426,6 +445,164 @@ __global__ __launch_bounds__(256) void skinny1_kernel(DenseArgs p) {
             Y[mm * p.ldy + n] = to_bits<DT>(v);
         }
     }
+}
+
+// Skinny products with n-contiguous B (MatMul's own layout: a few activation
+// rows against weights stored (K, N)), M <= 4.  B rows are read as 16-byte
+// chunks of 8 columns (a wave reads RPI rows x CW columns per instruction)
+// and multiplied on the vector ALU: each lane keeps MR x 8 fp32 sums for its
+// 8 columns over its rows (the work per B byte is MR/2 multiply-adds, well
+// under the ALU rate at the HBM rate).  A is held in LDS transposed to (K,
+// MR) so one small LDS read per row gives all MR values.  A workgroup owns CW
+// columns over the whole of K, split in 4 ranges over its waves; the partial
+// sums are reduced across the lanes that share columns (shuffles) and across
+// the waves in LDS in a fixed order; wave 0 applies the epilogue.
+template <int DT, int MR, int CW>
+__global__ __launch_bounds__(256) void skinny_nmaj_kernel(DenseArgs p) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t At[];  // (K, MR)
+    __shared__ float red[3][CW / 8][MR][8];
+    constexpr int LPR = CW / 8, RPI = 64 / LPR, U = 8;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int64_t z = blockIdx.y, z0 = z / p.nb1, z1 = z - z0 * p.nb1;
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const uint16_t* __restrict__ A = (const uint16_t*)p.A + z0 * p.a_bs0 + z1 * p.a_bs1;
+    // Workgroups of neighbouring columns share B's cache lines: keep them on
+    // one XCD (workgroup b runs on XCD b % 8), so each line leaves HBM once.
+    const int cg = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+    const int c = lane % LPR, r = lane / LPR;
+    const int64_t n = (int64_t)cg * CW + 8 * c;
+    const bool nok = n < N;  // N % 8 == 0: whole chunks
+    const int64_t groups = (K + RPI - 1) / RPI;
+    const int64_t g0 = groups * wave / 4, g1 = groups * (wave + 1) / 4;
+    const int ng = (int)(g1 - g0);
+    const __amdgpu_buffer_rsrc_t rsb = sk_rsrc((const uint16_t*)p.B + z0 * p.b_bs0 + z1 * p.b_bs1);
+    const int64_t kb = g0 * RPI + r;  // this lane's first row
+
+    float acc[MR][8];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[m][e] = 0.0f;
+    auto load = [&](u32x4_t (&rb)[U], int i0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t k = kb + (int64_t)RPI * (i0 + u);
+            const bool ok = nok && i0 + u < ng && k < K;
+            rb[u] = sk_load(rsb, ok ? (uint32_t)((k * p.ldb + n) * 2) : SK_OOB);
+        }
+    };
+    auto fma_rows = [&](const u32x4_t (&rb)[U], int i0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            // rows past this wave's range or K hold B = 0: read any valid A row
+            const int64_t k = min(kb + (int64_t)RPI * (i0 + u), K - 1);
+            float av[MR];
+            if constexpr (MR == 1) {
+                av[0] = from_bits<DT>(At[k]);
+            } else if constexpr (MR == 2) {
+                const uint32_t w = *(const uint32_t*)(At + 2 * k);
+                av[0] = from_bits<DT>((uint16_t)w);
+                av[1] = from_bits<DT>((uint16_t)(w >> 16));
+            } else {
+                const u32x2_t w = *(const u32x2_t*)(At + 4 * k);
+                av[0] = from_bits<DT>((uint16_t)w.x);
+                av[1] = from_bits<DT>((uint16_t)(w.x >> 16));
+                av[2] = from_bits<DT>((uint16_t)w.y);
+                av[3] = from_bits<DT>((uint16_t)(w.y >> 16));
+            }
+            const uint32_t bw[4] = {rb[u].x, rb[u].y, rb[u].z, rb[u].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float bv = from_bits<DT>((uint16_t)(bw[e >> 1] >> (16 * (e & 1))));
+#pragma unroll
+                for (int m = 0; m < MR; ++m) acc[m][e] = __builtin_fmaf(av[m], bv, acc[m][e]);
+            }
+        }
+    };
+    u32x4_t b0[U], b1[U];
+    load(b0, 0);  // the first B rows are on their way while A is staged
+    {
+        // A rows as 16-byte chunks (K % 8 == 0), UA loads in flight per thread
+        // (one load then store per iteration would wait out every load);
+        // rows MR > M hold zeros
+        constexpr int UA = 4;
+        const __amdgpu_buffer_rsrc_t rsa = sk_rsrc(A);
+        const int64_t kc = K / 8, total = kc * MR;
+        for (int64_t c0 = 0; c0 < total; c0 += 256 * UA) {
+            u32x4_t v[UA];
+#pragma unroll
+            for (int u = 0; u < UA; ++u) {
+                const int64_t c = c0 + t + 256 * u, m = c / kc, q = c - m * kc;
+                v[u] = sk_load(rsa, c < total && m < M ? (uint32_t)((m * p.lda + 8 * q) * 2) : SK_OOB);
+            }
+#pragma unroll
+            for (int u = 0; u < UA; ++u) {
+                const int64_t c = c0 + t + 256 * u, m = c / kc, q = c - m * kc;
+                if (c < total) {
+                    if constexpr (MR == 1) {
+                        *(u32x4_t*)(At + 8 * q) = v[u];
+                    } else {
+                        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) At[(8 * q + e) * MR + m] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // straight-line ping-pong: loads past the range are out of bounds (no
+    // memory access, zeros), so the loop needs no exits in the middle
+    for (int i0 = 0; i0 < ng; i0 += 2 * U) {
+        load(b1, i0 + U);
+        fma_rows(b0, i0);
+        load(b0, i0 + 2 * U);
+        fma_rows(b1, i0 + U);
+    }
+    // lanes with the same c hold the same columns: add over r (lane bits >= log2 LPR)
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[m][e] += __shfl_xor(acc[m][e], off);
+    if (wave > 0 && r == 0) {
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red[wave - 1][c][m][e] = acc[m][e];
+    }
+    __syncthreads();
+    if (wave != 0 || r != 0 || !nok) return;
+    uint16_t* __restrict__ Y = (uint16_t*)p.Y + z0 * p.y_bs0 + z1 * p.y_bs1;
+    const uint16_t* Cp = (const uint16_t*)p.C;
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        if (m >= M) break;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float v = acc[m][e];
+#pragma unroll
+            for (int w = 0; w < 3; ++w) v += red[w][c][m][e];
+            v *= p.alpha;
+            if (Cp) v += p.beta * from_bits<DT>(Cp[m * p.c_sm + (n + e) * p.c_sn]);
+            Y[m * p.ldy + n + e] = to_bits<DT>(v);
+        }
+    }
+}
+
+template <int DT, int MR>
+hipError_t launch_skinny_nmaj(const DenseArgs& a, hipStream_t s) {
+    const int64_t NB = a.nb0 * a.nb1;
+    const size_t lds = (size_t)a.K * MR * 2;
+    if ((a.N + 31) / 32 * NB >= 512) {
+        hipLaunchKernelGGL((skinny_nmaj_kernel<DT, MR, 32>), dim3((unsigned)((a.N + 31) / 32), (unsigned)NB), dim3(256),
+                           lds, s, a);
+    } else {
+        hipLaunchKernelGGL((skinny_nmaj_kernel<DT, MR, 16>), dim3((unsigned)((a.N + 15) / 16), (unsigned)NB), dim3(256),
+                           lds, s, a);
+    }
+    return hipGetLastError();
 }
 
 template <int BM, int BN, int DT, bool AK, bool BKM, int MODE>
@@ -472,12 +649,29 @@ hipError_t launch_dt(const DenseArgs& a, hipStream_t s) {
     }
     const int64_t NB = a.nb0 * a.nb1;
     // Skinny (M <= 16) with both operands k-contiguous: stream B, split K.
-    if (vec && a.M <= 16 && a.a_kmajor && a.b_kmajor && a.K >= 1024 && NB <= 65535 &&
+    // Skinny (M <= 4) against n-contiguous B, enough columns to fill the chip
+    // with 16-column workgroups, A (K x MR x 2 bytes) within 60 KB of LDS.
+    // (buffer offsets are 32-bit: one batch entry of B below 2 GiB)
+    const bool b_span = (a.b_kmajor ? a.N * a.ldb : a.K * a.ldb) * 2 < (1LL << 31);
+    const bool a_span = a.M * a.lda * 2 < (1LL << 31);
+    // (measured: ahead of the split-K path for M <= 2 at any K and for M <= 4
+    // up to K = 4096; behind it for 3-4 rows and longer K)
+    if (vec && b_span && a_span && (a.M <= 2 || (a.M <= 4 && a.K <= 4096)) && a.a_kmajor && !a.b_kmajor &&
+        a.K >= 1024 && NB <= 65535 &&
+        (a.N + 15) / 16 * NB >= 256 && (a.N + 15) / 16 <= 0x7fffffff) {
+        const int64_t mr = a.M <= 1 ? 1 : a.M <= 2 ? 2 : 4;
+        if (a.K * mr * 2 <= 61440) {
+            if (mr == 1) return launch_skinny_nmaj<DT, 1>(a, s);
+            if (mr == 2) return launch_skinny_nmaj<DT, 2>(a, s);
+            return launch_skinny_nmaj<DT, 4>(a, s);
+        }
+    }
+    if (vec && b_span && a_span && a.M <= 16 && a.a_kmajor && a.b_kmajor && a.K >= 1024 && NB <= 65535 &&
         (a.N + 15) / 16 * NB >= 512 && (a.N + 15) / 16 <= 0x7fffffff) {
         hipLaunchKernelGGL(skinny1_kernel<DT>, dim3((unsigned)((a.N + 15) / 16), (unsigned)NB), dim3(256), 0, s, a);
         return hipGetLastError();
     }
-    if (vec && a.M <= 16 && a.a_kmajor && a.b_kmajor && a.K >= 1024 && NB <= 65535) {
+    if (vec && b_span && a_span && a.M <= 16 && a.a_kmajor && a.b_kmajor && a.K >= 1024 && NB <= 65535) {
         const int64_t groups = (a.N + SK_COLS - 1) / SK_COLS;
         int64_t S = std::max<int64_t>((512 + groups * NB - 1) / (groups * NB), (a.K + SK_KMAX - 1) / SK_KMAX);
         S = std::min<int64_t>(S, (a.K + 255) / 256);

@@ -251,6 +251,40 @@ def test_gemm_skinny_stream(dt, M, N, K):
     check_close(host_f64(Y).ravel()[sel], y, 0.75 * t + 1.25 * cabs, dt, "skinny %s M=%d N=%d K=%d" % (dt, M, N, K))
 
 
+SKINNY_NMAJ = [  # MatMul with a few rows against B stored (K, N): the vector-ALU streaming kernel
+    ((1, 8192), (8192, 8192)), ((8192,), (8192, 4096)), ((3, 2048), (2048, 4104)), ((2, 1024), (1024, 8200)),
+    ((2, 1, 1024), (2, 1024, 2048)), ((4, 4096), (4096, 4096)), ((4, 7680), (7680, 4096)),
+]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("sa,sb", SKINNY_NMAJ)
+def test_matmul_skinny_nmajor(dt, sa, sb):
+    rng = np.random.default_rng(sum(sa) + sum(sb))
+    A = synth.store(synth.normal(rng, sa), dt)
+    B = synth.store(synth.normal(rng, sb, 0.02), dt)
+    Y = om.matmul(dev(A, dt), dev(B, dt))
+    torch.cuda.synchronize()
+    ysh = oracle.matmul_shape(A.shape, B.shape)
+    sel = sample_indices(int(np.prod(ysh)), 20000, 10)
+    y, t = oracle.matmul(A, B, dt=dt, sel=sel)
+    assert tuple(Y.shape) == tuple(ysh)
+    check_close(host_f64(Y).ravel()[sel], y, t, dt, "skinny n-major %s %s x %s" % (dt, sa, sb))
+
+
+def test_gemm_skinny_nmajor_epilogue_exact():
+    """Gemm transB=0 with 2 rows, C per row and column, small integers: bit-exact."""
+    rng = np.random.default_rng(12)
+    M, K, N = 2, 4096, 4096
+    A = synth.store(rng.integers(-1, 2, (M, K)).astype(np.float32) * (np.arange(K) % 16 == 0), "bf16")
+    B = synth.store(rng.integers(-1, 2, (K, N)).astype(np.float32), "bf16")
+    C = synth.store(rng.integers(-8, 9, (M, N)).astype(np.float32), "bf16")
+    Y = om.gemm(dev(A, "bf16"), dev(B, "bf16"), dev(C, "bf16"), 1.0, 2.0, 0, 0)
+    torch.cuda.synchronize()
+    y, _ = oracle.gemm(A, B, C, 1.0, 2.0, 0, 0, dt="bf16")
+    assert np.array_equal(host_f64(Y), y)
+
+
 @pytest.mark.parametrize("M", [1, 5, 16])
 def test_gemm_skinny_exact(M):
     """Small integers (entries in {-1, 0, 1}, |partial sums| <= 256): bit-exact."""
