@@ -586,53 +586,69 @@ __device__ __forceinline__ u32x2_t read_frag_q8(const char* lds, int colb, int s
     return __builtin_bit_cast(u32x2_t, v);
 }
 
+// Wave layout of the dequantising kernel: TM row blocks x TN column blocks of
+// 32 per wave, rows row0 + 32 i, columns col0 + 32 j (1x4: each wave all 256
+// rows and its own 64 columns, so every weight fragment is dequantised by one
+// wave only).
+template <int TM, int TN>
 struct FragsDQ {
-    u32x4_t a[4], b[4];
-    u32x2_t braw[4];
+    u32x4_t a[TM], b[TN];
+    u32x2_t braw[TN];
 };
 
-// read r of a k-block (frag_order: B0 A0 B1 B2 B3 A1 A2 A3) goes out after
-// MFMA 2r; weight fragment j is converted 4 MFMAs after its read
-constexpr int dq_read_pos(int f) {
-    for (int r = 0; r < 8; ++r)
-        if (core16::frag_order(4, 4, r) == f) return r;
+// reads of a k-block in order of first use (frag_order), read r after MFMA
+// slot dq_read_slot(r); weight fragment j converted 4 MFMAs after its read
+constexpr int dq_read_slot(int TM, int TN, int r) {
+    const int NM = TM * TN, NR = TM + TN;
+    for (int x = 0; x < NM; ++x)
+        if (r < ((x + 1) * NR + NM - 1) / NM) return x;
+    return NM - 1;
+}
+constexpr int dq_conv_slot(int TM, int TN, int j) {
+    for (int r = 0; r < TM + TN; ++r)
+        if (core16::frag_order(TM, TN, r) == TM + j) return dq_read_slot(TM, TN, r) + 4;
     return -1;
 }
-constexpr int dq_conv_slot(int j) { return 2 * dq_read_pos(4 + j) + 4; }
 
-// per-stage dequantisation constants of this lane's 4 columns: w = fma(q', sf, cf)
+// per-stage dequantisation constants of this lane's TN columns: w = fma(q', sf, cf)
+template <int TN>
 struct DqScales {
-    float sf[4], cf[4];
+    float sf[TN], cf[TN];
 };
 
-template <int DT, bool QU8, int X>
-__device__ __forceinline__ void dq_slot_reads(FragsDQ& nxt, const char* lds, int s, int lane, int wm, int wn,
-                                              const DqScales& sc) {
+template <int DT, bool QU8, int TM, int TN, int X>
+__device__ __forceinline__ void dq_slot_reads(FragsDQ<TM, TN>& nxt, const char* lds, int s, int lane, int row0,
+                                              int col0, const DqScales<TN>& sc) {
     using namespace core16;
     constexpr int A_BYTES = GBM * KSTEP * 2;
-    if constexpr (X % 2 == 0 && X / 2 < 8) {
-        constexpr int f = frag_order(4, 4, X / 2);
-        if constexpr (f < 4)
-            nxt.a[f] = read_frag<GBM, true>(lds, wm * 128 + 32 * f, s, lane);
-        else
-            nxt.braw[f - 4] = read_frag_q8(lds + A_BYTES, wn * 128 + 32 * (f - 4), s, lane);
-    }
-    static_for<0, 4>([&](auto jc) {
+    static_for<0, TM + TN>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        if constexpr (dq_read_slot(TM, TN, r) == X) {
+            constexpr int f = frag_order(TM, TN, r);
+            if constexpr (f < TM)
+                nxt.a[f] = read_frag<GBM, true>(lds, row0 + 32 * f, s, lane);
+            else
+                nxt.braw[f - TM] = read_frag_q8(lds + A_BYTES, col0 + 32 * (f - TM), s, lane);
+        }
+    });
+    static_for<0, TN>([&](auto jc) {
         constexpr int j = decltype(jc)::value;
-        if constexpr (dq_conv_slot(j) == X) nxt.b[j] = dq8<DT, QU8>(nxt.braw[j], sc.sf[j], sc.cf[j]);
+        if constexpr (dq_conv_slot(TM, TN, j) == X) nxt.b[j] = dq8<DT, QU8>(nxt.braw[j], sc.sf[j], sc.cf[j]);
     });
 }
 
 // One k-block of MFMAs on `cur`, the reads (and conversions) of k-block s of
 // `lds` into `nxt`, and this wave's DMA instructions D0 .. D1-1 of stage kt
 // into buffer Xb spread between the MFMAs (none when D0 == D1).
-template <int DT, bool QU8, int D0, int D1, class SA, class SB>
-__device__ __forceinline__ void kblock_dq(f32x16_t (&acc)[4][4], const FragsDQ& cur, FragsDQ& nxt, const char* lds,
-                                          int s, char* Xb, const SA& srcA, const SB& srcB, int kt, bool live,
-                                          int lane, int wm, int wn, int wave, const DqScales& sc) {
+template <int DT, bool QU8, int TM, int TN, int D0, int D1, class SA, class SB>
+__device__ __forceinline__ void kblock_dq(f32x16_t (&acc)[TM][TN], const FragsDQ<TM, TN>& cur,
+                                          FragsDQ<TM, TN>& nxt, const char* lds, int s, char* Xb, const SA& srcA,
+                                          const SB& srcB, int kt, bool live, int lane, int row0, int col0, int wave,
+                                          const DqScales<TN>& sc) {
     using namespace core16;
     constexpr int A_BYTES = GBM * KSTEP * 2;
-    constexpr int NM = 16, ND = D1 - D0, LA = SA::PER_WAVE;
+    constexpr int NM = TM * TN, ND = D1 - D0, LA = SA::PER_WAVE;
+    static_assert(dq_conv_slot(TM, TN, TN - 1) < NM, "every conversion inside the k-block");
     DmaCtx ca{}, cb{};
     if constexpr (ND > 0) {
         ca = srcA.ctx(Xb, kt, live);
@@ -640,11 +656,11 @@ __device__ __forceinline__ void kblock_dq(f32x16_t (&acc)[4][4], const FragsDQ& 
     }
     static_for<0, NM>([&](auto xc) {
         constexpr int x = decltype(xc)::value;
-        acc[x / 4][x % 4] = mfma32x32x16<DT>(cur.b[x % 4], cur.a[x / 4], acc[x / 4][x % 4]);
+        acc[x / TN][x % TN] = mfma32x32x16<DT>(cur.b[x % TN], cur.a[x / TN], acc[x / TN][x % TN]);
         if constexpr (ND > 0)
             static_for<D0 + (x * ND + NM - 1) / NM, D0 + ((x + 1) * ND + NM - 1) / NM>(
                 [&](auto dc) { dma_one<true, LA, decltype(dc)::value>(srcA, srcB, ca, cb, kt, wave); });
-        dq_slot_reads<DT, QU8, x>(nxt, lds, s, lane, wm, wn, sc);
+        dq_slot_reads<DT, QU8, TM, TN, x>(nxt, lds, s, lane, row0, col0, sc);
         fence_sched();
     });
 }
@@ -673,12 +689,12 @@ struct DqParams {
         const uint32_t voff = (lane < nl && n0 + (int64_t)lane * (16 / es) < N) ? (uint32_t)lane * 16u : DMA_OOB;
         dma16u(r, lds_addr(buf + DQ_SC_OFF + (isz ? 1024 : 0)), voff);
     }
-    // this lane's columns: wn * 128 + 32 j + lane % 32
-    template <int DT, bool QU8>
-    __device__ __forceinline__ void to_scales(const char* buf, int wn, int lane, DqScales& o) const {
+    // this lane's columns: col0 + 32 j + lane % 32
+    template <int DT, bool QU8, int TN>
+    __device__ __forceinline__ void to_scales(const char* buf, int col0, int lane, DqScales<TN>& o) const {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c = wn * 128 + 32 * j + (lane & 31);
+        for (int j = 0; j < TN; ++j) {
+            const int c = col0 + 32 * j + (lane & 31);
             o.sf[j] = from_bits<DT>(*(const uint16_t*)(buf + DQ_SC_OFF + 2 * c));
             const uint32_t zb = *(const uint8_t*)(buf + DQ_SC_OFF + 1024 + c);
             const int zs = QU8 ? (int)zb : (int)(int8_t)zb + 128;
@@ -687,28 +703,30 @@ struct DqParams {
     }
 };
 
-template <int DT, bool QU8, class SA, class SB>
-__device__ __forceinline__ void dq_stage(f32x16_t (&acc)[4][4], FragsDQ& fc, FragsDQ& fn, char* X, char* Y,
-                                         const SA& srcA, const SB& srcB, DqParams& prm, DqScales& sc, int kt, int nk,
-                                         int lane, int wm, int wn, int wave) {
+template <int DT, bool QU8, int TM, int TN, class SA, class SB>
+__device__ __forceinline__ void dq_stage(f32x16_t (&acc)[TM][TN], FragsDQ<TM, TN>& fc, FragsDQ<TM, TN>& fn, char* X,
+                                         char* Y, const SA& srcA, const SB& srcB, DqParams& prm, DqScales<TN>& sc,
+                                         int kt, int nk, int lane, int row0, int col0, int wave) {
     using namespace core16;
     constexpr int LD = SA::PER_WAVE + SB::PER_WAVE, H = LD / 2;
     fence_sched();
     prm.issue(Y, kt + 1, kt + 1 < nk, wave, lane);
-    kblock_dq<DT, QU8, H, LD>(acc, fc, fn, X, 1, Y, srcA, srcB, kt + 1, kt + 1 < nk, lane, wm, wn, wave, sc);
-    kblock_dq<DT, QU8, 0, 0>(acc, fn, fc, X, 2, Y, srcA, srcB, kt, false, lane, wm, wn, wave, sc);
-    kblock_dq<DT, QU8, 0, 0>(acc, fc, fn, X, 3, Y, srcA, srcB, kt, false, lane, wm, wn, wave, sc);
+    kblock_dq<DT, QU8, TM, TN, H, LD>(acc, fc, fn, X, 1, Y, srcA, srcB, kt + 1, kt + 1 < nk, lane, row0, col0, wave,
+                                      sc);
+    kblock_dq<DT, QU8, TM, TN, 0, 0>(acc, fn, fc, X, 2, Y, srcA, srcB, kt, false, lane, row0, col0, wave, sc);
+    kblock_dq<DT, QU8, TM, TN, 0, 0>(acc, fc, fn, X, 3, Y, srcA, srcB, kt, false, lane, row0, col0, wave, sc);
     wait_vm<0>();     // stage kt+1 (tiles and scales) has landed
     __syncthreads();  // ... for every wave; every read of X is done
-    prm.template to_scales<DT, QU8>(Y, wn, lane, sc);
+    prm.template to_scales<DT, QU8, TN>(Y, col0, lane, sc);
     fence_sched();
-    kblock_dq<DT, QU8, 0, H>(acc, fn, fc, Y, 0, X, srcA, srcB, kt + 2, kt + 2 < nk, lane, wm, wn, wave, sc);
+    kblock_dq<DT, QU8, TM, TN, 0, H>(acc, fn, fc, Y, 0, X, srcA, srcB, kt + 2, kt + 2 < nk, lane, row0, col0, wave,
+                                     sc);
 }
 
-template <int DT, bool QU8, class SA, class SB>
-__device__ __forceinline__ void mainloop_dq_dma(f32x16_t (&acc)[4][4], char* __restrict__ s0, char* __restrict__ s1,
+template <int DT, bool QU8, int TM, int TN, class SA, class SB>
+__device__ __forceinline__ void mainloop_dq_dma(f32x16_t (&acc)[TM][TN], char* __restrict__ s0, char* __restrict__ s1,
                                                 const SA& srcA, const SB& srcB, DqParams& prm, int nk, int lane,
-                                                int wm, int wn, int wave) {
+                                                int row0, int col0, int wave) {
     using namespace core16;
     constexpr int A_BYTES = GBM * KSTEP * 2;
     constexpr int LA = SA::PER_WAVE, LD = SA::PER_WAVE + SB::PER_WAVE, H = LD / 2;
@@ -722,20 +740,64 @@ __device__ __forceinline__ void mainloop_dq_dma(f32x16_t (&acc)[4][4], char* __r
     }
     wait_vm<H>();
     __syncthreads();
-    DqScales sc;
-    prm.template to_scales<DT, QU8>(s0, wn, lane, sc);
+    DqScales<TN> sc;
+    prm.template to_scales<DT, QU8, TN>(s0, col0, lane, sc);
     fence_sched();
-    FragsDQ fc, fn;
+    FragsDQ<TM, TN> fc, fn;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fc.a[i] = read_frag<GBM, true>(s0, wm * 128 + 32 * i, 0, lane);
+    for (int i = 0; i < TM; ++i) fc.a[i] = read_frag<GBM, true>(s0, row0 + 32 * i, 0, lane);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        fc.b[j] = dq8<DT, QU8>(read_frag_q8(s0 + A_BYTES, wn * 128 + 32 * j, 0, lane), sc.sf[j], sc.cf[j]);
+    for (int j = 0; j < TN; ++j)
+        fc.b[j] = dq8<DT, QU8>(read_frag_q8(s0 + A_BYTES, col0 + 32 * j, 0, lane), sc.sf[j], sc.cf[j]);
     for (int kt = 0; kt < nk; kt += 2) {
-        dq_stage<DT, QU8>(acc, fc, fn, s0, s1, srcA, srcB, prm, sc, kt, nk, lane, wm, wn, wave);
-        dq_stage<DT, QU8>(acc, fc, fn, s1, s0, srcA, srcB, prm, sc, kt + 1, nk, lane, wm, wn, wave);
+        dq_stage<DT, QU8, TM, TN>(acc, fc, fn, s0, s1, srcA, srcB, prm, sc, kt, nk, lane, row0, col0, wave);
+        dq_stage<DT, QU8, TM, TN>(acc, fc, fn, s1, s0, srcA, srcB, prm, sc, kt + 1, nk, lane, row0, col0, wave);
     }
     wait_vm<0>();
+}
+
+// Epilogue of a TM x TN block of 32x32 results (rows row0 + 32 i, columns
+// col0 + 32 j of the tile): + bias[g], one rounding to T, 4-value stores to
+// each row's output[pair] (output and bias 8-byte aligned, N % 8 == 0).
+template <int DT, int TM, int TN>
+__device__ __forceinline__ void grouped_epilogue_blocks(const f32x16_t (&acc)[TM][TN], const GroupedArgs& a, int g,
+                                                        int64_t n0, int row0, int col0, int lane, const int* orow_s) {
+    const int64_t N = a.N;
+    const uint16_t* __restrict__ bias = a.bias ? (const uint16_t*)a.bias + (int64_t)g * N : nullptr;
+    uint16_t* __restrict__ out = (uint16_t*)a.output;
+    const int64_t nl = n0 + col0 + 4 * (lane >> 5);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        float bv[4][4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t n = nl + 32 * j + 8 * q;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bv[q][e] = 0.0f;
+            if (bias && n < N) {
+                const u32x2_t b2 = *(const u32x2_t*)(bias + n);
+                bv[q][0] = from_bits<DT>((uint16_t)b2.x);
+                bv[q][1] = from_bits<DT>((uint16_t)(b2.x >> 16));
+                bv[q][2] = from_bits<DT>((uint16_t)b2.y);
+                bv[q][3] = from_bits<DT>((uint16_t)(b2.y >> 16));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int o = orow_s[row0 + 32 * i + (lane & 31)];
+            if (o < 0) continue;
+            uint16_t* __restrict__ yr = out + (int64_t)o * N;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t n = nl + 32 * j + 8 * q;
+                if (n >= N) continue;
+                u32x2_t st;
+                st.x = pack2<DT>(acc[i][j][4 * q + 0] + bv[q][0], acc[i][j][4 * q + 1] + bv[q][1]);
+                st.y = pack2<DT>(acc[i][j][4 * q + 2] + bv[q][2], acc[i][j][4 * q + 3] + bv[q][3]);
+                *(u32x2_t*)(yr + n) = st;
+            }
+        }
+    }
 }
 
 // Weights by DMA: K % 64 == 0, N % 16 == 0, 16-byte aligned q, scale and
@@ -759,14 +821,16 @@ __global__ __launch_bounds__(256) void grouped16_dq_dma_kernel(GroupedArgs a, co
     const int g = te.x, start = te.y, rows = te.z;
     const int* sorted = (const int*)(ws + off_sorted(a.M * a.S, a.G));
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
     const int64_t K = a.K, N = a.N, S = a.S;
     const int64_t n0 = (int64_t)tn * GBN;
-    f32x16_t acc[4][4];
+    // 1x4 wave layout: all 256 rows, 64 columns per wave
+    constexpr int TM = 8, TN = 2;
+    const int row0 = 0, col0 = 64 * wave;
+    f32x16_t acc[TM][TN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     const int nk = (int)(K / KSTEP);
@@ -791,8 +855,9 @@ __global__ __launch_bounds__(256) void grouped16_dq_dma_kernel(GroupedArgs a, co
     prm.N = N;
     prm.bs = a.bs;
     prm.n0 = n0;
-    mainloop_dq_dma<DT, QU8>(acc, s0, s1, srcA, srcB, prm, nk, lane, wm, wn, wave);
-    grouped_epilogue<DT, true>(acc, a, g, rows, start, sorted, n0, lane, wave, s0, s1, orow_s);
+    mainloop_dq_dma<DT, QU8, TM, TN>(acc, s0, s1, srcA, srcB, prm, nk, lane, row0, col0, wave);
+    __syncthreads();  // orow_s complete even when the K loop ran no stage (K = 0)
+    grouped_epilogue_blocks<DT, TM, TN>(acc, a, g, n0, row0, col0, lane, orow_s);
 }
 
 template <int DT, bool QU8, bool FAST>
