@@ -256,11 +256,13 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(DenseArgs p) {
 // B, so the kernel is built to stream B from HBM: each wave owns 16 columns
 // and loads its B operand straight from global memory in the
 // v_mfma_f32_16x16x32 operand layout (lane l: column l%16, 8 consecutive k at
-// 8 (l/16)), 8 k-steps of 32 in flight ahead of the MFMAs; A (16 rows, zero
-// past M) sits in LDS for the workgroup's K range and is shared by its 4
-// waves.  K is split over gridDim.y ranges so that every CU streams; the fp32
-// partial products go to the split-K workspace and splitk_reduce_kernel adds
-// them in a fixed order and applies the epilogue.
+// 8 (l/16)), one batch of SK_U k-steps of 32 in flight while the previous
+// batch multiplies; A (16 rows, zero past M) sits in LDS for the workgroup's
+// K range and is shared by its 4 waves.  K is split over gridDim.y ranges so
+// that every CU streams; the fp32 partial products go to the split-K
+// workspace and splitk_reduce_kernel adds them in a fixed order and applies
+// the epilogue.  (skinny1_kernel below covers shapes with enough columns in
+// one pass.)
 constexpr int SK_COLS = 64;      // columns per workgroup (4 waves x 16)
 constexpr int SK_U = 16;         // k-steps of 32 per batch of loads
 constexpr int SK_KMAX = 2048;    // k per workgroup (A rows in LDS: 16 x 2048 x 2 bytes)
