@@ -18,7 +18,11 @@
 //      from input[p / S], B = weights[g] (n contiguous, read through the
 //      transposing LDS path), epilogue adds bias[g] in fp32, rounds once and
 //      writes each row to output[p].  The grid is the upper bound
-//      (M*S/BM + G) x (N/BN); workgroups past the routed tile count exit.
+//      (M*S/BM + G) x (N/BN); the routed tiles are split evenly over the 8
+//      XCDs and each XCD's surplus workgroups exit.
+//   Weight-only quantised experts (int8/uint8 weights with block scales) run
+//   the same routing and grouped16_dq_dma_kernel / grouped16_dq_kernel, which
+//   dequantise each weight tile on its way into the MFMAs.
 // No host synchronisation between the two.  Each output row depends only on
 // its own pair, so the order of pairs inside a group never changes a value.
 #include "gemm16_core.hpp"
@@ -310,7 +314,7 @@ __device__ __forceinline__ void grouped_body(const GroupedArgs& a, const char* w
 }
 
 template <int DT, bool VEC>
-__global__ __launch_bounds__(256) void grouped16_kernel(GroupedArgs a, const char* ws, int max_mtiles, int tiles_n) {
+__global__ __launch_bounds__(256) void grouped16_kernel(GroupedArgs a, const char* ws, int tiles_n) {
     __shared__ __attribute__((aligned(1024))) char s0[(GBM + GBN) * core16::KSTEP * 2];
     __shared__ __attribute__((aligned(1024))) char s1[(GBM + GBN) * core16::KSTEP * 2];
     __shared__ int orow_s[GBM];
@@ -318,7 +322,6 @@ __global__ __launch_bounds__(256) void grouped16_kernel(GroupedArgs a, const cha
     // routed count is known only here.  Workgroup b runs on XCD b % 8, so the
     // routed tiles are split evenly over the 8 XCDs (each takes one contiguous
     // run of the tile order) and the surplus workgroups of every XCD exit.
-    (void)max_mtiles;
     const int ntiles = ((const int*)ws)[0];
     const int total = ntiles * tiles_n;
     const int b = (int)blockIdx.x, x = b & 7, l = b >> 3;
@@ -1087,11 +1090,11 @@ hipError_t launch_grouped(const GroupedArgs& a, int dt, void* ws, hipStream_t s)
     dim3 grid((unsigned)(max_mtiles * tiles_n));
     const char* wsc = (const char*)ws;
     if (dt == 0) {
-        if (vec) hipLaunchKernelGGL((grouped16_kernel<0, true>), grid, dim3(256), 0, s, a, wsc, (int)max_mtiles, (int)tiles_n);
-        else hipLaunchKernelGGL((grouped16_kernel<0, false>), grid, dim3(256), 0, s, a, wsc, (int)max_mtiles, (int)tiles_n);
+        if (vec) hipLaunchKernelGGL((grouped16_kernel<0, true>), grid, dim3(256), 0, s, a, wsc, (int)tiles_n);
+        else hipLaunchKernelGGL((grouped16_kernel<0, false>), grid, dim3(256), 0, s, a, wsc, (int)tiles_n);
     } else {
-        if (vec) hipLaunchKernelGGL((grouped16_kernel<1, true>), grid, dim3(256), 0, s, a, wsc, (int)max_mtiles, (int)tiles_n);
-        else hipLaunchKernelGGL((grouped16_kernel<1, false>), grid, dim3(256), 0, s, a, wsc, (int)max_mtiles, (int)tiles_n);
+        if (vec) hipLaunchKernelGGL((grouped16_kernel<1, true>), grid, dim3(256), 0, s, a, wsc, (int)tiles_n);
+        else hipLaunchKernelGGL((grouped16_kernel<1, false>), grid, dim3(256), 0, s, a, wsc, (int)tiles_n);
     }
     return hipGetLastError();
 }
