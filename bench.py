@@ -14,8 +14,8 @@ reported against the MI355X dense MFMA peak of its type under `per_config`;
 `cold_ms` there is the median of calls issued right after a 512 MiB write that
 evicts the last-level cache (operands start in HBM only).  `next_rows` times
 workloads outside the step the same way (GroupedMatMul over int8 weights with
-the dequantisation fused, an fp64 Gemm, decode-like skinny Gemms against the
-HBM peak); they are not part of `value`.
+the dequantisation fused, an fp64 Gemm, uint8 QLinearMatMul, decode-like
+skinny Gemms against the HBM peak); they are not part of `value`.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--only NAME]
        python bench.py --copy-calibration      (1 GiB device-to-device copies, for
@@ -164,6 +164,29 @@ def next_rows(torch, om, synth, dev, reps):
                      dtype="f64", ms=round(med, 4), tflops=round(rate, 2), frac_peak=round(rate / PEAK["f64"], 4),
                      hbm_gbs=round((3 * n * n + n) * 8 / (med * 1e-3) / 1e9, 1)))
     del A64, B64, C64, Y64
+    # QLinearMatMul with uint8 operands and output at the int8 workload's size
+    q = 4096
+    a8 = torch.from_numpy(rng.integers(0, 256, (q, q)).astype(np.uint8)).cuda()
+    b8 = torch.from_numpy(rng.integers(0, 256, (q, q)).astype(np.uint8)).cuda()
+    asc = torch.from_numpy(synth.uniform(rng, (q, 1), 0.002, 0.01)).cuda()
+    bsc = torch.from_numpy(synth.uniform(rng, (1, q), 0.002, 0.01)).cuda()
+    az = torch.from_numpy(rng.integers(112, 145, (q, 1)).astype(np.uint8)).cuda()
+    bz = torch.from_numpy(rng.integers(112, 145, (1, q)).astype(np.uint8)).cuda()
+    ys = torch.tensor(0.05, device="cuda")
+    yz = torch.tensor(128, dtype=torch.uint8, device="cuda")
+    y8 = torch.empty((q, q), dtype=torch.uint8, device="cuda")
+    fn = lambda: om.qlinear_matmul(a8, asc, az, b8, bsc, bz, ys, yz, y8)
+    fn()
+    torch.cuda.synchronize()
+    med, _ = time_each(torch, fn, reps)
+    rate = 2 * q ** 3 / (med * 1e-3) / 1e12
+    log("%-20s %9.4f ms  %8.1f T/s  %5.1f%% of int8 peak (not in the step)" % ("qlinear_u8_4096", med, rate,
+                                                                               100 * rate / PEAK["int8"]))
+    rows.append(dict(workload="qlinear_u8_4096", desc="QLinearMatMul uint8 x uint8 -> uint8 4096^3, per-row / per-column "
+                     "scales U(0.002,0.01), zero points U[112,144], y_scale 0.05, y_zp 128, seed 6", dtype="uint8",
+                     ms=round(med, 4), tflops=round(rate, 2), frac_peak=round(rate / PEAK["int8"], 4),
+                     hbm_gbs=round(3 * q * q / (med * 1e-3) / 1e9, 1)))
+    del a8, b8, y8
     # decode-like skinny Gemm (split-K path): HBM-bound, reported against the HBM peak
     for M, tB in ((1, 1), (16, 1), (1, 0)):
         N = K = 8192
