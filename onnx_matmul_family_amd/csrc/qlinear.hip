@@ -10,9 +10,10 @@
 // The row sums of a and column sums of b come from the MFMA operand fragments
 // already in registers, so no extra pass over memory: each dword of 4 signed
 // bytes is biased to unsigned (xor 0x80) and summed with v_sad_u8 against
-// zero, and the bias is taken off at the end.  (The v_dot4 instructions would
-// do it in one step, but on gfx950 they hold up the MFMAs issued around them;
-// v_sad_u8 and v_xor do not.)  uint8 operands are mapped to int8 by flipping the top bit
+// zero, and the bias is taken off at the end; of the two waves that read a
+// fragment, only one sums it.  (The v_dot4 instructions would do it in one
+// step, but on gfx950 they hold up the MFMAs issued around them; v_sad_u8 and
+// v_xor cost issue slots only.)  uint8 operands are mapped to int8 by flipping the top bit
 // (a - 128) and their zero points shifted by 128, which leaves every a - za
 // unchanged.  The requantisation uses IEEE fp32 multiply, correctly rounded
 // division and round-half-even, in the order above, with no contraction.
@@ -116,10 +117,10 @@ __device__ __forceinline__ i32x4_t frag_b(const char* s, int colb, int ks, int l
 // acc + sum of the 4 bytes of v taken as int8, each biased by +128 (the bias,
 // 128 per byte summed, is removed once after the K loop)
 __device__ __forceinline__ int bytesum1(int v, int acc) {
-    // the xor is opaque to the compiler: for uint8 operands v is itself a
-    // flipped value, and folding the two flips would keep both copies live
-    uint32_t u;
-    asm("v_xor_b32 %0, 0x80808080, %1" : "=v"(u) : "v"(v));
+    // plain C: for uint8 operands v comes out of the opaque flip below, so the
+    // compiler cannot fold the two xors (and keep both copies of the fragment
+    // live), and a known instruction needs no hazard padding before v_sad_u8
+    const uint32_t u = (uint32_t)v ^ 0x80808080u;
     return (int)__builtin_amdgcn_sad_u8(u, 0u, (uint32_t)acc);
 }
 __device__ __forceinline__ int bytesum(i32x4_t v, int acc) {
@@ -196,22 +197,29 @@ struct QFrags {
     }
 };
 
-// MFMA X of a k-block (tile (X/4, X%4)) plus one dword of the row sums and
-// one of the column sums, so the 32 sums ride along the 16 MFMAs.
-template <int X, class F>
+// MFMA X of a k-block (tile (X/4, X%4)) plus one dword of the byte sums.
+// The two waves that read the same a-fragments (same wm) have different roles
+// R = wm ^ wn, and so do the two that read the same b-fragments (same wn):
+// a wave sums only a-fragments 2R, 2R+1 (during MFMAs 0-7) and b-fragments
+// 2R, 2R+1 (MFMAs 8-15), so every fragment's bytes are summed once per
+// workgroup, 16 dwords per wave and k-block.
+template <int X, int R, class F>
 __device__ __forceinline__ void q_one(i32x16_t (&acc)[4][4], int (&rs)[4], int (&cs)[4], const F& f) {
     acc[X / 4][X % 4] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.b[X % 4], f.a[X / 4], acc[X / 4][X % 4], 0, 0, 0);
-    rs[X / 4] = bytesum1(f.a[X / 4][X % 4], rs[X / 4]);
-    cs[X / 4] = bytesum1(f.b[X / 4][X % 4], cs[X / 4]);
+    constexpr int I = 2 * R + (X & 7) / 4;
+    if constexpr (X < 8)
+        rs[I] = bytesum1(f.a[I][X % 4], rs[I]);
+    else
+        cs[I] = bytesum1(f.b[I][X % 4], cs[I]);
 }
 
-template <class F>
+template <int R, class F>
 __device__ __forceinline__ void q_kblock(i32x16_t (&acc)[4][4], int (&rs)[4], int (&cs)[4], const F& cur, F& nxt,
                                          const char* lds, int ks, int lane, int wm, int wn) {
     using namespace core16;
     static_for<0, 16>([&](auto xc) {
         constexpr int x = decltype(xc)::value;
-        q_one<x>(acc, rs, cs, cur);
+        q_one<x, R>(acc, rs, cs, cur);
         if constexpr ((x & 1) == 0) nxt.template read_one<core16::frag_order(4, 4, x / 2)>(lds, ks, lane, wm, wn);
         fence_sched();
     });
@@ -220,7 +228,7 @@ __device__ __forceinline__ void q_kblock(i32x16_t (&acc)[4][4], int (&rs)[4], in
 // A k-block of MFMAs on `cur`, the reads of k-block ks of `lds` into `nxt`,
 // and this wave's DMA instructions D0 .. D1-1 of stage kt (into buffer X)
 // spread evenly between the MFMAs.
-template <bool CHECKED, int D0, int D1, class F, class SA, class SB>
+template <bool CHECKED, int R, int D0, int D1, class F, class SA, class SB>
 __device__ __forceinline__ void q_kblock_dma(i32x16_t (&acc)[4][4], int (&rs)[4], int (&cs)[4], const F& cur, F& nxt,
                                              const char* lds, int ks, char* X, const SA& sa, const SB& sb, int kt,
                                              bool live, int lane, int wm, int wn, int wave) {
@@ -229,7 +237,7 @@ __device__ __forceinline__ void q_kblock_dma(i32x16_t (&acc)[4][4], int (&rs)[4]
     const DmaCtx ca = sa.ctx(X, kt, live), cb = sb.ctx(X + A_BYTES, kt, live);
     static_for<0, 16>([&](auto xc) {
         constexpr int x = decltype(xc)::value;
-        q_one<x>(acc, rs, cs, cur);
+        q_one<x, R>(acc, rs, cs, cur);
         static_for<D0 + (x * ND + 15) / 16, D0 + ((x + 1) * ND + 15) / 16>(
             [&](auto dc) { dma_one<CHECKED, LA, decltype(dc)::value>(sa, sb, ca, cb, kt, wave); });
         if constexpr ((x & 1) == 0) nxt.template read_one<core16::frag_order(4, 4, x / 2)>(lds, ks, lane, wm, wn);
@@ -241,26 +249,26 @@ __device__ __forceinline__ void q_kblock_dma(i32x16_t (&acc)[4][4], int (&rs)[4]
 // k-block ahead; the second half of stage kt+1's DMA (into Y) during k-block
 // 0, the barrier after k-block 2, the first half of stage kt+2's DMA (into X)
 // during k-block 3; no data-dependent branches.
-template <bool CHECKED, class SA, class SB, class F>
+template <bool CHECKED, int R, class SA, class SB, class F>
 __device__ __forceinline__ void q_stage(i32x16_t (&acc)[4][4], int (&rs)[4], int (&cs)[4], F& fc, F& fn, char* X,
                                         char* Y, const SA& sa, const SB& sb, int kt, int nk, int lane, int wm, int wn,
                                         int wave) {
     using namespace core16;
     constexpr int LD = SA::PER_WAVE + SB::PER_WAVE, H = LD / 2;
     fence_sched();
-    q_kblock_dma<CHECKED, H, LD>(acc, rs, cs, fc, fn, X, 1, Y, sa, sb, kt + 1, kt + 1 < nk, lane, wm, wn, wave);
-    q_kblock(acc, rs, cs, fn, fc, X, 2, lane, wm, wn);
-    q_kblock(acc, rs, cs, fc, fn, X, 3, lane, wm, wn);
+    q_kblock_dma<CHECKED, R, H, LD>(acc, rs, cs, fc, fn, X, 1, Y, sa, sb, kt + 1, kt + 1 < nk, lane, wm, wn, wave);
+    q_kblock<R>(acc, rs, cs, fn, fc, X, 2, lane, wm, wn);
+    q_kblock<R>(acc, rs, cs, fc, fn, X, 3, lane, wm, wn);
     wait_vm<0>();
     __syncthreads();
     fence_sched();
-    q_kblock_dma<CHECKED, 0, H>(acc, rs, cs, fn, fc, Y, 0, X, sa, sb, kt + 2, kt + 2 < nk, lane, wm, wn, wave);
+    q_kblock_dma<CHECKED, R, 0, H>(acc, rs, cs, fn, fc, Y, 0, X, sa, sb, kt + 2, kt + 2 < nk, lane, wm, wn, wave);
 }
 
 // An odd stage count runs one more stage of zeros (no effect on the products;
 // the sums count its bytes like any other).  On return no DMA is in flight and
 // every wave is done with LDS.
-template <bool AU8, bool BU8, bool CHECKED, class SA, class SB>
+template <bool AU8, bool BU8, bool CHECKED, int R, class SA, class SB>
 __device__ __forceinline__ void qloop_dma(i32x16_t (&acc)[4][4], int (&rs)[4], int (&cs)[4], char* __restrict__ s0,
                                           char* __restrict__ s1, const SA& sa, const SB& sb, int nk, int lane, int wm,
                                           int wn, int wave) {
@@ -279,8 +287,8 @@ __device__ __forceinline__ void qloop_dma(i32x16_t (&acc)[4][4], int (&rs)[4], i
     QFrags<AU8, BU8> fc, fn;
     fc.read(s0, 0, lane, wm, wn);
     for (int kt = 0; kt < nk; kt += 2) {
-        q_stage<CHECKED>(acc, rs, cs, fc, fn, s0, s1, sa, sb, kt, nk, lane, wm, wn, wave);
-        q_stage<CHECKED>(acc, rs, cs, fc, fn, s1, s0, sa, sb, kt + 1, nk, lane, wm, wn, wave);
+        q_stage<CHECKED, R>(acc, rs, cs, fc, fn, s0, s1, sa, sb, kt, nk, lane, wm, wn, wave);
+        q_stage<CHECKED, R>(acc, rs, cs, fc, fn, s1, s0, sa, sb, kt + 1, nk, lane, wm, wn, wave);
     }
     wait_vm<0>();
     __syncthreads();
@@ -483,12 +491,21 @@ __global__ __launch_bounds__(NT) void qlinear_kernel(QArgs p, int tiles_m, int t
         core16::DmaSrcMN8<BNQ> sb;
         sa.init(a, p.lda, m0, M, K, lane);
         sb.init(b, p.ldb, n0, N, K, lane);
+        // the wave's role (which fragments it sums) is a template argument
+        // so that the loop has no role-dependent branches
+        auto run = [&](auto checked) {
+            constexpr bool C = decltype(checked)::value;
+            if ((wm ^ wn) == 0)
+                qloop_dma<AU8, BU8, C, 0>(acc, rs, cs, smem, smem1, sa, sb, nk, lane, wm, wn, wave);
+            else
+                qloop_dma<AU8, BU8, C, 1>(acc, rs, cs, smem, smem1, sa, sb, nk, lane, wm, wn, wave);
+        };
         if constexpr (MODE == 2)
-            qloop_dma<AU8, BU8, false>(acc, rs, cs, smem, smem1, sa, sb, nk, lane, wm, wn, wave);
+            run(std::false_type{});
         else if (m0 + BMQ <= M && n0 + BNQ <= N && K % KB == 0)
-            qloop_dma<AU8, BU8, false>(acc, rs, cs, smem, smem1, sa, sb, nk, lane, wm, wn, wave);
+            run(std::false_type{});
         else
-            qloop_dma<AU8, BU8, true>(acc, rs, cs, smem, smem1, sa, sb, nk, lane, wm, wn, wave);
+            run(std::true_type{});
         nk_run = nk > 0 ? (nk + 1) & ~1 : 0;
     } else {
         QSrc<true, AU8> sa;
@@ -500,20 +517,23 @@ __global__ __launch_bounds__(NT) void qlinear_kernel(QArgs p, int tiles_m, int t
     }
     const uint32_t bias = 128u * 64u * (uint32_t)nk_run;
 
-    // full row / column sums: lanes l and l^32 hold the two k-halves
+    // full row / column sums: lanes l and l^32 hold the two k-halves.  The
+    // DMA loop sums fragments 2R, 2R+1 of each operand in the wave of role
+    // R = wm ^ wn; the register loop sums every fragment in every wave.
     int* rowsum = (int*)smem;        // 256 tile rows
     int* colsum = (int*)smem + 256;  // 256 tile columns
+    const int role = wm ^ wn;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t r = (uint32_t)rs[i] - bias;
         const int rr = (int)(r + (uint32_t)__shfl_xor((int)r, 32));
-        if (wn == 0 && lane < 32) rowsum[wm * 128 + 32 * i + lane] = rr;
+        if ((VEC ? (i >> 1) == role : wn == 0) && lane < 32) rowsum[wm * 128 + 32 * i + lane] = rr;
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const uint32_t c = (uint32_t)cs[j] - bias;
         const int cc = (int)(c + (uint32_t)__shfl_xor((int)c, 32));
-        if (wm == 0 && lane < 32) colsum[wn * 128 + 32 * j + lane] = cc;
+        if ((VEC ? (j >> 1) == role : wm == 0) && lane < 32) colsum[wn * 128 + 32 * j + lane] = cc;
     }
     __syncthreads();
 
