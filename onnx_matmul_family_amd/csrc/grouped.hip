@@ -34,6 +34,12 @@ namespace {
 
 constexpr int ROUTE_THREADS = 1024;
 constexpr int GBM = 256, GBN = 256;  // grouped tile
+// Tile order of the bf16 / fp16 kernel: runs of 8 row tiles (about one
+// expert's rows when tokens spread evenly over the experts) times every column
+// tile, so the 32 tiles an XCD runs at once share about one expert's weight
+// panel and each panel streams from memory about once.  Measured on the
+// 64-expert routing: 1.5 % faster than runs of 4.
+constexpr int ORDER_ROWS = 8;
 constexpr int MAX_G = 8192;          // groups handled by the single-workgroup router
 
 // workspace layout (bytes, from a 256-byte aligned base)
@@ -329,7 +335,7 @@ __global__ __launch_bounds__(256) void grouped16_kernel(GroupedArgs a, const cha
     if (l >= per + (x < extra ? 1 : 0)) return;
     const int w = x * per + min(x, extra) + l;
     int tm, tn;
-    grouped_order(w, ntiles, tiles_n, 4, tm, tn);
+    grouped_order(w, ntiles, tiles_n, ORDER_ROWS, tm, tn);
     grouped_body<DT, VEC>(a, ws, tm, tn, s0, s1, orow_s);
 }
 
