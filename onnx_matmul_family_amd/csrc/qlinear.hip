@@ -170,8 +170,6 @@ __device__ __forceinline__ void qloop(i32x16_t (&acc)[4][4], int (&rs)[4], int (
     }
 }
 
-// int8 MFMA operand fragments of one 32-value k-block (uint8 operands flipped
-// to int8 here: the DMA copies raw bytes).
 // uint8 -> int8 (a - 128) in place; opaque to the compiler so that it keeps
 // one copy of each fragment
 __device__ __forceinline__ void flip(i32x4_t& v) {
@@ -179,48 +177,83 @@ __device__ __forceinline__ void flip(i32x4_t& v) {
     for (int e = 0; e < 4; ++e) asm("v_xor_b32 %0, 0x80808080, %0" : "+v"(v[e]));
 }
 
+// sum of the 4 bytes of v taken as uint8
+__device__ __forceinline__ int bytesum_u8(int v, int acc) {
+    return (int)__builtin_amdgcn_sad_u8((uint32_t)v, 0u, (uint32_t)acc);
+}
+
+// int8 MFMA operand fragments of one 32-value k-block, ids 0-3: a, 4-7: b.
+// The DMA copies uint8 operands as they are; a uint8 fragment is flipped to
+// int8 (flip_one) at its first use, one MFMA ahead: b j is first used by MFMA
+// j, a i by MFMA 4i, and their reads went out a k-block earlier, so no flip
+// waits on LDS.
 template <bool AU8, bool BU8>
 struct QFrags {
+    static constexpr bool A_U8 = AU8;
     i32x4_t a[4], b[4];
     template <int R>
     __device__ __forceinline__ void read_one(const char* st, int ks, int lane, int wm, int wn) {
-        if constexpr (R < 4) {
+        if constexpr (R < 4)
             a[R] = frag_a(st, wm * 128 + 32 * R, ks, lane);
+        else
+            b[R - 4] = frag_b(st, wn * 128 + 32 * (R - 4), ks, lane);
+    }
+    template <int R>
+    __device__ __forceinline__ void flip_one() {
+        if constexpr (R < 4) {
             if constexpr (AU8) flip(a[R]);
         } else {
-            b[R - 4] = frag_b(st, wn * 128 + 32 * (R - 4), ks, lane);
             if constexpr (BU8) flip(b[R - 4]);
         }
+    }
+    // the fragments MFMA 0 of the k-block needs
+    __device__ __forceinline__ void flip_first() {
+        flip_one<4>();
+        flip_one<0>();
     }
     __device__ __forceinline__ void read(const char* st, int ks, int lane, int wm, int wn) {
         core16::static_for<0, 8>([&](auto rc) { read_one<decltype(rc)::value>(st, ks, lane, wm, wn); });
     }
 };
 
+// The fragment first used by MFMA x + 1 (other than those of MFMA 0), -1 if none.
+constexpr int first_used_next(int x) {
+    return x == 0 ? 5 : x == 1 ? 6 : x == 2 ? 7 : x == 3 ? 1 : x == 7 ? 2 : x == 11 ? 3 : -1;
+}
+
 // MFMA X of a k-block (tile (X/4, X%4)) plus one dword of the byte sums.
 // The two waves that read the same a-fragments (same wm) have different roles
 // R = wm ^ wn, and so do the two that read the same b-fragments (same wn):
 // a wave sums only a-fragments 2R, 2R+1 (during MFMAs 0-7) and b-fragments
 // 2R, 2R+1 (MFMAs 8-15), so every fragment's bytes are summed once per
-// workgroup, 16 dwords per wave and k-block.
+// workgroup, 16 dwords per wave and k-block.  A uint8 a-fragment not yet
+// flipped (first used after MFMA X) is summed as it is; every other dword is
+// int8 (raw or flipped) and is biased first.  Then the flip of the fragment
+// MFMA X+1 first uses.
 template <int X, int R, class F>
-__device__ __forceinline__ void q_one(i32x16_t (&acc)[4][4], int (&rs)[4], int (&cs)[4], const F& f) {
+__device__ __forceinline__ void q_one(i32x16_t (&acc)[4][4], int (&rs)[4], int (&cs)[4], F& f) {
     acc[X / 4][X % 4] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.b[X % 4], f.a[X / 4], acc[X / 4][X % 4], 0, 0, 0);
     constexpr int I = 2 * R + (X & 7) / 4;
-    if constexpr (X < 8)
-        rs[I] = bytesum1(f.a[I][X % 4], rs[I]);
-    else
-        cs[I] = bytesum1(f.b[I][X % 4], cs[I]);
+    if constexpr (X < 8) {
+        if constexpr (F::A_U8 && 4 * I > X)
+            rs[I] = bytesum_u8(f.a[I][X % 4], rs[I]);
+        else
+            rs[I] = bytesum1(f.a[I][X % 4], rs[I]);
+    } else {
+        cs[I] = bytesum1(f.b[I][X % 4], cs[I]);  // every b-fragment is int8 from MFMA 3 on
+    }
+    if constexpr (first_used_next(X) >= 0) f.template flip_one<first_used_next(X)>();
 }
 
 template <int R, class F>
-__device__ __forceinline__ void q_kblock(i32x16_t (&acc)[4][4], int (&rs)[4], int (&cs)[4], const F& cur, F& nxt,
+__device__ __forceinline__ void q_kblock(i32x16_t (&acc)[4][4], int (&rs)[4], int (&cs)[4], F& cur, F& nxt,
                                          const char* lds, int ks, int lane, int wm, int wn) {
     using namespace core16;
     static_for<0, 16>([&](auto xc) {
         constexpr int x = decltype(xc)::value;
         q_one<x, R>(acc, rs, cs, cur);
         if constexpr ((x & 1) == 0) nxt.template read_one<core16::frag_order(4, 4, x / 2)>(lds, ks, lane, wm, wn);
+        if constexpr (x == 15) nxt.flip_first();
         fence_sched();
     });
 }
@@ -229,7 +262,7 @@ __device__ __forceinline__ void q_kblock(i32x16_t (&acc)[4][4], int (&rs)[4], in
 // and this wave's DMA instructions D0 .. D1-1 of stage kt (into buffer X)
 // spread evenly between the MFMAs.
 template <bool CHECKED, int R, int D0, int D1, class F, class SA, class SB>
-__device__ __forceinline__ void q_kblock_dma(i32x16_t (&acc)[4][4], int (&rs)[4], int (&cs)[4], const F& cur, F& nxt,
+__device__ __forceinline__ void q_kblock_dma(i32x16_t (&acc)[4][4], int (&rs)[4], int (&cs)[4], F& cur, F& nxt,
                                              const char* lds, int ks, char* X, const SA& sa, const SB& sb, int kt,
                                              bool live, int lane, int wm, int wn, int wave) {
     using namespace core16;
@@ -241,6 +274,7 @@ __device__ __forceinline__ void q_kblock_dma(i32x16_t (&acc)[4][4], int (&rs)[4]
         static_for<D0 + (x * ND + 15) / 16, D0 + ((x + 1) * ND + 15) / 16>(
             [&](auto dc) { dma_one<CHECKED, LA, decltype(dc)::value>(sa, sb, ca, cb, kt, wave); });
         if constexpr ((x & 1) == 0) nxt.template read_one<core16::frag_order(4, 4, x / 2)>(lds, ks, lane, wm, wn);
+        if constexpr (x == 15) nxt.flip_first();
         fence_sched();
     });
 }
@@ -286,6 +320,7 @@ __device__ __forceinline__ void qloop_dma(i32x16_t (&acc)[4][4], int (&rs)[4], i
     __syncthreads();
     QFrags<AU8, BU8> fc, fn;
     fc.read(s0, 0, lane, wm, wn);
+    fc.flip_first();
     for (int kt = 0; kt < nk; kt += 2) {
         q_stage<CHECKED, R>(acc, rs, cs, fc, fn, s0, s1, sa, sb, kt, nk, lane, wm, wn, wave);
         q_stage<CHECKED, R>(acc, rs, cs, fc, fn, s1, s0, sa, sb, kt + 1, nk, lane, wm, wn, wave);
