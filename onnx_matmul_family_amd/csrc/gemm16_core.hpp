@@ -642,13 +642,14 @@ __device__ __forceinline__ void mainloop_dma(f32x16_t (&acc)[BM / 64][BN / 64], 
 // (this wave's 32 KiB: row-major, 256 bytes per row, 16-byte chunk c of row r
 // in slot c ^ (r % 16)), then read back as 16-byte lanes, 16 lanes per row,
 // and stored to rowp(r) (the block row's first column; nullptr skips the row)
-// so that every store instruction writes 4 whole 256-byte row segments.
+// so that every store instruction writes 4 whole 256-byte row segments
+// (store(k, r, c, d): lane chunk c of row r, the k-th of the lane's 32 rows).
 // BIAS: bias holds the block's 128 column values; otherwise no term is added
 // (not even beta * 0).  The caller has synchronised the workgroup since the
 // last read of `stage` as a K buffer.
-template <int DT, bool BIAS, class RowPtr>
-__device__ __forceinline__ void wave_epilogue_lds(const f32x16_t (&acc)[4][4], float alpha, const uint16_t* bias,
-                                                  float beta, char* stage, int lane, RowPtr&& rowp) {
+template <int DT, bool BIAS, class StoreRow>
+__device__ __forceinline__ void wave_epilogue_lds_f(const f32x16_t (&acc)[4][4], float alpha, const uint16_t* bias,
+                                                    float beta, char* stage, int lane, StoreRow&& store) {
     constexpr int ROWB = 256, NCH = 16;
     const int h = lane >> 5;
     // the bias stays packed (two 16-bit values per register) until its column
@@ -693,9 +694,17 @@ __device__ __forceinline__ void wave_epilogue_lds(const f32x16_t (&acc)[4][4], f
     for (int k = 0; k < 32; ++k) {
         const int r = 4 * k + (lane >> 4), c = lane & 15;
         const u32x4_t d = *(const u32x4_t*)(stage + r * ROWB + ((c ^ (r % NCH)) << 4));
+        store(k, r, c, d);
+    }
+}
+// ... storing row r to rowp(r) (its first column; nullptr skips the row)
+template <int DT, bool BIAS, class RowPtr>
+__device__ __forceinline__ void wave_epilogue_lds(const f32x16_t (&acc)[4][4], float alpha, const uint16_t* bias,
+                                                  float beta, char* stage, int lane, RowPtr&& rowp) {
+    wave_epilogue_lds_f<DT, BIAS>(acc, alpha, bias, beta, stage, lane, [&](int, int r, int c, const u32x4_t& d) {
         uint16_t* dst = rowp(r);
         if (dst) *(u32x4_t*)(dst + 8 * c) = d;
-    }
+    });
 }
 
 }  // namespace core16

@@ -254,7 +254,7 @@ __device__ __forceinline__ void grouped_epilogue(const f32x16_t (&acc)[4][4], co
 // rows / columns / K with zeros); otherwise element-wise register-staged loads.
 template <int DT, bool VEC>
 __device__ __forceinline__ void grouped_body(const GroupedArgs& a, const char* ws, int tile, int tn, char* s0,
-                                             char* s1, int* orow_s) {
+                                             char* s1, int* orow_s, uint32_t* roff_s, uint16_t* bias_s) {
     const int4 te = ((const int4*)(ws + off_tiles(a.G)))[tile];
     const int g = te.x, start = te.y, rows = te.z;
     const int* sorted = (const int*)(ws + off_sorted(a.M * a.S, a.G));
@@ -273,7 +273,21 @@ __device__ __forceinline__ void grouped_body(const GroupedArgs& a, const char* w
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     const int nk = (int)((K + KSTEP - 1) / KSTEP);
     const uint16_t* wg = (const uint16_t*)a.weights + (int64_t)g * K * N;
-    if (t < GBM) orow_s[t] = t < rows ? sorted[start + t] : -1;
+    const int srow = t < rows ? sorted[start + t] : -1;  // output row (token * S + slot) of tile row t
+    orow_s[t] = srow;
+    // Whole-tile epilogue with 32-bit row offsets: the tile's bias columns and
+    // its output row byte offsets are staged in LDS now, so the epilogue
+    // neither waits on global loads nor branches per row.  Row r of wave
+    // block wm goes to roff_s[128 wm + 32 (r % 4) + r / 4 % 32]: the 32 rows a
+    // lane stores are contiguous.
+    const bool fast = VEC && n0 + GBN <= N && N % 8 == 0 && ((uintptr_t)a.output & 15) == 0 &&
+                      (int64_t)a.M * S * N * 2 < (1LL << 31);
+    if (fast) {
+        const int rr = t & 127;
+        roff_s[(t & 128) + 32 * (rr & 3) + (rr >> 2)] = srow >= 0 ? (uint32_t)srow * (uint32_t)(N * 2) : DMA_OOB;
+        if (a.bias && t < GBN / 4)
+            *(u32x2_t*)(bias_s + 4 * t) = *(const u32x2_t*)((const uint16_t*)a.bias + (int64_t)g * N + n0 + 4 * t);
+    }
 
     if constexpr (VEC) {
         GatherDma<GBM> srcA;
@@ -316,6 +330,37 @@ __device__ __forceinline__ void grouped_body(const GroupedArgs& a, const char* w
         mainloop<GBM, GBN, DT, true, false, 2>(acc, s0, s1, srcA, srcB, nk, t, lane, wm, wn);
     }
 
+    if (fast) {
+        __syncthreads();  // every wave is done reading the last stage
+        char* stage = (wave < 2 ? s0 : s1) + (wave & 1) * (GBM * KSTEP * 2);
+        // the base made visibly wave-uniform, so that the resource sits in
+        // scalar registers (no per-lane loop around the stores)
+        const uint64_t ob = (uint64_t)((uint16_t*)a.output + n0 + wn * (GBN / 2));
+        const uint64_t obu = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)ob) |
+                             ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(ob >> 32)) << 32);
+        const __amdgpu_buffer_rsrc_t out =
+            __builtin_amdgcn_make_buffer_rsrc((void*)obu, (short)0, 0x7fffffff, 0x00020000);
+        uint32_t ro[32];
+        const u32x4_t* rw = (const u32x4_t*)(roff_s + 128 * wm + 32 * (lane >> 4));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const u32x4_t v = rw[i];
+            ro[4 * i] = v.x;
+            ro[4 * i + 1] = v.y;
+            ro[4 * i + 2] = v.z;
+            ro[4 * i + 3] = v.w;
+        }
+        // rows past the tile's valid rows carry an offset beyond the buffer's
+        // range: their stores are dropped
+        auto st = [&](int k, int, int c, const u32x4_t& d) {
+            __builtin_amdgcn_raw_buffer_store_b128(d, out, (int)(ro[k] + 16 * c), 0, 0);
+        };
+        if (a.bias)
+            wave_epilogue_lds_f<DT, true>(acc, 1.0f, bias_s + wn * (GBN / 2), 1.0f, stage, lane, st);
+        else
+            wave_epilogue_lds_f<DT, false>(acc, 1.0f, nullptr, 1.0f, stage, lane, st);
+        return;
+    }
     grouped_epilogue<DT, VEC>(acc, a, g, rows, start, sorted, n0, lane, wave, s0, s1, orow_s);
 }
 
@@ -324,6 +369,8 @@ __global__ __launch_bounds__(256) void grouped16_kernel(GroupedArgs a, const cha
     __shared__ __attribute__((aligned(1024))) char s0[(GBM + GBN) * core16::KSTEP * 2];
     __shared__ __attribute__((aligned(1024))) char s1[(GBM + GBN) * core16::KSTEP * 2];
     __shared__ int orow_s[GBM];
+    __shared__ __attribute__((aligned(16))) uint32_t roff_s[GBM];
+    __shared__ __attribute__((aligned(16))) uint16_t bias_s[GBN];
     // The grid is sized for the most row tiles any routing can produce; the
     // routed count is known only here.  Workgroup b runs on XCD b % 8, so the
     // routed tiles are split evenly over the 8 XCDs (each takes one contiguous
@@ -336,7 +383,7 @@ __global__ __launch_bounds__(256) void grouped16_kernel(GroupedArgs a, const cha
     const int w = x * per + min(x, extra) + l;
     int tm, tn;
     grouped_order(w, ntiles, tiles_n, ORDER_ROWS, tm, tn);
-    grouped_body<DT, VEC>(a, ws, tm, tn, s0, s1, orow_s);
+    grouped_body<DT, VEC>(a, ws, tm, tn, s0, s1, orow_s, roff_s, bias_s);
 }
 
 // ---------------------------------------------------------------------------
