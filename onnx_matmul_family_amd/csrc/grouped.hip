@@ -856,6 +856,67 @@ __device__ __forceinline__ void grouped_epilogue_blocks(const f32x16_t (&acc)[TM
     }
 }
 
+// Epilogue of the 1x4 wave layout (each wave: all 256 rows, 64 columns) for a
+// tile wholly inside the output with 32-bit row offsets: the bias columns
+// (bias_s, the tile's 256) and the output row byte offsets (roff_s, row r at
+// 32 (r % 8) + r / 8, so the 32 rows a lane stores are contiguous; rows past
+// the tile's valid rows hold an offset beyond the buffer's range and their
+// stores are dropped) were staged in LDS at tile start.  Each wave converts
+// its block into its 32 KiB of `stage` (row r: 128 bytes, 16-byte chunk c in
+// slot c ^ (r % 8)) and stores whole 128-byte row segments, 8 rows per
+// instruction.
+template <int DT>
+__device__ __forceinline__ void dq_epilogue_lds(const f32x16_t (&acc)[8][2], const GroupedArgs& a, int64_t n0,
+                                                int col0, int lane, int wave, char* stage, const uint32_t* roff_s,
+                                                const uint16_t* bias_s) {
+    const int h = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (a.bias) {
+                const u32x2_t b2 = *(const u32x2_t*)(bias_s + col0 + 32 * j + 8 * q + 4 * h);
+                bv[0] = from_bits<DT>((uint16_t)b2.x);
+                bv[1] = from_bits<DT>((uint16_t)(b2.x >> 16));
+                bv[2] = from_bits<DT>((uint16_t)b2.y);
+                bv[3] = from_bits<DT>((uint16_t)(b2.y >> 16));
+            }
+            const int c = 4 * j + q;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int r = 32 * i + (lane & 31);
+                u32x2_t o;
+                o.x = pack2<DT>(acc[i][j][4 * q + 0] + bv[0], acc[i][j][4 * q + 1] + bv[1]);
+                o.y = pack2<DT>(acc[i][j][4 * q + 2] + bv[2], acc[i][j][4 * q + 3] + bv[3]);
+                *(u32x2_t*)(stage + r * 128 + ((c ^ (r & 7)) << 4) + 8 * h) = o;
+            }
+        }
+    }
+    uint32_t ro[32];
+    const u32x4_t* rw = (const u32x4_t*)(roff_s + 32 * (lane >> 3));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const u32x4_t v = rw[i];
+        ro[4 * i] = v.x;
+        ro[4 * i + 1] = v.y;
+        ro[4 * i + 2] = v.z;
+        ro[4 * i + 3] = v.w;
+    }
+    // the base made visibly wave-uniform, so that the resource sits in scalar registers
+    const uint64_t ob = (uint64_t)((uint16_t*)a.output + n0 + 64 * wave);
+    const uint64_t obu = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)ob) |
+                         ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(ob >> 32)) << 32);
+    const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc((void*)obu, (short)0, 0x7fffffff, 0x00020000);
+    const int c = lane & 7;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+        const int r = 8 * k + (lane >> 3);
+        const u32x4_t d = *(const u32x4_t*)(stage + r * 128 + ((c ^ (r & 7)) << 4));
+        __builtin_amdgcn_raw_buffer_store_b128(d, out, (int)(ro[k] + 16 * c), 0, 0);
+    }
+}
+
 // Weights by DMA: K % 64 == 0, N % 16 == 0, 16-byte aligned q, scale and
 // zero-point rows (16-byte aligned bases), block size a multiple of 64 (one
 // block per stage).
@@ -864,6 +925,8 @@ __global__ __launch_bounds__(256) void grouped16_dq_dma_kernel(GroupedArgs a, co
     __shared__ __attribute__((aligned(1024))) char s0[(GBM + GBN) * core16::KSTEP * 2];
     __shared__ __attribute__((aligned(1024))) char s1[(GBM + GBN) * core16::KSTEP * 2];
     __shared__ int orow_s[GBM];
+    __shared__ __attribute__((aligned(16))) uint32_t roff_s[GBM];
+    __shared__ __attribute__((aligned(16))) uint16_t bias_s[GBN];
     using namespace core16;
     const int ntiles = ((const int*)ws)[0];
     const int total = ntiles * tiles_n;
@@ -890,7 +953,15 @@ __global__ __launch_bounds__(256) void grouped16_dq_dma_kernel(GroupedArgs a, co
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     const int nk = (int)(K / KSTEP);
-    if (t < GBM) orow_s[t] = t < rows ? sorted[start + t] : -1;
+    const int srow = t < rows ? sorted[start + t] : -1;  // output row of tile row t
+    orow_s[t] = srow;
+    const bool fast = n0 + GBN <= N && N % 8 == 0 && ((uintptr_t)a.output & 15) == 0 &&
+                      (!a.bias || ((uintptr_t)a.bias & 7) == 0) && (int64_t)a.M * S * N * 2 < (1LL << 31);
+    if (fast) {
+        roff_s[32 * (t & 7) + (t >> 3)] = srow >= 0 ? (uint32_t)srow * (uint32_t)(N * 2) : DMA_OOB;
+        if (a.bias && t < GBN / 4)
+            *(u32x2_t*)(bias_s + 4 * t) = *(const u32x2_t*)((const uint16_t*)a.bias + (int64_t)g * N + n0 + 4 * t);
+    }
 
     GatherDma<GBM> srcA;
     srcA.base = (const char*)a.input;
@@ -912,8 +983,12 @@ __global__ __launch_bounds__(256) void grouped16_dq_dma_kernel(GroupedArgs a, co
     prm.bs = a.bs;
     prm.n0 = n0;
     mainloop_dq_dma<DT, QU8, TM, TN>(acc, s0, s1, srcA, srcB, prm, nk, lane, row0, col0, wave);
-    __syncthreads();  // orow_s complete even when the K loop ran no stage (K = 0)
-    grouped_epilogue_blocks<DT, TM, TN>(acc, a, g, n0, row0, col0, lane, orow_s);
+    __syncthreads();  // the LDS tables complete even when the K loop ran no stage (K = 0); stages free
+    if (fast)
+        dq_epilogue_lds<DT>(acc, a, n0, col0, lane, wave, (wave < 2 ? s0 : s1) + (wave & 1) * (GBM * 128), roff_s,
+                            bias_s);
+    else
+        grouped_epilogue_blocks<DT, TM, TN>(acc, a, g, n0, row0, col0, lane, orow_s);
 }
 
 template <int DT, bool QU8, bool FAST>
