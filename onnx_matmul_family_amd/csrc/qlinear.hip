@@ -220,6 +220,19 @@ struct QFrags {
 constexpr int first_used_next(int x) {
     return x == 0 ? 5 : x == 1 ? 6 : x == 2 ? 7 : x == 3 ? 1 : x == 7 ? 2 : x == 11 ? 3 : -1;
 }
+// MFMA X uses a-fragment X / 4 and b-fragment X % 4 (q_one): fragment f is
+// first used by MFMA 4f (a) or f - 4 (b); check the table against that.
+constexpr bool flip_table_ok() {
+    for (int f = 0; f < 8; ++f) {
+        const int use = f < 4 ? 4 * f : f - 4;
+        int flips = 0;
+        for (int x = 0; x < 15; ++x)
+            if (first_used_next(x) == f) flips += (x + 1 == use) ? 1 : 100;
+        if (flips != (use == 0 ? 0 : 1)) return false;  // MFMA 0's fragments: flip_first
+    }
+    return true;
+}
+static_assert(flip_table_ok(), "each uint8 fragment is flipped right before its first MFMA");
 
 // MFMA X of a k-block (tile (X/4, X%4)) plus one dword of the byte sums.
 // The two waves that read the same a-fragments (same wm) have different roles
