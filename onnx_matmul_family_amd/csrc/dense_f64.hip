@@ -5,8 +5,12 @@
 // (alpha and beta are the operator's float attributes, taken exactly).  Structure:
 // any layout and extents, element loads with range checks, one 128x128
 // output tile per workgroup of 4 waves (each wave 64x64 as 4x4 MFMA tiles of
-// 16x16), K staged through two LDS buffers 16 values at a time with the next
-// stage's loads in flight during the current stage's MFMAs.
+// 16x16), K staged through three LDS buffers 16 values at a time.  Stage k+2
+// is loaded into registers while stage k multiplies and stored to LDS at the
+// end of stage k (into the buffer stage k-1 left), so stage k+1 has been in
+// LDS for a whole stage when it starts: its first fragments are read before
+// the stage barrier and the MFMAs run across it.  Within a stage the fragments
+// of the next 4-deep k step are read while the current one multiplies.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -18,22 +22,49 @@ typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int T = 128;   // output tile edge (4 waves of 64 x 64)
 constexpr int KS = 16;   // k per stage
+constexpr int NB = 3;    // LDS stage buffers
 constexpr int PAD = 130; // LDS row stride (doubles)
 constexpr int NL = T * KS / 256;  // elements per thread per operand and stage
 
-// Element loads of one operand's stage (KS x T values), the contiguous dim of
-// the stored operand across consecutive threads; zeros outside the matrix.
-__device__ __forceinline__ void f64_load(double (&r)[NL], const double* X, int64_t ld, bool kmajor, int64_t mn0,
-                                         int64_t MN, int64_t k0, int64_t K, int t) {
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-        int kk, mm;
-        if (kmajor) { kk = t & 15; mm = (t >> 4) + 16 * i; }
-        else { mm = t & 127; kk = (t >> 7) + 2 * i; }
-        const int64_t m = mn0 + mm, k = k0 + kk;
-        r[i] = (m < MN && k < K) ? (kmajor ? X[m * ld + k] : X[k * ld + m]) : 0.0;
+// One operand's element loads: thread t owns NL elements of each stage (the
+// contiguous dim of the stored operand across consecutive threads); zeros
+// outside the matrix.  Addresses advance by a fixed step per stage.
+struct F64Src {
+    const double* p;   // element 0 of this thread at stage 0
+    int64_t si;        // distance between the thread's elements
+    int64_t step;      // advance per stage
+    int64_t mn_first, k_first, MN, K;
+    bool kmajor;
+    __device__ void init(const double* X, int64_t ld, bool km, int64_t mn0, int64_t MN_, int64_t K_, int t) {
+        kmajor = km;
+        MN = MN_;
+        K = K_;
+        if (km) {  // element i: k = t % 16, m/n = t / 16 + 16 i
+            k_first = t & 15;
+            mn_first = mn0 + (t >> 4);
+            p = X + mn_first * ld + k_first;
+            si = 16 * ld;
+            step = KS;
+        } else {   // element i: m/n = t % 128, k = t / 128 + 2 i
+            k_first = t >> 7;
+            mn_first = mn0 + (t & 127);
+            p = X + k_first * ld + mn_first;
+            si = 2 * ld;
+            step = KS * ld;
+        }
     }
-}
+    __device__ __forceinline__ void load(double (&r)[NL], int kt) const {
+        const double* q = p + kt * step;
+        const int64_t k0 = k_first + (int64_t)kt * KS;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int64_t m = kmajor ? mn_first + 16 * i : mn_first;
+            const int64_t k = kmajor ? k0 : k0 + 2 * i;
+            r[i] = (m < MN && k < K) ? q[i * si] : 0.0;
+        }
+    }
+};
+
 __device__ __forceinline__ void f64_store(double (*S)[PAD], const double (&r)[NL], bool kmajor, int t) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
@@ -44,9 +75,28 @@ __device__ __forceinline__ void f64_store(double (*S)[PAD], const double (&r)[NL
     }
 }
 
+// lane l supplies A[m = l%16][k = l/16] and B[k = l/16][n = l%16] of a 4-deep k step
+struct F64Frags {
+    double a[4], b[4];
+    __device__ __forceinline__ void read(const double (*As)[PAD], const double (*Bs)[PAD], int kk, int lane, int wm,
+                                         int wn) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = As[kk + (lane >> 4)][wm * 64 + 16 * i + (lane & 15)];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = Bs[kk + (lane >> 4)][wn * 64 + 16 * j + (lane & 15)];
+    }
+};
+
+__device__ __forceinline__ void f64_mma(f64x4_t (&acc)[4][4], const F64Frags& f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+
 __global__ __launch_bounds__(256) void dense_f64_kernel(DenseArgs p, int tiles_m, int tiles_n) {
-    __shared__ double As[2][KS][PAD];
-    __shared__ double Bs[2][KS][PAD];
+    __shared__ double As[NB][KS][PAD];
+    __shared__ double Bs[NB][KS][PAD];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int tiles = tiles_m * tiles_n;
@@ -67,43 +117,46 @@ __global__ __launch_bounds__(256) void dense_f64_kernel(DenseArgs p, int tiles_m
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f64x4_t{0.0, 0.0, 0.0, 0.0};
 
-    // stage k+1 is loaded into registers while stage k multiplies from LDS
     const int nk = (int)((K + KS - 1) / KS);
+    F64Src sa, sb;
+    sa.init(A, p.lda, ak, m0, M, K, t);
+    sb.init(B, p.ldb, bk, n0, N, K, t);
     double ra[NL], rb[NL];
-    if (nk > 0) {
-        f64_load(ra, A, p.lda, ak, m0, M, 0, K, t);
-        f64_load(rb, B, p.ldb, bk, n0, N, 0, K, t);
-        f64_store(As[0], ra, ak, t);
-        f64_store(Bs[0], rb, bk, t);
+    // stages 0 and 1 into buffers 0 and 1
+    for (int s = 0; s < 2 && s < nk; ++s) {
+        sa.load(ra, s);
+        sb.load(rb, s);
+        f64_store(As[s], ra, ak, t);
+        f64_store(Bs[s], rb, bk, t);
     }
     __syncthreads();
+    F64Frags fc, fn;
+    if (nk > 0) fc.read(As[0], Bs[0], 0, lane, wm, wn);
+    int b0 = 0;  // buffer of stage kt
     for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) {
-            f64_load(ra, A, p.lda, ak, m0, M, (int64_t)(kt + 1) * KS, K, t);
-            f64_load(rb, B, p.ldb, bk, n0, N, (int64_t)(kt + 1) * KS, K, t);
+        const int b1 = b0 == NB - 1 ? 0 : b0 + 1, b2 = b1 == NB - 1 ? 0 : b1 + 1;
+        const bool more = kt + 2 < nk;
+        if (more) {
+            sa.load(ra, kt + 2);
+            sb.load(rb, kt + 2);
         }
-        // lane l supplies A[m = l%16][k = l/16] and B[k = l/16][n = l%16]
-#pragma unroll
-        for (int kk = 0; kk < KS; kk += 4) {
-            double a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = As[buf][kk + (lane >> 4)][wm * 64 + 16 * i + (lane & 15)];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = Bs[buf][kk + (lane >> 4)][wn * 64 + 16 * j + (lane & 15)];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
-        }
-        if (kt + 1 < nk) {
-            f64_store(As[buf ^ 1], ra, ak, t);
-            f64_store(Bs[buf ^ 1], rb, bk, t);
+        fn.read(As[b0], Bs[b0], 4, lane, wm, wn);
+        f64_mma(acc, fc);
+        fc.read(As[b0], Bs[b0], 8, lane, wm, wn);
+        f64_mma(acc, fn);
+        fn.read(As[b0], Bs[b0], 12, lane, wm, wn);
+        f64_mma(acc, fc);
+        // stage kt+1 has been in LDS since the last barrier (junk past the last stage, unused)
+        fc.read(As[b1], Bs[b1], 0, lane, wm, wn);
+        f64_mma(acc, fn);
+        if (more) {
+            // the buffer stage kt-1 used: every wave finished reading it before the last barrier
+            f64_store(As[b2], ra, ak, t);
+            f64_store(Bs[b2], rb, bk, t);
         }
         __syncthreads();
+        b0 = b1;
     }
-
     // result register r of lane l in a 16x16 tile: row l/16 + 4 r, column l%16
     const double* Cp = (const double*)p.C;
     const double alpha = (double)p.alpha, beta = (double)p.beta;

@@ -310,3 +310,19 @@ def test_matmul_split_k_decode_batch_exact():
     assert tuple(Y.shape) == (8, 1, 3072)
     assert np.abs(y).max() < 2048
     assert np.array_equal(host_f64(Y), y)
+
+
+def test_gemm_f64_full_size_sampled():
+    """The fp64 Gemm at its benchmark size (4096^3, B stored (N, K), a C row),
+    in the launch configuration the benchmark times: sampled outputs against
+    the oracle's fp64 sums."""
+    rng = np.random.default_rng(64)
+    n = 4096
+    A = synth.store(synth.normal(rng, (n, n)), "f64")
+    B = synth.store(synth.normal(rng, (n, n)), "f64")
+    C = synth.store(synth.normal(rng, (n,)), "f64")
+    Y = om.gemm(dev(A, "f64"), dev(B, "f64"), dev(C, "f64"), 1.0, 1.0, 0, 1)
+    torch.cuda.synchronize()
+    sel = sample_indices(n * n, 3000, 11)
+    y, t = oracle.gemm(A, B, C, 1.0, 1.0, 0, 1, dt="f64", sel=sel)
+    check_close(host_f64(Y).ravel()[sel], y, t + np.abs(C[sel % n]), "f64", "gemm f64 4096^3 sampled")
