@@ -170,11 +170,13 @@ __device__ __forceinline__ void qloop(i32x16_t (&acc)[4][4], int (&rs)[4], int (
     }
 }
 
-// uint8 -> int8 (a - 128) in place; opaque to the compiler so that it keeps
-// one copy of each fragment
+// uint8 -> int8 (a - 128) in place: the top bit of each byte flipped with the
+// three-input bit operation (table 0x3c: src0 xor src1), which the compiler
+// does not fold into the xor of a later byte sum, so one copy of each
+// fragment stays live
 __device__ __forceinline__ void flip(i32x4_t& v) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) asm("v_xor_b32 %0, 0x80808080, %0" : "+v"(v[e]));
+    for (int e = 0; e < 4; ++e) v[e] = (int)__builtin_amdgcn_bitop3_b32((uint32_t)v[e], 0x80808080u, 0u, 0x3c);
 }
 
 // sum of the 4 bytes of v taken as uint8
@@ -184,9 +186,11 @@ __device__ __forceinline__ int bytesum_u8(int v, int acc) {
 
 // int8 MFMA operand fragments of one 32-value k-block, ids 0-3: a, 4-7: b.
 // The DMA copies uint8 operands as they are; a uint8 fragment is flipped to
-// int8 (flip_one) at its first use, one MFMA ahead: b j is first used by MFMA
-// j, a i by MFMA 4i, and their reads went out a k-block earlier, so no flip
-// waits on LDS.
+// int8 (flip_one) shortly before its first use, at least one MFMA ahead (b j
+// is first used by MFMA j, a i by MFMA 4i): the fragments of MFMAs 0 and 1
+// near the end of the k-block before, the others within their own k-block.
+// Every fragment's read went out a k-block earlier, so no flip waits on LDS,
+// and no MFMA waits on the flip of its operand.
 template <bool AU8, bool BU8>
 struct QFrags {
     static constexpr bool A_U8 = AU8;
@@ -206,33 +210,44 @@ struct QFrags {
             if constexpr (BU8) flip(b[R - 4]);
         }
     }
-    // the fragments MFMA 0 of the k-block needs
+    // the fragments MFMAs 0 and 1 of the k-block need
     __device__ __forceinline__ void flip_first() {
         flip_one<4>();
         flip_one<0>();
+        flip_one<5>();
     }
     __device__ __forceinline__ void read(const char* st, int ks, int lane, int wm, int wn) {
         core16::static_for<0, 8>([&](auto rc) { read_one<decltype(rc)::value>(st, ks, lane, wm, wn); });
     }
 };
 
-// The fragment first used by MFMA x + 1 (other than those of MFMA 0), -1 if none.
-constexpr int first_used_next(int x) {
-    return x == 0 ? 5 : x == 1 ? 6 : x == 2 ? 7 : x == 3 ? 1 : x == 7 ? 2 : x == 11 ? 3 : -1;
+// The fragment flipped right after MFMA x of its k-block, -1 if none (b 2, b 3,
+// a 1, a 2, a 3; flip_first does b 0, a 0, b 1 near the end of the k-block
+// before, after MFMA FLIP_FIRST_AT).
+constexpr int flip_after(int x) { return x == 0 ? 6 : x == 1 ? 7 : x == 2 ? 1 : x == 6 ? 2 : x == 10 ? 3 : -1; }
+constexpr int FLIP_FIRST_AT = 13;
+// MFMA after which fragment f is flipped (-1: in the k-block before)
+constexpr int flipped_after(int f) {
+    for (int x = 0; x < 16; ++x)
+        if (flip_after(x) == f) return x;
+    return -1;
 }
 // MFMA X uses a-fragment X / 4 and b-fragment X % 4 (q_one): fragment f is
-// first used by MFMA 4f (a) or f - 4 (b); check the table against that.
+// first used by MFMA 4f (a) or f - 4 (b); every flip lands at least one MFMA
+// before that, and every fragment is flipped exactly once.
 constexpr bool flip_table_ok() {
     for (int f = 0; f < 8; ++f) {
         const int use = f < 4 ? 4 * f : f - 4;
-        int flips = 0;
-        for (int x = 0; x < 15; ++x)
-            if (first_used_next(x) == f) flips += (x + 1 == use) ? 1 : 100;
-        if (flips != (use == 0 ? 0 : 1)) return false;  // MFMA 0's fragments: flip_first
+        int n = 0;
+        for (int x = 0; x < 16; ++x) n += flip_after(x) == f;
+        const bool first = f == 4 || f == 0 || f == 5;
+        if (n + (first ? 1 : 0) != 1) return false;
+        if (!first && flipped_after(f) > use - 2) return false;
+        if (first && use > 1) return false;
     }
-    return true;
+    return FLIP_FIRST_AT < 15;
 }
-static_assert(flip_table_ok(), "each uint8 fragment is flipped right before its first MFMA");
+static_assert(flip_table_ok(), "each uint8 fragment is flipped once, at least one MFMA before its first use");
 
 // MFMA X of a k-block (tile (X/4, X%4)) plus one dword of the byte sums.
 // The two waves that read the same a-fragments (same wm) have different roles
@@ -240,22 +255,22 @@ static_assert(flip_table_ok(), "each uint8 fragment is flipped right before its 
 // a wave sums only a-fragments 2R, 2R+1 (during MFMAs 0-7) and b-fragments
 // 2R, 2R+1 (MFMAs 8-15), so every fragment's bytes are summed once per
 // workgroup, 16 dwords per wave and k-block.  A uint8 a-fragment not yet
-// flipped (first used after MFMA X) is summed as it is; every other dword is
-// int8 (raw or flipped) and is biased first.  Then the flip of the fragment
-// MFMA X+1 first uses.
+// flipped is summed as it is; every other dword is int8 (raw or flipped) and
+// is biased first.  Then the flip scheduled after MFMA X.
 template <int X, int R, class F>
 __device__ __forceinline__ void q_one(i32x16_t (&acc)[4][4], int (&rs)[4], int (&cs)[4], F& f) {
     acc[X / 4][X % 4] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.b[X % 4], f.a[X / 4], acc[X / 4][X % 4], 0, 0, 0);
     constexpr int I = 2 * R + (X & 7) / 4;
     if constexpr (X < 8) {
-        if constexpr (F::A_U8 && 4 * I > X)
+        if constexpr (F::A_U8 && flipped_after(I) >= X)
             rs[I] = bytesum_u8(f.a[I][X % 4], rs[I]);
         else
             rs[I] = bytesum1(f.a[I][X % 4], rs[I]);
     } else {
-        cs[I] = bytesum1(f.b[I][X % 4], cs[I]);  // every b-fragment is int8 from MFMA 3 on
+        static_assert(X < 8 || flipped_after(4 + (2 * R + (X & 7) / 4)) < 8, "b-fragments are int8 when summed");
+        cs[I] = bytesum1(f.b[I][X % 4], cs[I]);
     }
-    if constexpr (first_used_next(X) >= 0) f.template flip_one<first_used_next(X)>();
+    if constexpr (flip_after(X) >= 0) f.template flip_one<flip_after(X)>();
 }
 
 template <int R, class F>
@@ -266,7 +281,7 @@ __device__ __forceinline__ void q_kblock(i32x16_t (&acc)[4][4], int (&rs)[4], in
         constexpr int x = decltype(xc)::value;
         q_one<x, R>(acc, rs, cs, cur);
         if constexpr ((x & 1) == 0) nxt.template read_one<core16::frag_order(4, 4, x / 2)>(lds, ks, lane, wm, wn);
-        if constexpr (x == 15) nxt.flip_first();
+        if constexpr (x == FLIP_FIRST_AT) nxt.flip_first();
         fence_sched();
     });
 }
@@ -287,7 +302,7 @@ __device__ __forceinline__ void q_kblock_dma(i32x16_t (&acc)[4][4], int (&rs)[4]
         static_for<D0 + (x * ND + 15) / 16, D0 + ((x + 1) * ND + 15) / 16>(
             [&](auto dc) { dma_one<CHECKED, LA, decltype(dc)::value>(sa, sb, ca, cb, kt, wave); });
         if constexpr ((x & 1) == 0) nxt.template read_one<core16::frag_order(4, 4, x / 2)>(lds, ks, lane, wm, wn);
-        if constexpr (x == 15) nxt.flip_first();
+        if constexpr (x == FLIP_FIRST_AT) nxt.flip_first();
         fence_sched();
     });
 }
