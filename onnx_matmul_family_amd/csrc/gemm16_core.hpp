@@ -707,5 +707,180 @@ __device__ __forceinline__ void wave_epilogue_lds(const f32x16_t (&acc)[4][4], f
     });
 }
 
+
+// ---------------------------------------------------------------------------
+// 16x16x32 form of the K loop (both operands k-major).  Each wave's 128 x 128
+// sub-tile is 8 x 8 MFMA tiles of 16 x 16; a 64-k stage is two k-blocks of 32,
+// each 64 MFMAs.  Operand fragment of rows [mnb, mnb+16), k-block s: lane l
+// gets mn = mnb + l%16, k = 32 s + 8 (l/16) + 0..7 (one swizzled chunk).
+//
+// The MFMAs are issued from inline assembly with the accumulator tied to its
+// AGPRs: with 64 separate 4-register accumulators filling the AGPR file the
+// compiler picks the untied MFMA form for some of them and then shuffles
+// accumulators between register files every iteration (measured: ~150 move
+// instructions per two stages and a 10 % slower kernel).  The compiler does
+// not see inside the assembly, so the hazards it would guard are fenced by
+// hand: the first k-block writes the accumulators with C = 0 instead of
+// reading zeroed registers, and acc_fence (a few wait states, with every
+// accumulator as an operand so that no read moves above it) separates the
+// last MFMA from the first read of its result.
+// Z: the first k-block, C = 0 (the accumulators are never zeroed by VALU
+// writes, which an MFMA must not read too soon after).
+template <int DT, bool Z>
+__device__ __forceinline__ void mfma16_tied(f32x4_t& acc, const u32x4_t& a, const u32x4_t& b) {
+    if constexpr (Z && DT == 0)
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+    else if constexpr (Z)
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+    else if constexpr (DT == 0)
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    else
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+template <int TM>
+__device__ __forceinline__ void acc_fence(f32x4_t (&acc)[TM][8]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"
+                     : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
+                       "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
+}
+__device__ __forceinline__ u32x4_t read_frag16k(const char* lds, int mnb, int s, int lane) {
+    const int r = lane & 15, c = 4 * s + (lane >> 4);
+    return *(const u32x4_t*)(lds + (mnb + r) * 128 + ((c ^ kswz(r)) << 4));
+}
+template <int BM, int BN>
+struct Frags16 {
+    static constexpr int TM = BM / 32, TN = BN / 32;
+    u32x4_t a[TM], b[TN];
+    template <int R>
+    __device__ __forceinline__ void read_one(const char* st, int s, int lane, int wm, int wn) {
+        constexpr int A_BYTES = BM * KSTEP * 2;
+        if constexpr (R < TM)
+            a[R] = read_frag16k(st, wm * (BM / 2) + 16 * R, s, lane);
+        else
+            b[R - TM] = read_frag16k(st + A_BYTES, wn * (BN / 2) + 16 * (R - TM), s, lane);
+    }
+    __device__ __forceinline__ void read(const char* st, int s, int lane, int wm, int wn) {
+        static_for<0, TM + TN>([&](auto rc) { read_one<decltype(rc)::value>(st, s, lane, wm, wn); });
+    }
+};
+
+// One 32-k block of MFMAs on `cur`; the fragment reads of k-block s of `lds`
+// into `nxt` and (D1 > D0) this wave's DMA instructions D0 .. D1-1 of stage kt
+// into buffer X, each spread evenly over the MFMAs.
+template <int DT, int TM, int TN, bool CHECKED, int D0, int D1, bool Z, class F, class SA, class SB>
+__device__ __forceinline__ void kblock16(f32x4_t (&acc)[TM][TN], const F& cur, F& nxt, const char* lds, int s,
+                                         char* X, int A_BYTES, const SA& srcA, const SB& srcB, int kt, bool live,
+                                         int lane, int wm, int wn, int wave) {
+    constexpr int NM = TM * TN, NR = TM + TN, ND = D1 - D0;
+    constexpr int LA = SA::PER_WAVE;
+    DmaCtx ca, cb;
+    if constexpr (ND > 0) {
+        ca = srcA.ctx(X, kt, live);
+        cb = srcB.ctx(X + A_BYTES, kt, live);
+    }
+    static_for<0, NM>([&](auto xc) {
+        constexpr int x = decltype(xc)::value;
+        mfma16_tied<DT, Z>(acc[x / TN][x % TN], cur.b[x % TN], cur.a[x / TN]);
+        if constexpr (ND > 0)
+            static_for<D0 + (x * ND + NM - 1) / NM, D0 + ((x + 1) * ND + NM - 1) / NM>(
+                [&](auto dc) { dma_one<CHECKED, LA, decltype(dc)::value>(srcA, srcB, ca, cb, kt, wave); });
+        static_for<(x * NR + NM - 1) / NM, ((x + 1) * NR + NM - 1) / NM>([&](auto rc) {
+            nxt.template read_one<frag_order(TM, TN, decltype(rc)::value)>(lds, s, lane, wm, wn);
+        });
+        fence_sched();
+    });
+}
+
+// One stage: k-block 0 (reads of k-block 1 of X), the barrier that retires X
+// and publishes Y (stage kt+1, whose DMA went out a whole k-block earlier),
+// k-block 1 (reads of Y's k-block 0, stage kt+2's DMA into X).
+template <int BM, int BN, int DT, bool CHECKED, bool Z, class SA, class SB, class F>
+__device__ __forceinline__ void dma_stage16(f32x4_t (&acc)[BM / 32][BN / 32], F& fc, F& fn, char* X, char* Y,
+                                            const SA& srcA, const SB& srcB, int kt, int nk, int lane, int wm, int wn,
+                                            int wave) {
+    constexpr int A_BYTES = BM * KSTEP * 2;
+    constexpr int LD = SA::PER_WAVE + SB::PER_WAVE;
+    constexpr int TM = BM / 32, TN = BN / 32;
+    fence_sched();
+    kblock16<DT, TM, TN, CHECKED, 0, 0, Z>(acc, fc, fn, X, 1, X, A_BYTES, srcA, srcB, kt, false, lane, wm, wn, wave);
+    wait_vm<0>();
+    __syncthreads();
+    fence_sched();
+    kblock16<DT, TM, TN, CHECKED, 0, LD, false>(acc, fn, fc, Y, 0, X, A_BYTES, srcA, srcB, kt + 2, kt + 2 < nk, lane, wm, wn,
+                                         wave);
+}
+
+template <int BM, int BN, int DT, bool CHECKED, class SA, class SB>
+__device__ __forceinline__ void mainloop_dma16(f32x4_t (&acc)[BM / 32][BN / 32], char* __restrict__ s0,
+                                               char* __restrict__ s1, const SA& srcA, const SB& srcB, int nk, int lane,
+                                               int wm, int wn, int wave) {
+    constexpr int A_BYTES = BM * KSTEP * 2;
+    constexpr int LA = SA::PER_WAVE, LD = SA::PER_WAVE + SB::PER_WAVE;
+    // nk >= 1: the first two stages run unconditionally
+    {
+        const DmaCtx a0 = srcA.ctx(s0, 0, true), b0 = srcB.ctx(s0 + A_BYTES, 0, true);
+        static_for<0, LD>([&](auto dc) { dma_one<CHECKED, LA, decltype(dc)::value>(srcA, srcB, a0, b0, 0, wave); });
+        const DmaCtx a1 = srcA.ctx(s1, 1, nk > 1), b1 = srcB.ctx(s1 + A_BYTES, 1, nk > 1);
+        static_for<0, LD>([&](auto dc) { dma_one<CHECKED, LA, decltype(dc)::value>(srcA, srcB, a1, b1, 1, wave); });
+    }
+    wait_vm<LD>();
+    __syncthreads();
+    Frags16<BM, BN> fc, fn;
+    fc.read(s0, 0, lane, wm, wn);
+    dma_stage16<BM, BN, DT, CHECKED, true>(acc, fc, fn, s0, s1, srcA, srcB, 0, nk, lane, wm, wn, wave);
+    dma_stage16<BM, BN, DT, CHECKED, false>(acc, fc, fn, s1, s0, srcA, srcB, 1, nk, lane, wm, wn, wave);
+    for (int kt = 2; kt < nk; kt += 2) {
+        dma_stage16<BM, BN, DT, CHECKED, false>(acc, fc, fn, s0, s1, srcA, srcB, kt, nk, lane, wm, wn, wave);
+        dma_stage16<BM, BN, DT, CHECKED, false>(acc, fc, fn, s1, s0, srcA, srcB, kt + 1, nk, lane, wm, wn, wave);
+    }
+    wait_vm<0>();
+    acc_fence(acc);
+}
+
+// Epilogue of one wave's 128 x 128 block in the 16x16 accumulator layout
+// (tile (i, j), register e of lane l: row 16 i + l%16, column 16 j + 4 (l/16) + e),
+// through the same LDS staging and row-segment stores as wave_epilogue_lds_f.
+template <int DT, bool BIAS, class StoreRow>
+__device__ __forceinline__ void wave_epilogue_lds16(const f32x4_t (&acc)[8][8], float alpha, const uint16_t* bias,
+                                                    float beta, char* stage, int lane, StoreRow&& store) {
+    constexpr int ROWB = 256, NCH = 16;
+    const int g = lane >> 4, h = g & 1;
+    u32x2_t craw[8];
+    if constexpr (BIAS) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) craw[j] = *(const u32x2_t*)(bias + 16 * j + 4 * g);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        float cb[4];
+        if constexpr (BIAS) {
+            cb[0] = beta * from_bits<DT>((uint16_t)craw[j].x);
+            cb[1] = beta * from_bits<DT>((uint16_t)(craw[j].x >> 16));
+            cb[2] = beta * from_bits<DT>((uint16_t)craw[j].y);
+            cb[3] = beta * from_bits<DT>((uint16_t)(craw[j].y >> 16));
+        }
+        const int c = 2 * j + (g >> 1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 16 * i + (lane & 15);
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = BIAS ? alpha * acc[i][j][e] + cb[e] : alpha * acc[i][j][e];
+            u32x2_t o;
+            o.x = pack2<DT>(v[0], v[1]);
+            o.y = pack2<DT>(v[2], v[3]);
+            *(u32x2_t*)(stage + r * ROWB + ((c ^ (r % NCH)) << 4) + (h << 3)) = o;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+        const int r = 4 * k + (lane >> 4), c = lane & 15;
+        const u32x4_t d = *(const u32x4_t*)(stage + r * ROWB + ((c ^ (r % NCH)) << 4));
+        store(k, r, c, d);
+    }
+}
+
 }  // namespace core16
 }  // namespace omm
