@@ -234,14 +234,14 @@ __global__ __launch_bounds__(NT) void dense16_kernel(DenseArgs p, int tiles_m, i
         epilogue16<BM, BN, DT, VEC>(p, acc, Y, m0, n0, lane, wm, wn);
 }
 
-// Full 256x256 tiles with both operands k-major (Gemm with transB = 1, the
-// usual weight layout), no C or a bias row C: the same tile, DMA stages and
-// LDS layout as dense16_kernel in the 16x16x32 MFMA form (mainloop_dma16).
-// Same work per stage as the 32x32x16 form, but measured on gfx950 the chip
-// holds a higher shader clock under it (~1.55 against ~1.35 GHz on one box at
-// 8192^3), which more than pays for its lower matrix-pipe busy share.
-template <int DT, int MODE>
-__global__ __launch_bounds__(NT) void dense16_nt16_kernel(DenseArgs p, int tiles_m, int tiles_n) {
+// Full 256x256 tiles, no C or a bias row C: the same tile, DMA stages and LDS
+// layouts as dense16_kernel in the 16x16x32 MFMA form (mainloop_dma16).  Same
+// work per stage as the 32x32x16 form, but measured on gfx950 the chip holds a
+// higher shader clock under it (~1.55 against ~1.35 GHz on one box at 8192^3
+// with both operands k-major), which more than pays for its lower
+// matrix-pipe busy share.
+template <int DT, int MODE, bool AK, bool BKM>
+__global__ __launch_bounds__(NT) void dense16_t16_kernel(DenseArgs p, int tiles_m, int tiles_n) {
     constexpr int BM = 256, BN = 256;
     constexpr int STAGE = (BM + BN) * KSTEP * 2;
     __shared__ __attribute__((aligned(1024))) char smem0[STAGE];
@@ -260,11 +260,11 @@ __global__ __launch_bounds__(NT) void dense16_nt16_kernel(DenseArgs p, int tiles
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     f32x4_t acc[8][8];  // written by the first k-block (K > 0 on this path)
     const int nk = (int)((p.K + KSTEP - 1) / KSTEP);
-    DmaSrc<BM, true> srcA;
-    DmaSrc<BN, true> srcB;
+    DmaSrc<BM, AK> srcA;
+    DmaSrc<BN, BKM> srcB;
     srcA.init(A, p.lda, m0, p.M, p.K, lane);
     srcB.init(B, p.ldb, n0, p.N, p.K, lane);
-    mainloop_dma16<BM, BN, DT, false>(acc, smem0, smem1, srcA, srcB, nk, lane, wm, wn, wave);
+    mainloop_dma16<BM, BN, DT, AK, BKM, false>(acc, smem0, smem1, srcA, srcB, nk, lane, wm, wn, wave);
     __syncthreads();
     char* stage = (wave < 2 ? smem0 : smem1) + (wave & 1) * (STAGE / 2);
     const int64_t col0 = n0 + wn * (BN / 2);
@@ -660,18 +660,24 @@ hipError_t launch_cfg(const DenseArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int DT, int MODE, bool AK, bool BKM>
+hipError_t launch_t16(const DenseArgs& a, hipStream_t s) {
+    const int64_t tiles_m = a.M / 256, tiles_n = a.N / 256;
+    const int64_t total = tiles_m * tiles_n * a.nb0 * a.nb1;
+    if (total <= 0) return hipSuccess;
+    if (total > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((dense16_t16_kernel<DT, MODE, AK, BKM>), dim3((unsigned)total), dim3(NT), 0, s, a, (int)tiles_m,
+                       (int)tiles_n);
+    return hipGetLastError();
+}
+
 template <int BM, int BN, int DT, int MODE>
 hipError_t launch_layout(const DenseArgs& a, hipStream_t s) {
     if constexpr (BM == 256 && (MODE == 2 || MODE == 3)) {
-        if (a.a_kmajor && a.b_kmajor) {
-            const int64_t tiles_m = a.M / 256, tiles_n = a.N / 256;
-            const int64_t total = tiles_m * tiles_n * a.nb0 * a.nb1;
-            if (total <= 0) return hipSuccess;
-            if (total > 0x7fffffff) return hipErrorInvalidValue;
-            hipLaunchKernelGGL((dense16_nt16_kernel<DT, MODE>), dim3((unsigned)total), dim3(NT), 0, s, a, (int)tiles_m,
-                               (int)tiles_n);
-            return hipGetLastError();
-        }
+        if (a.a_kmajor && a.b_kmajor) return launch_t16<DT, MODE, true, true>(a, s);
+        if (a.a_kmajor) return launch_t16<DT, MODE, true, false>(a, s);
+        if (a.b_kmajor) return launch_t16<DT, MODE, false, true>(a, s);
+        return launch_t16<DT, MODE, false, false>(a, s);
     }
     if (a.a_kmajor && a.b_kmajor) return launch_cfg<BM, BN, DT, true, true, MODE>(a, s);
     if (a.a_kmajor && !a.b_kmajor) return launch_cfg<BM, BN, DT, true, false, MODE>(a, s);

@@ -51,12 +51,16 @@ __device__ __forceinline__ int kmaj_lane(int lane, int s) {
 
 // "MN-major" tile of 16-bit elements (operand stored with m or n contiguous):
 // BK rows (k) of BMN elements.  32-byte granule g of row k is stored at
-// granule g ^ mswz16(k), mswz16(k) = 2 (k % 4) + (k / 4) % 2: any 8 consecutive
-// rows put one granule in 8 different slots.  Fragments are read with
-// ds_read_b64_tr_b16 (a 16-lane group covers 4 consecutive rows of one
-// granule); measured on gfx950 this swizzle gives the highest throughput of
-// that instruction (~75 B/clk/CU against ~63 for a 4-row swizzle).
-__device__ __forceinline__ int mswz16(int k) { return ((k & 3) << 1) + ((k >> 2) & 1); }
+// granule g ^ mswz16(k), mswz16(k) = 2 (k % 4) + ((k / 4) ^ (k / 8)) % 2.
+// Fragments are read with ds_read_b64_tr_b16, a 16-lane group covering 4
+// consecutive rows (k = 4q .. 4q+3) of one granule: those 4 rows take 4
+// distinct slots of one parity, so two groups on the same rows and adjacent
+// granules (the 32x32x16 operand layout) or on the same granule and rows 8
+// apart (the 16x16x32 layout) fill all 8 slots, i.e. every bank once per
+// half-wave.  Measured on gfx950 the 32x32 pattern on such a swizzle gives the
+// highest throughput of that instruction (~75 B/clk/CU against ~63 for a
+// 4-row swizzle).
+__device__ __forceinline__ int mswz16(int k) { return ((k & 3) << 1) + (((k >> 2) ^ (k >> 3)) & 1); }
 template <int ROWB>
 __device__ __forceinline__ int mmaj16_off(int k, int byte_in_row) {
     return k * ROWB + ((((byte_in_row >> 5) ^ mswz16(k))) << 5) + (byte_in_row & 31);

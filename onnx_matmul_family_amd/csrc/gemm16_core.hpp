@@ -288,8 +288,8 @@ struct DmaSrc {
     static constexpr int PER_WAVE = NBLK / 4;
     static constexpr int RPB = KMAJ ? 8 : 1024 / (2 * R);
     static constexpr int LPR = R / 8;
-    // MN-major: the swizzle repeats every 8 rows, so blocks come in 8 / RPB phases
-    static constexpr int NQ = KMAJ ? 2 : (8 / RPB > 1 ? 8 / RPB : 1);
+    // MN-major: the swizzle repeats every 16 rows, so blocks come in 16 / RPB phases
+    static constexpr int NQ = KMAJ ? 2 : (16 / RPB > 1 ? 16 / RPB : 1);
     static_assert(KMAJ || PER_WAVE % NQ == 0, "block phase == phase of the wave-local block index");
     static constexpr int KE = 128 / ES;  // k elements per stage
     const char* base;   // tile origin at stage 0 (bytes)
@@ -709,7 +709,7 @@ __device__ __forceinline__ void wave_epilogue_lds(const f32x16_t (&acc)[4][4], f
 
 
 // ---------------------------------------------------------------------------
-// 16x16x32 form of the K loop (both operands k-major).  Each wave's 128 x 128
+// 16x16x32 form of the K loop.  Each wave's 128 x 128
 // sub-tile is 8 x 8 MFMA tiles of 16 x 16; a 64-k stage is two k-blocks of 32,
 // each 64 MFMAs.  Operand fragment of rows [mnb, mnb+16), k-block s: lane l
 // gets mn = mnb + l%16, k = 32 s + 8 (l/16) + 0..7 (one swizzled chunk).
@@ -745,11 +745,27 @@ __device__ __forceinline__ void acc_fence(f32x4_t (&acc)[TM][8]) {
                      : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
                        "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
 }
-__device__ __forceinline__ u32x4_t read_frag16k(const char* lds, int mnb, int s, int lane) {
-    const int r = lane & 15, c = 4 * s + (lane >> 4);
-    return *(const u32x4_t*)(lds + (mnb + r) * 128 + ((c ^ kswz(r)) << 4));
+template <int R, bool KMAJ>
+__device__ __forceinline__ u32x4_t read_frag16(const char* lds, int mnb, int s, int lane) {
+    if constexpr (KMAJ) {
+        // 16 lanes on 16 consecutive rows of one chunk: 16 distinct bank quads
+        const int r = lane & 15, c = 4 * s + (lane >> 4);
+        return *(const u32x4_t*)(lds + (mnb + r) * 128 + ((c ^ kswz(r)) << 4));
+    } else {
+        // group g = l/16 takes k rows 32 s + 8 g + (0..3, then 4..7); lane i of a
+        // group reads columns mnb + 4 (i%4) .. +3 of row i/4, and the transposing
+        // read hands lane i column mnb + i of the group's 4 rows
+        const int g = lane >> 4, i = lane & 15;
+        const int krow = 32 * s + 8 * g + (i >> 2);
+        const int n = mnb + 4 * (i & 3);
+        const int off = mmaj16_off<R * 2>(krow, n * 2), off4 = mmaj16_off<R * 2>(krow + 4, n * 2);
+        i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(OMM_LDS(i16x4_t, lds + off));
+        i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(OMM_LDS(i16x4_t, lds + off4));
+        u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+        return u32x4_t{l2.x, l2.y, h2.x, h2.y};
+    }
 }
-template <int BM, int BN>
+template <int BM, int BN, bool AK, bool BKM>
 struct Frags16 {
     static constexpr int TM = BM / 32, TN = BN / 32;
     u32x4_t a[TM], b[TN];
@@ -757,9 +773,9 @@ struct Frags16 {
     __device__ __forceinline__ void read_one(const char* st, int s, int lane, int wm, int wn) {
         constexpr int A_BYTES = BM * KSTEP * 2;
         if constexpr (R < TM)
-            a[R] = read_frag16k(st, wm * (BM / 2) + 16 * R, s, lane);
+            a[R] = read_frag16<BM, AK>(st, wm * (BM / 2) + 16 * R, s, lane);
         else
-            b[R - TM] = read_frag16k(st + A_BYTES, wn * (BN / 2) + 16 * (R - TM), s, lane);
+            b[R - TM] = read_frag16<BN, BKM>(st + A_BYTES, wn * (BN / 2) + 16 * (R - TM), s, lane);
     }
     __device__ __forceinline__ void read(const char* st, int s, int lane, int wm, int wn) {
         static_for<0, TM + TN>([&](auto rc) { read_one<decltype(rc)::value>(st, s, lane, wm, wn); });
@@ -812,7 +828,7 @@ __device__ __forceinline__ void dma_stage16(f32x4_t (&acc)[BM / 32][BN / 32], F&
                                          wave);
 }
 
-template <int BM, int BN, int DT, bool CHECKED, class SA, class SB>
+template <int BM, int BN, int DT, bool AK, bool BKM, bool CHECKED, class SA, class SB>
 __device__ __forceinline__ void mainloop_dma16(f32x4_t (&acc)[BM / 32][BN / 32], char* __restrict__ s0,
                                                char* __restrict__ s1, const SA& srcA, const SB& srcB, int nk, int lane,
                                                int wm, int wn, int wave) {
@@ -827,7 +843,7 @@ __device__ __forceinline__ void mainloop_dma16(f32x4_t (&acc)[BM / 32][BN / 32],
     }
     wait_vm<LD>();
     __syncthreads();
-    Frags16<BM, BN> fc, fn;
+    Frags16<BM, BN, AK, BKM> fc, fn;
     fc.read(s0, 0, lane, wm, wn);
     dma_stage16<BM, BN, DT, CHECKED, true>(acc, fc, fn, s0, s1, srcA, srcB, 0, nk, lane, wm, wn, wave);
     dma_stage16<BM, BN, DT, CHECKED, false>(acc, fc, fn, s1, s0, srcA, srcB, 1, nk, lane, wm, wn, wave);
