@@ -16,8 +16,9 @@
 //      one global atomic;
 //   2. grouped16_kernel: one 256x256 output tile per workgroup, rows gathered
 //      from input[p / S], B = weights[g] (n contiguous, read through the
-//      transposing LDS path), epilogue adds bias[g] in fp32, rounds once and
-//      writes each row to output[p].  The grid is the upper bound
+//      transposing LDS path), 16x16x32 MFMAs (32x32x16 on the element-wise
+//      path for unaligned operands), epilogue adds bias[g] in fp32, rounds
+//      once and writes each row to output[p].  The grid is the upper bound
 //      (M*S/BM + G) x (N/BN); the routed tiles are split evenly over the 8
 //      XCDs and each XCD's surplus workgroups exit.
 //   Weight-only quantised experts (int8/uint8 weights with block scales) run
@@ -250,11 +251,11 @@ __device__ __forceinline__ void grouped_epilogue(const f32x16_t (&acc)[4][4], co
     }
 }
 
-// One 256x256 tile of the grouped product.  VEC: DMA path (CHECKED pads ragged
-// rows / columns / K with zeros); otherwise element-wise register-staged loads.
-template <int DT, bool VEC>
+// One 256x256 tile of the grouped product with element-wise register-staged
+// loads (any alignment and shape; the DMA form is grouped_body16).
+template <int DT>
 __device__ __forceinline__ void grouped_body(const GroupedArgs& a, const char* ws, int tile, int tn, char* s0,
-                                             char* s1, int* orow_s, uint32_t* roff_s, uint16_t* bias_s) {
+                                             char* s1, int* orow_s) {
     const int4 te = ((const int4*)(ws + off_tiles(a.G)))[tile];
     const int g = te.x, start = te.y, rows = te.z;
     const int* sorted = (const int*)(ws + off_sorted(a.M * a.S, a.G));
@@ -273,6 +274,108 @@ __device__ __forceinline__ void grouped_body(const GroupedArgs& a, const char* w
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     const int nk = (int)((K + KSTEP - 1) / KSTEP);
     const uint16_t* wg = (const uint16_t*)a.weights + (int64_t)g * K * N;
+    orow_s[t] = t < rows ? sorted[start + t] : -1;  // output row (token * S + slot) of tile row t
+
+    GatherSrc<GBM> srcA;
+    srcA.base = (const uint16_t*)a.input;
+    srcA.K = K;
+    int r0, lk;
+    Chunks<GBM, true>::coords(t, 0, r0, lk);
+    srcA.lk = lk;
+    srcA.valid = 0;
+#pragma unroll
+    for (int i = 0; i < GatherSrc<GBM>::NC; ++i) {
+        const int r = r0 + 32 * i;
+        int64_t off = 0;
+        if (r < rows) {
+            srcA.valid |= 1u << i;
+            off = (int64_t)(sorted[start + r] / S) * K;
+        }
+        srcA.roff[i] = off + srcA.lk;
+    }
+    TileSrc<GBN, false> srcB;
+    srcB.init(wg, N, n0, N, K, t);
+    mainloop<GBM, GBN, DT, true, false, 2>(acc, s0, s1, srcA, srcB, nk, t, lane, wm, wn);
+    grouped_epilogue<DT, false>(acc, a, g, rows, start, sorted, n0, lane, wave, s0, s1, orow_s);
+}
+
+// The same tile in the 16x16x32 MFMA form (DMA operands, K > 0): accumulator
+// tile (i, j), register e of lane l holds row 16 i + l%16, column
+// 16 j + 4 (l/16) + e of the wave's 128 x 128 block.  Whole 256-column tiles
+// leave through LDS as whole row segments; a ragged column tile (N % 8 == 0
+// here, so a lane's 4 columns are all in range or all out) stores 4 values
+// per row.
+template <int DT>
+__device__ __forceinline__ void grouped_epilogue16(const f32x4_t (&acc)[8][8], const GroupedArgs& a, int g, int rows,
+                                                   int start, const int* sorted, int64_t n0, int lane, int wave,
+                                                   char* s0, char* s1, const int* orow_s) {
+    using namespace core16;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t N = a.N;
+    if (n0 + GBN <= N && ((uintptr_t)a.output & 15) == 0) {
+        __syncthreads();  // every wave is done reading the last stage
+        char* stage = (wave < 2 ? s0 : s1) + (wave & 1) * (GBM * KSTEP * 2);
+        const int64_t col0 = n0 + wn * (GBN / 2);
+        uint16_t* out = (uint16_t*)a.output + col0;
+        const int* orow_w = orow_s + wm * (GBM / 2);
+        auto st = [&](int, int r, int c, const u32x4_t& d) {
+            const int o = orow_w[r];
+            if (o >= 0) *(u32x4_t*)(out + (int64_t)o * N + 8 * c) = d;
+        };
+        if (a.bias)
+            wave_epilogue_lds16<DT, true>(acc, 1.0f, (const uint16_t*)a.bias + (int64_t)g * N + col0, 1.0f, stage,
+                                          lane, st);
+        else
+            wave_epilogue_lds16<DT, false>(acc, 1.0f, nullptr, 1.0f, stage, lane, st);
+        return;
+    }
+    const uint16_t* __restrict__ bias = a.bias ? (const uint16_t*)a.bias + (int64_t)g * N : nullptr;
+    uint16_t* __restrict__ out = (uint16_t*)a.output;
+    const int64_t nl = n0 + wn * 128 + 4 * (lane >> 4);
+    int orow[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = wm * 128 + 16 * i + (lane & 15);
+        orow[i] = r < rows ? sorted[start + r] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int64_t n = nl + 16 * j;
+        if (n >= N) continue;
+        float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (bias) {
+            const u32x2_t b2 = *(const u32x2_t*)(bias + n);
+            bv[0] = from_bits<DT>((uint16_t)b2.x);
+            bv[1] = from_bits<DT>((uint16_t)(b2.x >> 16));
+            bv[2] = from_bits<DT>((uint16_t)b2.y);
+            bv[3] = from_bits<DT>((uint16_t)(b2.y >> 16));
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (orow[i] < 0) continue;
+            u32x2_t o;
+            o.x = pack2<DT>(acc[i][j][0] + bv[0], acc[i][j][1] + bv[1]);
+            o.y = pack2<DT>(acc[i][j][2] + bv[2], acc[i][j][3] + bv[3]);
+            *(u32x2_t*)(out + (int64_t)orow[i] * N + n) = o;
+        }
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void grouped_body16(const GroupedArgs& a, const char* ws, int tile, int tn, char* s0,
+                                               char* s1, int* orow_s, uint32_t* roff_s, uint16_t* bias_s) {
+    const int4 te = ((const int4*)(ws + off_tiles(a.G)))[tile];
+    const int g = te.x, start = te.y, rows = te.z;
+    const int* sorted = (const int*)(ws + off_sorted(a.M * a.S, a.G));
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t K = a.K, N = a.N, S = a.S;
+    const int64_t n0 = (int64_t)tn * GBN;
+
+    using namespace core16;
+    f32x4_t acc[8][8];  // written by the first k-block
+    const int nk = (int)((K + KSTEP - 1) / KSTEP);
+    const uint16_t* wg = (const uint16_t*)a.weights + (int64_t)g * K * N;
     const int srow = t < rows ? sorted[start + t] : -1;  // output row (token * S + slot) of tile row t
     orow_s[t] = srow;
     // Whole-tile epilogue with 32-bit row offsets: the tile's bias columns and
@@ -280,61 +383,33 @@ __device__ __forceinline__ void grouped_body(const GroupedArgs& a, const char* w
     // neither waits on global loads nor branches per row.  Row r of wave
     // block wm goes to roff_s[128 wm + 32 (r % 4) + r / 4 % 32]: the 32 rows a
     // lane stores are contiguous.
-    const bool fast = VEC && n0 + GBN <= N && N % 8 == 0 && ((uintptr_t)a.output & 15) == 0 &&
-                      (int64_t)a.M * S * N * 2 < (1LL << 31);
+    const bool fast = n0 + GBN <= N && ((uintptr_t)a.output & 15) == 0 && (int64_t)a.M * S * N * 2 < (1LL << 31);
     if (fast) {
         const int rr = t & 127;
         roff_s[(t & 128) + 32 * (rr & 3) + (rr >> 2)] = srow >= 0 ? (uint32_t)srow * (uint32_t)(N * 2) : DMA_OOB;
         if (a.bias && t < GBN / 4)
             *(u32x2_t*)(bias_s + 4 * t) = *(const u32x2_t*)((const uint16_t*)a.bias + (int64_t)g * N + n0 + 4 * t);
     }
-
-    if constexpr (VEC) {
-        GatherDma<GBM> srcA;
-        srcA.base = (const char*)a.input;
-        srcA.K = K;
-        srcA.lane = lane;
+    GatherDma<GBM> srcA;
+    srcA.base = (const char*)a.input;
+    srcA.K = K;
+    srcA.lane = lane;
 #pragma unroll
-        for (int j = 0; j < GatherDma<GBM>::PER_WAVE; ++j) {
-            const int r = GatherDma<GBM>::row_of(wave, j, lane);
-            srcA.roff[j] = r < rows ? (uint32_t)((int64_t)(sorted[start + r] / S) * K * 2) +
-                                          (GatherDma<GBM>::chunk(j, lane) << 4)
-                                    : DMA_OOB;
-        }
-        DmaSrc<GBN, false> srcB;
-        srcB.init(wg, N, n0, N, K, lane);
-        if (rows == GBM && n0 + GBN <= N && K % KSTEP == 0)
-            mainloop_dma<GBM, GBN, DT, true, false, false>(acc, s0, s1, srcA, srcB, nk, lane, wm, wn, wave);
-        else
-            mainloop_dma<GBM, GBN, DT, true, false, true>(acc, s0, s1, srcA, srcB, nk, lane, wm, wn, wave);
-    } else {
-        GatherSrc<GBM> srcA;
-        srcA.base = (const uint16_t*)a.input;
-        srcA.K = K;
-        int r0, lk;
-        Chunks<GBM, true>::coords(t, 0, r0, lk);
-        srcA.lk = lk;
-        srcA.valid = 0;
-#pragma unroll
-        for (int i = 0; i < GatherSrc<GBM>::NC; ++i) {
-            const int r = r0 + 32 * i;
-            int64_t off = 0;
-            if (r < rows) {
-                srcA.valid |= 1u << i;
-                off = (int64_t)(sorted[start + r] / S) * K;
-            }
-            srcA.roff[i] = off + srcA.lk;
-        }
-        TileSrc<GBN, false> srcB;
-        srcB.init(wg, N, n0, N, K, t);
-        mainloop<GBM, GBN, DT, true, false, 2>(acc, s0, s1, srcA, srcB, nk, t, lane, wm, wn);
+    for (int j = 0; j < GatherDma<GBM>::PER_WAVE; ++j) {
+        const int r = GatherDma<GBM>::row_of(wave, j, lane);
+        srcA.roff[j] = r < rows ? (uint32_t)((int64_t)(sorted[start + r] / S) * K * 2) + (GatherDma<GBM>::chunk(j, lane) << 4)
+                                : DMA_OOB;
     }
+    DmaSrc<GBN, false> srcB;
+    srcB.init(wg, N, n0, N, K, lane);
+    if (rows == GBM && n0 + GBN <= N && K % KSTEP == 0)
+        mainloop_dma16<GBM, GBN, DT, true, false, false>(acc, s0, s1, srcA, srcB, nk, lane, wm, wn, wave);
+    else
+        mainloop_dma16<GBM, GBN, DT, true, false, true>(acc, s0, s1, srcA, srcB, nk, lane, wm, wn, wave);
 
     if (fast) {
         __syncthreads();  // every wave is done reading the last stage
         char* stage = (wave < 2 ? s0 : s1) + (wave & 1) * (GBM * KSTEP * 2);
-        // the base made visibly wave-uniform, so that the resource sits in
-        // scalar registers (no per-lane loop around the stores)
         const uint64_t ob = (uint64_t)((uint16_t*)a.output + n0 + wn * (GBN / 2));
         const uint64_t obu = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)ob) |
                              ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(ob >> 32)) << 32);
@@ -350,18 +425,16 @@ __device__ __forceinline__ void grouped_body(const GroupedArgs& a, const char* w
             ro[4 * i + 2] = v.z;
             ro[4 * i + 3] = v.w;
         }
-        // rows past the tile's valid rows carry an offset beyond the buffer's
-        // range: their stores are dropped
         auto st = [&](int k, int, int c, const u32x4_t& d) {
             __builtin_amdgcn_raw_buffer_store_b128(d, out, (int)(ro[k] + 16 * c), 0, 0);
         };
         if (a.bias)
-            wave_epilogue_lds_f<DT, true>(acc, 1.0f, bias_s + wn * (GBN / 2), 1.0f, stage, lane, st);
+            wave_epilogue_lds16<DT, true>(acc, 1.0f, bias_s + wn * (GBN / 2), 1.0f, stage, lane, st);
         else
-            wave_epilogue_lds_f<DT, false>(acc, 1.0f, nullptr, 1.0f, stage, lane, st);
+            wave_epilogue_lds16<DT, false>(acc, 1.0f, nullptr, 1.0f, stage, lane, st);
         return;
     }
-    grouped_epilogue<DT, VEC>(acc, a, g, rows, start, sorted, n0, lane, wave, s0, s1, orow_s);
+    grouped_epilogue16<DT>(acc, a, g, rows, start, sorted, n0, lane, wave, s0, s1, orow_s);
 }
 
 template <int DT, bool VEC>
@@ -383,7 +456,10 @@ __global__ __launch_bounds__(256) void grouped16_kernel(GroupedArgs a, const cha
     const int w = x * per + min(x, extra) + l;
     int tm, tn;
     grouped_order(w, ntiles, tiles_n, ORDER_ROWS, tm, tn);
-    grouped_body<DT, VEC>(a, ws, tm, tn, s0, s1, orow_s, roff_s, bias_s);
+    if constexpr (VEC)
+        grouped_body16<DT>(a, ws, tm, tn, s0, s1, orow_s, roff_s, bias_s);
+    else
+        grouped_body<DT>(a, ws, tm, tn, s0, s1, orow_s);
 }
 
 // ---------------------------------------------------------------------------
@@ -1214,7 +1290,8 @@ hipError_t launch_grouped(const GroupedArgs& a, int dt, void* ws, hipStream_t s)
     if (max_mtiles * tiles_n > 0x7fffffff) return hipErrorInvalidValue;
     // DMA offsets are 32-bit: the gathered input and one k-stage of a group's weights must span < 2 GiB
     const bool vec = al(a.input, 16) && al(a.weights, 16) && al(a.output, 8) && (!a.bias || al(a.bias, 8)) &&
-                     a.K % 8 == 0 && a.N % 8 == 0 && a.M * a.K * 2 < (1LL << 31) && 64 * a.N * 2 < (1LL << 31);
+                     a.K % 8 == 0 && a.N % 8 == 0 && a.M * a.K * 2 < (1LL << 31) && 64 * a.N * 2 < (1LL << 31) &&
+                     a.K > 0;  // the DMA K loop runs at least one stage
     dim3 grid((unsigned)(max_mtiles * tiles_n));
     const char* wsc = (const char*)ws;
     if (dt == 0) {
