@@ -118,3 +118,45 @@ def test_empty(M, S):
     out, ws = om.grouped_matmul(inp, w, idx)
     assert tuple(out.shape) == (M, S, 8)
     assert om.grouped_matmul_check(ws) == 0
+
+
+def test_output_8_byte_aligned_full_column_tiles():
+    """Whole 256-column tiles with an output that is 8- but not 16-byte aligned:
+    the 4-value store epilogue instead of whole-row segments."""
+    rng = np.random.default_rng(21)
+    M, K, N, G, S = 300, 128, 512, 6, 2
+    inp = synth.store(synth.normal(rng, (M, K)), "bf16")
+    w = synth.store(synth.normal(rng, (G, K, N), 0.05), "bf16")
+    bias = synth.store(synth.uniform(rng, (G, N), -0.1, 0.1), "bf16")
+    idx = synth.distinct_groups(rng, M, S, G, np.int32)
+    flat = torch.full((M * S * N + 8,), 3.0, dtype=torch.bfloat16, device="cuda")
+    out = flat[4:4 + M * S * N].view(M, S, N)
+    assert out.data_ptr() % 16 == 8
+    _, ws = om.grouped_matmul(dev(inp, "bf16"), dev(w, "bf16"), dev(idx), dev(bias, "bf16"), output=out)
+    assert om.grouped_matmul_check(ws) == 0
+    y, t = oracle.grouped_matmul(inp, w, idx, bias, dt="bf16")
+    check_close(host_f64(out), y, t, "bf16", "grouped, 8-byte aligned output")
+    assert (flat[:4].float() == 3.0).all() and (flat[-4:].float() == 3.0).all()
+
+
+def test_output_beyond_2gib_sampled():
+    """An output of 2 GiB (row byte offsets no longer fit the 32-bit buffer
+    offsets of the whole-tile epilogue): rows are stored through row pointers."""
+    rng = np.random.default_rng(22)
+    M, K, N, G, S = 65536, 64, 2048, 8, 8
+    inp = synth.store(synth.normal(rng, (M, K)), "bf16")
+    w = synth.store(synth.normal(rng, (G, K, N), 0.05), "bf16")
+    bias = synth.store(synth.uniform(rng, (G, N), -0.1, 0.1), "bf16")
+    idx = synth.distinct_groups(rng, M, S, G, np.int32)
+    out = torch.full((M, S, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    assert out.numel() * 2 >= 1 << 31
+    _, ws = om.grouped_matmul(dev(inp, "bf16"), dev(w, "bf16"), dev(idx), dev(bias, "bf16"), output=out)
+    assert om.grouped_matmul_check(ws) == 0
+    rows = rng.choice(M * S, size=64, replace=False)
+    got = out.view(M * S, N)[torch.from_numpy(rows).cuda()]
+    assert torch.isfinite(got.float()).all()
+    sel = (rows[:, None] * N + np.arange(N)[None, :]).reshape(-1)
+    y, t = oracle.grouped_matmul(inp, w, idx, bias, dt="bf16", sel=sel)
+    check_close(host_f64(got).reshape(-1), y, t, "bf16", "grouped, 2 GiB output, sampled rows")
+    del out
+    torch.cuda.empty_cache()
