@@ -200,6 +200,25 @@ def test_full_tile_modes_exact(dt, tA, tB, cform):
     assert torch.isfinite(Y.float()).all()
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("tA,tB", [(0, 1), (0, 0), (1, 0), (1, 1)])
+@pytest.mark.parametrize("K", [192, 320])
+def test_full_tile_odd_stage_counts(dt, tA, tB, K):
+    """Whole 256x256 tiles with an odd number of 64-k stages (3 and 5): the
+    K loop runs stages in pairs, the last pair's second stage on zeros."""
+    rng = np.random.default_rng(400 + 2 * tA + tB + K)
+    M, N = 4096, 4096
+    A = synth.store(synth.normal(rng, (K, M) if tA else (M, K), 0.05), dt)
+    B = synth.store(synth.normal(rng, (N, K) if tB else (K, N), 0.05), dt)
+    C = synth.store(synth.uniform(rng, (N,), -0.1, 0.1), dt)
+    Y = om.gemm(dev(A, dt), dev(B, dt), dev(C, dt), 0.75, 1.25, tA, tB)
+    torch.cuda.synchronize()
+    sel = sample_indices(M * N, 20000, 8)
+    y, t = oracle.gemm(A, B, C, 0.75, 1.25, tA, tB, dt=dt, sel=sel)
+    check_close(host_f64(Y).ravel()[sel], y, t, dt, "gemm full tiles K=%d tA=%d tB=%d" % (K, tA, tB))
+    assert torch.isfinite(Y.float()).all()
+
+
 SPLITK = [  # (A shape, B shape, transA, transB): few output tiles, long K -> split-K path
     ((64, 8192), (8192, 4096), 0, 0), ((64, 8192), (4096, 8192), 0, 1), ((8192, 96), (8192, 1024), 1, 0),
     ((200, 4104), (4104, 320), 0, 0), ((1, 6144), (6144, 2048), 0, 0),
