@@ -1,0 +1,91 @@
+"""Wait-state check of the 16x16x32 MFMAs issued from inline assembly.
+
+The bf16/fp16 16x16x32 K loops issue their MFMAs as inline assembly (so each
+accumulator stays in its AGPRs), which the compiler's hazard recognizer does
+not look into.  An MFMA needs a few wait states after a VALU instruction
+writes one of its source registers; the loops never produce such a write
+(operands come from LDS reads, accumulators are first written by the MFMAs
+themselves).  This test compiles the two kernel files for gfx950 and checks
+that no VALU instruction writes a source register of a 16x16x32 MFMA within
+4 wait states before it.  CPU only (hipcc cross-compiles); skipped without
+hipcc."""
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "onnx_matmul_family_amd", "csrc")
+HIPCC = "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else shutil.which("hipcc")
+
+
+def _regs(tok):
+    m = re.match(r"([va])\[(\d+):(\d+)\]", tok)
+    if m:
+        return {(m.group(1), i) for i in range(int(m.group(2)), int(m.group(3)) + 1)}
+    m = re.match(r"([va])(\d+)$", tok)
+    return {(m.group(1), int(m.group(2)))} if m else set()
+
+
+def _instructions(asm):
+    out = []
+    for line in asm.splitlines():
+        s = line.strip()
+        if s and not s.startswith((";", ".", "_")) and not s.endswith(":"):
+            out.append(s)
+    return out
+
+
+def _violations(ins, window=4):
+    bad, n = [], 0
+    for i, line in enumerate(ins):
+        if not line.startswith("v_mfma_f32_16x16x32"):
+            continue
+        n += 1
+        ops = [o.strip() for o in line.split(None, 1)[1].split(",")]
+        src = set().union(*[_regs(o) for o in ops[1:]])
+        ws, j = 0, i - 1
+        while j >= 0 and ws < window:
+            p = ins[j]
+            if p.startswith("s_nop"):
+                ws += int(p.split()[1]) + 1
+            else:
+                if p.startswith("v_") and not p.startswith("v_mfma"):
+                    if _regs(p.split(None, 1)[1].split(",")[0].strip()) & src:
+                        bad.append((p, line, ws))
+                ws += 1
+            j -= 1
+    return n, bad
+
+
+def _compile(src, out):
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "--cuda-device-only", "-S",
+           os.path.join(CSRC, src), "-o", out]
+    subprocess.run(cmd, check=True, capture_output=True)
+    with open(out) as f:
+        return f.read()
+
+
+def test_checker_flags_a_planted_write():
+    ins = ["v_mov_b32_e32 v5, v9", "v_mfma_f32_16x16x32_bf16 a[0:3], v[2:5], v[6:9], a[0:3]"]
+    assert len(_violations(ins)[1]) == 1
+    assert len(_violations(["s_nop 3"] + ins[:1] + ["s_nop 3"] + ins[1:])[1]) == 0
+
+
+@pytest.mark.skipif(HIPCC is None, reason="hipcc not available")
+def test_no_valu_write_of_mfma16_operands():
+    with tempfile.TemporaryDirectory() as d:
+        srcs = ["dense16.hip", "grouped.hip"]
+        with ThreadPoolExecutor(2) as ex:
+            asms = list(ex.map(lambda s: _compile(s, os.path.join(d, s + ".s")), srcs))
+    total = 0
+    for src, asm in zip(srcs, asms):
+        n, bad = _violations(_instructions(asm))
+        total += n
+        assert not bad, "%s: %s" % (src, bad[:3])
+    assert total > 1000  # the 16x16x32 loops were found
