@@ -234,8 +234,86 @@ __global__ __launch_bounds__(NT) void dense16_kernel(DenseArgs p, int tiles_m, i
         epilogue16<BM, BN, DT, VEC>(p, acc, Y, m0, n0, lane, wm, wn);
 }
 
-// Full 256x256 tiles, no C or a bias row C: the same tile, DMA stages and LDS
-// layouts as dense16_kernel in the 16x16x32 MFMA form (mainloop_dma16).  Same
+// The same epilogue in the 16x16 accumulator layout (tile (i, j), register e
+// of lane l: row 16 i + l%16, column 16 j + 4 (l/16) + e of the wave's
+// 128 x 128 block); operands and output as the DMA path requires (Y 8-byte
+// aligned).
+template <int DT>
+__device__ __forceinline__ void epilogue_t16(const DenseArgs& p, const f32x4_t (&acc)[8][8], uint16_t* __restrict__ Y,
+                                             int64_t m0, int64_t n0, int lane, int wm, int wn) {
+    const float alpha = p.alpha, beta = p.beta;
+    const int64_t M = p.M, N = p.N;
+    const uint16_t* __restrict__ Cp = (const uint16_t*)p.C;
+    const bool vec_store = (N % 4 == 0) && (p.ldy % 4 == 0);
+    const bool c_cols = Cp && p.c_sm == 0;  // C constant along m
+    const int64_t nl = n0 + wn * 128 + 4 * (lane >> 4);
+    const int64_t ml = m0 + wm * 128 + (lane & 15);
+    float cb[8][4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cb[j][e] = 0.0f;
+    if (c_cols) {
+        const bool c_vec = p.c_sn == 1 && (N % 4 == 0) && (((uintptr_t)Cp & 7) == 0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t n = nl + 16 * j;
+            if (c_vec && n < N) {
+                const u32x2_t c2 = *(const u32x2_t*)(Cp + n);
+                cb[j][0] = from_bits<DT>((uint16_t)c2.x);
+                cb[j][1] = from_bits<DT>((uint16_t)(c2.x >> 16));
+                cb[j][2] = from_bits<DT>((uint16_t)c2.y);
+                cb[j][3] = from_bits<DT>((uint16_t)(c2.y >> 16));
+            } else if (!c_vec) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < N) cb[j][e] = from_bits<DT>(Cp[(n + e) * p.c_sn]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cb[j][e] *= beta;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t m = ml + 16 * i;
+        if (m >= M) continue;
+        uint16_t* __restrict__ yr = Y + m * p.ldy;
+        if (Cp && !c_cols) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t n = nl + 16 * j + e;
+                    cb[j][e] = n < N ? beta * from_bits<DT>(Cp[m * p.c_sm + n * p.c_sn]) : 0.0f;
+                }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t n = nl + 16 * j;
+            if (n >= N) continue;
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = alpha * acc[i][j][e] + cb[j][e];
+            if (vec_store) {
+                u32x2_t o;
+                o.x = pack2<DT>(v[0], v[1]);
+                o.y = pack2<DT>(v[2], v[3]);
+                *(u32x2_t*)(yr + n) = o;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < N) yr[n + e] = to_bits<DT>(v[e]);
+            }
+        }
+    }
+}
+
+// 256x256 tiles on the DMA path in the 16x16x32 MFMA form (mainloop_dma16):
+// MODE 2 / 3 as in dense16_kernel (every tile full, no C or a bias row C, the
+// LDS-staged epilogue); MODE 1 any shape and C (checked loads on ragged
+// tiles, epilogue_t16).  Same
 // work per stage as the 32x32x16 form, but measured on gfx950 the chip holds a
 // higher shader clock under it (~1.55 against ~1.35 GHz on one box at 8192^3
 // with both operands k-major), which more than pays for its lower
@@ -264,15 +342,32 @@ __global__ __launch_bounds__(NT) void dense16_t16_kernel(DenseArgs p, int tiles_
     DmaSrc<BN, BKM> srcB;
     srcA.init(A, p.lda, m0, p.M, p.K, lane);
     srcB.init(B, p.ldb, n0, p.N, p.K, lane);
-    mainloop_dma16<BM, BN, DT, AK, BKM, false>(acc, smem0, smem1, srcA, srcB, nk, lane, wm, wn, wave);
+    // the loop runs at least two stages: unchecked loads only for whole tiles and K > 0
+    if (MODE != 1 || (m0 + BM <= p.M && n0 + BN <= p.N && p.K % KSTEP == 0 && p.K > 0))
+        mainloop_dma16<BM, BN, DT, AK, BKM, false>(acc, smem0, smem1, srcA, srcB, nk, lane, wm, wn, wave);
+    else
+        mainloop_dma16<BM, BN, DT, AK, BKM, true>(acc, smem0, smem1, srcA, srcB, nk, lane, wm, wn, wave);
+    if constexpr (MODE == 1) {
+        // whole tiles with no C or a bias row C leave through LDS as whole row
+        // segments (16-byte stores: Y and its row stride 16-byte aligned); edge
+        // tiles and a C that varies along m use the 4-value stores
+        const bool staged = m0 + BM <= p.M && n0 + BN <= p.N && p.ldy % 8 == 0 && ((uintptr_t)Y & 15) == 0 &&
+                            (!p.C || (p.c_sm == 0 && p.c_sn == 1 && ((uintptr_t)p.C & 7) == 0));
+        if (!staged) {
+            epilogue_t16<DT>(p, acc, Y, m0, n0, lane, wm, wn);
+            return;
+        }
+    }
     __syncthreads();
     char* stage = (wave < 2 ? smem0 : smem1) + (wave & 1) * (STAGE / 2);
     const int64_t col0 = n0 + wn * (BN / 2);
-    const uint16_t* bias = MODE == 3 ? (const uint16_t*)p.C + col0 : nullptr;
     uint16_t* yb = Y + (m0 + wm * (BM / 2)) * p.ldy + col0;
     const int64_t ldy = p.ldy;
-    wave_epilogue_lds16<DT, MODE == 3>(acc, p.alpha, bias, p.beta, stage, lane,
-                                       [&](int, int r, int c, const u32x4_t& d) { *(u32x4_t*)(yb + r * ldy + 8 * c) = d; });
+    auto st = [&](int, int r, int c, const u32x4_t& d) { *(u32x4_t*)(yb + r * ldy + 8 * c) = d; };
+    if (MODE == 3 || (MODE == 1 && p.C))
+        wave_epilogue_lds16<DT, true>(acc, p.alpha, (const uint16_t*)p.C + col0, p.beta, stage, lane, st);
+    else
+        wave_epilogue_lds16<DT, false>(acc, p.alpha, nullptr, p.beta, stage, lane, st);
 }
 
 
@@ -662,7 +757,7 @@ hipError_t launch_cfg(const DenseArgs& a, hipStream_t s) {
 
 template <int DT, int MODE, bool AK, bool BKM>
 hipError_t launch_t16(const DenseArgs& a, hipStream_t s) {
-    const int64_t tiles_m = a.M / 256, tiles_n = a.N / 256;
+    const int64_t tiles_m = (a.M + 255) / 256, tiles_n = (a.N + 255) / 256;
     const int64_t total = tiles_m * tiles_n * a.nb0 * a.nb1;
     if (total <= 0) return hipSuccess;
     if (total > 0x7fffffff) return hipErrorInvalidValue;
@@ -673,7 +768,7 @@ hipError_t launch_t16(const DenseArgs& a, hipStream_t s) {
 
 template <int BM, int BN, int DT, int MODE>
 hipError_t launch_layout(const DenseArgs& a, hipStream_t s) {
-    if constexpr (BM == 256 && (MODE == 2 || MODE == 3)) {
+    if constexpr (BM == 256 && MODE >= 1 && MODE <= 3) {
         if (a.a_kmajor && a.b_kmajor) return launch_t16<DT, MODE, true, true>(a, s);
         if (a.a_kmajor) return launch_t16<DT, MODE, true, false>(a, s);
         if (a.b_kmajor) return launch_t16<DT, MODE, false, true>(a, s);
