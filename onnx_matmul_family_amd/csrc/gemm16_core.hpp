@@ -343,16 +343,18 @@ struct DmaSrc {
             if constexpr (KMAJ) {
                 voff = lane_off[j & 1] + (uint32_t)(b * 8) * ldb;
                 if (CHECKED) {
+                    // a select, not a branch: exec-mask writes between the
+                    // MFMAs stall their issue
                     const int64_t row = mn0 + b * 8 + (lane >> 3);
                     const int64_t k = (int64_t)kt * KE + (16 / ES) * kchunk(j & 1);
-                    if (!(row < MN && k < K)) voff = DMA_OOB;
+                    voff = ((row < MN) & (k < K)) ? voff : DMA_OOB;
                 }
             } else {
                 voff = lane_off[j % NQ] + (uint32_t)(b * RPB) * ldb;
                 if (CHECKED) {
                     const int64_t k = (int64_t)kt * KE + b * RPB + lane / LPR;
                     const int64_t mn = mn0 + 8 * (int64_t)chunk(j % NQ);
-                    if (!(k < K && mn < MN)) voff = DMA_OOB;
+                    voff = ((k < K) & (mn < MN)) ? voff : DMA_OOB;
                 }
             }
             dma16u(c.r, c.l0 + b * 1024, voff);
@@ -406,7 +408,7 @@ struct DmaSrcMN8 {
         if (CHECKED) {
             const int64_t k = (int64_t)kt * KR + b * 4 + (lane >> 4);
             const int64_t mn = mn0 + 16 * (int64_t)chunk(j & 1);
-            if (!(k < K && mn < MN)) voff = DMA_OOB;
+            voff = ((k < K) & (mn < MN)) ? voff : DMA_OOB;
         }
         dma16u(c.r, c.l0 + b * 1024, voff);
     }
@@ -446,7 +448,7 @@ struct GatherDma {
         uint32_t voff = roff[j];
         if (CHECKED) {
             const int64_t k = (int64_t)kt * KSTEP + 8 * chunk(j, lane);
-            if (k >= K) voff = DMA_OOB;
+            voff = k < K ? voff : DMA_OOB;
         }
         dma16u(c.r, c.l0 + b * 1024, voff);
     }
