@@ -340,7 +340,7 @@ def main():
         return
     from onnx_matmul_family_amd import _omm as om
     from onnx_matmul_family_amd import synth
-    from tests.gpu_util import dev
+    from onnx_matmul_family_amd.hostdev import dev
 
     assert torch.cuda.is_available(), "bench needs a GPU"
     om.lib()

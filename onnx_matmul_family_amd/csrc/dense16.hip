@@ -1,10 +1,19 @@
-// bf16 / fp16 batched GEMM on gfx950 MFMA (v_mfma_f32_32x32x16_{bf16,f16}).
+// bf16 / fp16 batched GEMM on gfx950 MFMA.
 //
 // Computes Y = alpha * A' B' + beta * C (Gemm, since version 13) and the
 // numpy.matmul product with broadcast batch dims (MatMul, since version 13):
 // fp32 accumulation, one round-to-nearest-even conversion to the output type.
-// The K loop is the shared MFMA core; this file adds the batch / tile mapping
-// and the alpha-beta-C epilogue, which stores 4 consecutive outputs per lane.
+// Kernels, chosen on the host by shape:
+//   dense16_t16_kernel   256x256 tiles, operands by LDS-DMA, 16x16x32 MFMAs
+//                        (v_mfma_f32_16x16x32_{bf16,f16}); whole tiles without
+//                        bounds checks, ragged tiles and any C form checked
+//   dense16_kernel       128x128 tiles on 32x32x16 MFMAs for shapes with few
+//                        tiles, its split-K partial-product mode, and the
+//                        register-staged mode for unaligned operands
+//   skinny*_kernel       decode-like products (a few rows): B streamed once
+//   splitk_reduce_kernel fixed-order sum of split-K partials + the epilogue
+// The K loops are the shared MFMA core (gemm16_core.hpp); this file adds the
+// batch / tile mapping and the alpha-beta-C epilogues.
 #include <algorithm>
 
 #include "gemm16_core.hpp"

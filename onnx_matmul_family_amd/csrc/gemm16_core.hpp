@@ -1,16 +1,19 @@
 // MFMA core shared by the bf16 / fp16 GEMM kernels (dense and grouped): the
-// operand tile sources (global -> registers), the swizzled LDS tile stores,
-// the MFMA fragment reads and the double-buffered K loop.
+// operand tile sources, the swizzled LDS tile layouts, the MFMA fragment reads
+// and the double-buffered K loops.
 //
 // Per workgroup of 256 threads = 4 waves on the CU's 4 SIMDs: output tile
 // BM x BN (256x256 or 128x128), K consumed 64 values per stage, each wave owns
 // a (BM/2) x (BN/2) sub-tile in fp32 accumulators (AGPRs at 256x256).
-// Tiles go global -> registers (16-byte loads, coalesced along the contiguous
-// dim) -> LDS, double-buffered with one barrier per stage; stage k+1's global
-// loads are in flight while stage k's MFMAs run.  Operands with k contiguous
-// sit in LDS as XOR-swizzled 128-byte rows read with ds_read_b128; operands
-// with m/n contiguous are copied as they are (swizzled 32-byte granules) and
-// read with the transposing ds_read_b64_tr_b16, so no register transpose.
+// The main path moves tiles global -> LDS directly (buffer_load ... lds, no
+// register staging), double-buffered, the DMA of stage k+2 in flight while
+// stage k multiplies (mainloop_dma16: 16x16x32 MFMAs; mainloop_dma: 32x32x16).
+// Unaligned operands take a register-staged loop (mainloop: 16-byte or element
+// loads into registers, then LDS stores, one barrier per stage).  Operands with
+// k contiguous sit in LDS as XOR-swizzled 128-byte rows read with ds_read_b128;
+// operands with m/n contiguous are copied as they are (swizzled 32-byte
+// granules) and read with the transposing ds_read_b64_tr_b16, so no register
+// transpose.
 #pragma once
 #include <type_traits>
 

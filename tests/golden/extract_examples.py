@@ -1,7 +1,7 @@
 """Transcribe the worked examples printed on the operator pages into JSON fixtures.
 
-This recipe reads the extracted page text at /root/reference/PAPER.md (the only
-place it exists) and writes one JSON file per operator next to this script:
+This recipe reads a plain-text extraction of the operator pages (the path is
+its one argument) and writes one JSON file per operator next to this script:
 
   matmul_examples.json         ONNX MatMul (onnx-light docs), "Examples" section
   gemm_examples.json           ONNX Gemm (onnx-light docs), "Examples" section
@@ -15,7 +15,7 @@ printed precision of each value. Nothing here is evaluated: the GroupedMatMul
 snippets are parsed with `ast.literal_eval` on list literals plus a few regexes
 for `np.arange(...).reshape(...)`, `np.zeros(...)` and `np.empty(...)`.
 
-Run:  python tests/golden/extract_examples.py   (needs the page text mounted)
+Run:  python tests/golden/extract_examples.py PAGE_TEXT_FILE
 """
 import ast
 import json
@@ -23,7 +23,6 @@ import os
 import re
 import sys
 
-SRC = "/root/reference/PAPER.md"
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 NUM = re.compile(r"[-+]?(?:\d+\.?\d*|\.\d+)(?:[eE][-+]?\d+)?")
@@ -174,8 +173,11 @@ def parse_grouped(page_text, title):
     return examples
 
 
-def main():
-    with open(SRC, encoding="utf-8") as f:
+def main(argv):
+    if len(argv) != 2:
+        print("usage: extract_examples.py PAGE_TEXT_FILE", file=sys.stderr)
+        return 2
+    with open(argv[1], encoding="utf-8") as f:
         text = f.read()
     pages = _split_pages(text)
     t1 = "ONNX MatMul (onnx-light operator docs, since version 13)"
@@ -199,4 +201,4 @@ def main():
 
 
 if __name__ == "__main__":
-    sys.exit(main())
+    sys.exit(main(sys.argv))

@@ -1,56 +1,15 @@
-"""Helpers for the GPU parity tests: host <-> device copies and the tolerance check.
+"""Helpers for the GPU parity tests.
 
-Tolerances (fixed for this operator family):
-  fp32 outputs:       |y_gpu - y| <= 1e-5 * t + 1e-6
-  bf16 / fp16 outputs: |y_gpu - y| <= 1e-2 * t + 1e-3
-where y is the oracle's unrounded fp64 value and t = sum_k |a_ik * b_kj|.  For
-Gemm with alpha != 1 or a beta*C term, t is taken as |alpha| t + |beta C|
-(the same bound applied to each term of the sum); the five workloads are
-checked with the plain t.  Integer results (QLinearMatMul) compare exactly.
+The tolerance check lives with the oracle (oracle/tolerance.py); host <-> device
+copies live in the package (onnx_matmul_family_amd/hostdev.py).  For Gemm with
+alpha != 1 or a beta*C term, a test may take t as |alpha| t + |beta C| (the same
+bound applied to each term of the sum); the five workloads are checked with the
+plain t.
 """
 import numpy as np
-import torch
 
-from onnx_matmul_family_amd import synth
-
-# fp64 (no stated bound): the GPU sums the same products in another order, each
-# fp64 operation off by at most 2^-53 relative, so |err| <= K * 2^-53 * t, under
-# 1e-12 * t for every K tested (K <= 4096)
-TOL = {"f32": (1e-5, 1e-6), "bf16": (1e-2, 1e-3), "f16": (1e-2, 1e-3), "f64": (1e-12, 1e-300)}
-TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "f64": torch.float64}
-
-
-def dev(arr, dt=None):
-    """numpy array -> GPU tensor (bf16 arrays are uint16 bit patterns, pass dt='bf16')."""
-    arr = np.ascontiguousarray(arr)
-    if dt == "bf16":
-        return torch.from_numpy(arr.view(np.int16).copy()).view(torch.bfloat16).cuda()
-    return torch.from_numpy(arr.copy()).cuda()
-
-
-def host_f64(t):
-    """GPU tensor -> float64 numpy (exact for bf16 / fp16 / fp32 / fp64)."""
-    t = t.detach()
-    if t.dtype == torch.bfloat16:
-        bits = t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-        return synth.bf16_to_f32(bits).astype(np.float64).reshape(t.shape)
-    return t.cpu().numpy().astype(np.float64)
-
-
-def check_close(got, y, t, dt, what=""):
-    """Assert |got - y| <= rtol * t + atol elementwise; report the worst offender."""
-    rt, at = TOL[dt]
-    got = np.asarray(got, np.float64).ravel()
-    y = np.asarray(y, np.float64).ravel()
-    t = np.asarray(t, np.float64).ravel()
-    assert got.shape == y.shape, (what, got.shape, y.shape)
-    err = np.abs(got - y)
-    tol = rt * t + at
-    bad = ~(err <= tol)  # NaN counts as bad
-    if bad.any():
-        i = int(np.argmax(np.where(bad, err / tol, 0)))
-        raise AssertionError("%s: %d / %d outside tolerance; worst at %d: got %r want %r (t=%r, tol=%r)"
-                             % (what, int(bad.sum()), bad.size, i, got[i], y[i], t[i], tol[i]))
+from onnx_matmul_family_amd.hostdev import dev, host_f32, host_f64  # noqa: F401
+from oracle.tolerance import TOL, check_close  # noqa: F401
 
 
 def sample_indices(total, n, seed):
@@ -60,3 +19,51 @@ def sample_indices(total, n, seed):
     s = rng.choice(total, size=n, replace=False).astype(np.int64)
     # always include the first and last elements (tile corners and the ragged tail)
     return np.unique(np.concatenate([s, [0, total - 1]]))
+
+
+def routing_from_workspace(ws, M, S, G):
+    """The grouped routing's result as the grouped kernels read it from the
+    workspace: (tile table rows (group, first sorted pair, rows), sorted pair
+    ids).  Offsets as the library lays the workspace out: a 64-byte header
+    (tile count, invalid count), counts and cursors (int32 x G each), the tile
+    table at the next 256-byte boundary (room for P/128 + G + 1 entries of 4
+    int32), the sorted pair ids at the 256-byte boundary after it."""
+    P = M * S
+    off_tiles = (64 + 8 * G + 255) // 256 * 256
+    cap = P // 128 + G + 1
+    off_sorted = (off_tiles + 16 * cap + 255) // 256 * 256
+    w = ws.cpu().numpy()
+    hdr = w[:8].view(np.int32)
+    ntiles = int(hdr[0])
+    assert 0 < ntiles <= cap
+    tiles = w[off_tiles:off_tiles + 16 * ntiles].view(np.int32).reshape(ntiles, 4)[:, :3]
+    sorted_ids = w[off_sorted:off_sorted + 4 * P].view(np.int32)
+    return int(hdr[1]), tiles, sorted_ids
+
+
+def check_routing(idx, tiles, sorted_ids, G, BM):
+    """The routing is a counting sort of the pairs by group cut into BM-row
+    tiles (every index valid): tile count, permutation, group runs, tile bounds."""
+    idx = np.asarray(idx).reshape(-1)
+    counts = np.bincount(idx, minlength=G)
+    assert len(tiles) == int(((counts + BM - 1) // BM).sum())
+    assert np.array_equal(np.sort(sorted_ids), np.arange(idx.size))
+    starts = np.concatenate([[0], np.cumsum(counts)[:-1]])
+    for g in range(G):
+        assert np.all(idx[sorted_ids[starts[g]:starts[g] + counts[g]]] == g), g
+    for ti, (g, start, rows) in enumerate(tiles):
+        assert 1 <= rows <= BM and starts[g] <= start and start + rows <= starts[g] + counts[g], (ti, g, start, rows)
+    assert int(tiles[:, 2].sum()) == idx.size
+
+
+def tile_row_pairs(tiles, sorted_ids, per_tile, BM):
+    """Pairs whose whole output rows a test compares: per_tile rows of every
+    routed tile, at slots (j * BM / per_tile + 11 * tile) % BM, which walk every
+    row slot of a tile over a launch of enough tiles."""
+    pairs = set()
+    for ti, (g, start, rows) in enumerate(tiles):
+        for j in range(per_tile):
+            slot = (j * (BM // per_tile) + 11 * ti) % BM
+            if slot < rows:
+                pairs.add(int(sorted_ids[start + slot]))
+    return np.array(sorted(pairs), dtype=np.int64)

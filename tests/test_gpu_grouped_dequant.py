@@ -12,7 +12,8 @@ import torch
 
 import oracle
 from onnx_matmul_family_amd import synth
-from tests.gpu_util import check_close, dev, host_f64, sample_indices
+from tests.gpu_util import (check_close, check_routing, dev, host_f64, routing_from_workspace, sample_indices,
+                            tile_row_pairs)
 
 pytestmark = pytest.mark.gpu
 
@@ -154,16 +155,26 @@ def test_empty_shapes():
     assert torch.equal(out0[:, 0].float(), b[idx0[:, 0].long()].float())
 
 
-def test_full_size_workload_sampled():
-    """The benchmark's quantised-experts workload at full size; 4000 sampled outputs."""
+def test_full_size_workload_tile_rows():
+    """The benchmark's quantised-experts workload at full size: the routing
+    checked as a counting sort, two complete output rows of every routed tile
+    (over every row slot of a tile) and 4000 sampled elements."""
     c = synth.grouped_dq_int8_moe()
-    out, bad = run(c["input"], c["qweights"], c["scale"], c["zero_point"], c["block_size"], c["group_indices"],
-                   c["bias"], "bf16")
-    assert bad == 0
     M, S = c["group_indices"].shape
-    N = c["qweights"].shape[2]
-    sel = sample_indices(M * S * N, 4000, 11)
+    G, K, N = c["qweights"].shape
+    out = torch.full((M, S, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    out, ws = om.grouped_matmul_dequant(dev(c["input"], "bf16"), dev(c["qweights"]), dev(c["scale"], "bf16"),
+                                        dev(c["zero_point"]), c["block_size"], dev(c["group_indices"]),
+                                        dev(c["bias"], "bf16"), output=out)
+    assert om.grouped_matmul_check(ws) == 0
+    bad, tiles, sorted_ids = routing_from_workspace(ws, M, S, G)
+    assert bad == 0
+    check_routing(c["group_indices"], tiles, sorted_ids, G, 256)
+    pairs = tile_row_pairs(tiles, sorted_ids, 2, 256)
+    sel = np.concatenate([(pairs[:, None] * N + np.arange(N, dtype=np.int64)[None, :]).ravel(),
+                          sample_indices(M * S * N, 4000, 11)])
     y, t = oracle.grouped_matmul_dequant(c["input"], c["qweights"], c["scale"], c["zero_point"], c["block_size"],
                                          c["group_indices"], c["bias"], dt="bf16", sel=sel)
-    got = host_f64(out).ravel()[sel]
-    check_close(got, y, t, "bf16", "grouped dq full size")
+    got = host_f64(out.reshape(-1)[torch.from_numpy(sel).cuda()])
+    check_close(got, y, t, "bf16", "grouped dq full size: %d whole rows + samples" % len(pairs))
+    assert torch.isfinite(out.float()).all()
