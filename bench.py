@@ -19,11 +19,13 @@ skinny Gemms against the HBM peak); they are not part of `value`.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--only NAME]
        python bench.py --copy-calibration      (1 GiB device-to-device copies, for
-                                                 scaling the HBM byte counters)
+                                                 scaling the L2 byte counters)
 
 `roofline.traffic` comes from profiles/traffic_grouped_bf16_moe.txt (FETCH_SIZE and
-WRITE_SIZE of the grouped kernel, scaled by the same counters on a plain copy); it
-is null when the kernel sources differ from the ones the counters were taken on.
+WRITE_SIZE of the grouped kernel, scaled by the same counters on a plain copy): bytes
+between the XCDs' L2 caches and the memory side, last-level-cache hits included (HBM
+bytes alone are not observable with the profiler's counters); it is null when the
+kernel sources differ from the ones the counters were taken on.
 """
 import argparse
 import hashlib
@@ -146,6 +148,29 @@ def next_rows(torch, om, synth, dev, reps):
                  ms=round(med, 4), tflops=round(rate, 2), frac_peak=round(rate / PEAK["bf16"], 4),
                  hbm_gbs=round(byts / (med * 1e-3) / 1e9, 1))]
     del d, out, ws
+    # fp32 / fp64 GroupedMatMul on the matrix cores (4096 tokens x 4 of 16 experts, K = N = 1024)
+    for dt in ("f32", "f64"):
+        c = synth.grouped_fp_moe(dt)
+        M, S = c["group_indices"].shape
+        G, K, N = c["weights"].shape
+        d = dict(input=dev(c["input"]), w=dev(c["weights"]), idx=dev(c["group_indices"]), bias=dev(c["bias"]))
+        out = torch.empty((M, S, N), dtype=torch.float64 if dt == "f64" else torch.float32, device="cuda")
+        ws = torch.empty(om.grouped_matmul_workspace_size(M, S, G), dtype=torch.uint8, device="cuda")
+        fn = lambda: om.grouped_matmul(d["input"], d["w"], d["idx"], d["bias"], out, ws)
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        med, _ = time_each(torch, fn, reps)
+        es = 8 if dt == "f64" else 4
+        rate = 2 * M * S * K * N / (med * 1e-3) / 1e12
+        name = "grouped_%s_moe" % dt
+        log("%-20s %9.4f ms  %8.1f T/s  %5.1f%% of %s peak (not in the step)" % (name, med, rate,
+                                                                               100 * rate / PEAK[dt], dt))
+        rows.append(dict(workload=name, desc=synth.GROUPED_FP_WORKLOAD % dt, dtype=dt, ms=round(med, 4),
+                         tflops=round(rate, 2), frac_peak=round(rate / PEAK[dt], 4),
+                         hbm_gbs=round(((M * K + G * K * N + G * N + M * S * N) * es + M * S * 4) / (med * 1e-3)
+                                       / 1e9, 1)))
+        del d, out, ws
     # fp64 Gemm (MFMA f64), 4096^3, N(0,1) operands, C[4096], alpha=beta=1
     n = 4096
     rng = np.random.default_rng(6)
@@ -239,7 +264,11 @@ def kernel_source_hash():
 
 
 def measured_traffic(kernel_key):
-    """HBM bytes per launch from the committed counter summary, or None if stale/missing."""
+    """Bytes per launch between the XCDs' L2 caches and the memory side (FETCH_SIZE +
+    WRITE_SIZE, scaled by the same counters on a plain copy) from the committed counter
+    summary, or None if stale/missing.  The memory side includes the 256 MB last-level
+    cache: no counter the profiler offers on this GPU separates its hits from HBM
+    reads, so this is an upper bound on HBM traffic, not HBM traffic itself."""
     path = os.path.join(ROOT, "profiles", "traffic_%s.txt" % kernel_key)
     if not os.path.exists(path):
         return None

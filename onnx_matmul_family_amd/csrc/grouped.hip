@@ -1137,63 +1137,189 @@ __global__ __launch_bounds__(256) void grouped16_dq_kernel(GroupedArgs a, const 
     grouped_epilogue<DT, FAST>(acc, a, g, rows, start, sorted, n0, lane, wave, s0, s1, orow_s);
 }
 
-// fp32 with quantised weights: one workgroup per (pair, 256 columns); each
-// weight dequantised with one fp32 rounding of (q - zp) * scale.
-__global__ __launch_bounds__(256) void grouped_dq_f32_kernel(GroupedArgs a, int qu8) {
-    __shared__ float row[1024];
-    const int64_t p = blockIdx.x;
-    const int64_t n = (int64_t)blockIdx.y * 256 + threadIdx.x;
-    const int64_t g = load_idx(a.idx, p, a.idx64);
-    if (g < 0 || g >= a.G) return;
-    const float* in = (const float*)a.input + (p / a.S) * a.K;
-    const uint8_t* qg = (const uint8_t*)a.weights + g * a.K * a.N;
-    const float* sg = (const float*)a.wscale + g * a.nkb * a.N;
-    const uint8_t* zg = a.wzp ? (const uint8_t*)a.wzp + g * a.nkb * a.N : nullptr;
-    float acc = 0.0f;
-    for (int64_t k0 = 0; k0 < a.K; k0 += 1024) {
-        __syncthreads();
-        for (int k = threadIdx.x; k < 1024; k += 256) row[k] = (k0 + k < a.K) ? in[k0 + k] : 0.0f;
-        __syncthreads();
-        if (n < a.N) {
-            const int64_t kend = min((int64_t)1024, a.K - k0);
-            for (int64_t k = 0; k < kend; ++k) {
-                const int64_t kk = k0 + k, po = (kk / a.bs) * a.N + n;
-                const uint32_t qb = qg[kk * a.N + n], zb = zg ? zg[po] : 0u;
-                const int qi = qu8 ? (int)qb : (int)(int8_t)qb, zi = qu8 ? (int)zb : (int)(int8_t)zb;
-                acc += row[k] * ((float)(qi - zi) * sg[po]);
-            }
-        }
-    }
-    if (n < a.N) {
-        if (a.bias) acc += ((const float*)a.bias)[g * a.N + n];
-        ((float*)a.output)[p * a.N + n] = acc;
-    }
-}
+// ---------------------------------------------------------------------------
+// fp32 / fp64 grouped product on the matrix cores: v_mfma_f32_16x16x4f32 and
+// v_mfma_f64_16x16x4f64 (fp32 accumulation for fp32, fp64 for fp64), over the
+// same routing with 128-row tiles.  One 128x128 output tile per workgroup of 4
+// waves (each 64x64: 4x4 MFMA tiles of 16x16); its 128 rows are the tile's
+// sorted pairs, gathered from input[pair / S]; B is weights[g] (n
+// contiguous).  K is staged 16 values at a time through three LDS buffers:
+// stage k+2 is loaded into registers while stage k multiplies and written to
+// LDS at the end of stage k (into the buffer stage k-1 left), so stage k+1 is
+// in LDS a whole stage before it starts and its first fragments are read
+// ahead of the barrier.  Element loads with range checks (any K, N, alignment).
+// WQ = 0: weights of type F.  WQ = 1 / 2 (fp32 only): int8 / uint8 weights
+// dequantised on load, w = fp32((q - zp) * scale) with the scale and zero
+// point of block k / bs and column n (one rounding, as DequantizeLinear to fp32).
+constexpr int FT = 128;  // output tile edge
+constexpr int FKS = 16;  // k per stage
+constexpr int FNB = 3;   // LDS stage buffers
+constexpr int FNL = FT * FKS / 256;  // elements per thread per operand and stage
+// LDS tiles (elements): A as 128 rows of 16 k at a stride of 18 (the 16 lanes
+// reading one k of 16 consecutive rows hit distinct banks), B as 16 k rows of
+// 128 n at a stride of 130
+constexpr int FA_ELEMS = FT * 18, FB_ELEMS = FKS * 130;
 
-// fp32 / fp64: one workgroup per (pair, 256 columns); plain dot products in
-// the tensors' own type.
 template <class F>
-__global__ __launch_bounds__(256) void grouped_fp_kernel(GroupedArgs a) {
-    __shared__ F row[1024];
-    const int64_t p = blockIdx.x;
-    const int64_t n = (int64_t)blockIdx.y * 256 + threadIdx.x;
-    const int64_t g = load_idx(a.idx, p, a.idx64);
-    if (g < 0 || g >= a.G) return;  // the whole workgroup has the same pair
-    const F* in = (const F*)a.input + (p / a.S) * a.K;
-    const F* wg = (const F*)a.weights + g * a.K * a.N;
-    F acc = 0;
-    for (int64_t k0 = 0; k0 < a.K; k0 += 1024) {
-        __syncthreads();
-        for (int k = threadIdx.x; k < 1024; k += 256) row[k] = (k0 + k < a.K) ? in[k0 + k] : (F)0;
-        __syncthreads();
-        if (n < a.N) {
-            const int64_t kend = min((int64_t)1024, a.K - k0);
-            for (int64_t k = 0; k < kend; ++k) acc += row[k] * wg[(k0 + k) * a.N + n];
+struct FpMfma;
+template <>
+struct FpMfma<double> {
+    typedef double v4 __attribute__((ext_vector_type(4)));
+    __device__ static v4 mma(double a, double b, v4 c) { return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0); }
+    // result register r of lane l: row l/16 + 4 r, column l%16
+    __device__ static int row(int lane, int r) { return (lane >> 4) + 4 * r; }
+};
+template <>
+struct FpMfma<float> {
+    typedef float v4 __attribute__((ext_vector_type(4)));
+    __device__ static v4 mma(float a, float b, v4 c) { return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0); }
+    // result register r of lane l: row 4 (l/16) + r, column l%16
+    __device__ static int row(int lane, int r) { return 4 * (lane >> 4) + r; }
+};
+
+template <class F, int WQ>
+__global__ __launch_bounds__(256) void grouped_fp_kernel(GroupedArgs a, const char* ws, int tiles_n) {
+    typedef typename FpMfma<F>::v4 v4;
+    __shared__ F As[FNB * FA_ELEMS];
+    __shared__ F Bs[FNB * FB_ELEMS];
+    __shared__ int orow_s[FT];
+    // routed tiles split evenly over the 8 XCDs, surplus workgroups exit (as grouped16_kernel)
+    const int ntiles = ((const int*)ws)[0];
+    const int total = ntiles * tiles_n;
+    const int bid = (int)blockIdx.x, x = bid & 7, l = bid >> 3;
+    const int per = total >> 3, extra = total & 7;
+    if (l >= per + (x < extra ? 1 : 0)) return;
+    int tm, tn;
+    grouped_order(x * per + min(x, extra) + l, ntiles, tiles_n, ORDER_ROWS, tm, tn);
+
+    const int4 te = ((const int4*)(ws + off_tiles(a.G)))[tm];
+    const int g = te.x, start = te.y, rows = te.z;
+    const int* sorted = (const int*)(ws + off_sorted(a.M * a.S, a.G));
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t K = a.K, N = a.N, S = a.S;
+    const int64_t n0 = (int64_t)tn * FT;
+    if (t < FT) orow_s[t] = t < rows ? sorted[start + t] : -1;
+
+    // A: thread t loads k = t % 16 of tile rows t / 16 + 16 i (gathered token rows)
+    const F* __restrict__ in = (const F*)a.input;
+    const int ka = t & 15;
+    int64_t aoff[FNL];
+    uint32_t avalid = 0;
+#pragma unroll
+    for (int i = 0; i < FNL; ++i) {
+        const int r = (t >> 4) + 16 * i;
+        aoff[i] = 0;
+        if (r < rows) {
+            avalid |= 1u << i;
+            aoff[i] = (int64_t)(sorted[start + r] / S) * K + ka;
         }
     }
-    if (n < a.N) {
-        if (a.bias) acc += ((const F*)a.bias)[g * a.N + n];
-        ((F*)a.output)[p * a.N + n] = acc;
+    // B: thread t loads column n0 + t % 128 of k rows t / 128 + 2 i
+    const int nb = t & 127, kb = t >> 7;
+    const int64_t ncol = n0 + nb;
+    const bool nok = ncol < N;
+    const int64_t wbase = (int64_t)g * K * N + ncol;
+    const float* wsc = WQ ? (const float*)a.wscale + (int64_t)g * a.nkb * N + ncol : nullptr;
+    const uint8_t* wzp = (WQ && a.wzp) ? (const uint8_t*)a.wzp + (int64_t)g * a.nkb * N + ncol : nullptr;
+
+    auto load = [&](F (&ra)[FNL], F (&rb)[FNL], int kt) {
+        const int64_t k0 = (int64_t)kt * FKS;
+#pragma unroll
+        for (int i = 0; i < FNL; ++i) ra[i] = (((avalid >> i) & 1u) && k0 + ka < K) ? in[aoff[i] + k0] : (F)0;
+#pragma unroll
+        for (int i = 0; i < FNL; ++i) {
+            const int64_t k = k0 + kb + 2 * i;
+            F v = (F)0;
+            if (nok && k < K) {
+                if constexpr (WQ == 0) {
+                    v = ((const F*)a.weights)[wbase + k * N];
+                } else {
+                    const uint8_t qb = ((const uint8_t*)a.weights)[wbase + k * N];
+                    const int64_t po = (k / a.bs) * N;
+                    const uint8_t zb = wzp ? wzp[po] : (uint8_t)0;
+                    const int qi = WQ == 2 ? (int)qb : (int)(int8_t)qb, zi = WQ == 2 ? (int)zb : (int)(int8_t)zb;
+                    v = (F)((float)(qi - zi) * wsc[po]);
+                }
+            }
+            rb[i] = v;
+        }
+    };
+    auto store = [&](int buf, const F (&ra)[FNL], const F (&rb)[FNL]) {
+        F* A_ = As + buf * FA_ELEMS;
+        F* B_ = Bs + buf * FB_ELEMS;
+#pragma unroll
+        for (int i = 0; i < FNL; ++i) A_[((t >> 4) + 16 * i) * 18 + ka] = ra[i];
+#pragma unroll
+        for (int i = 0; i < FNL; ++i) B_[(kb + 2 * i) * 130 + nb] = rb[i];
+    };
+    // lane l supplies A[m = l%16][k = kk + l/16] and B[k = kk + l/16][n = l%16]
+    struct Fr {
+        F a[4], b[4];
+    };
+    auto read = [&](Fr& f, int buf, int kk) {
+        const F* A_ = As + buf * FA_ELEMS;
+        const F* B_ = Bs + buf * FB_ELEMS;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f.a[i] = A_[(wm * 64 + 16 * i + (lane & 15)) * 18 + kk + (lane >> 4)];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f.b[j] = B_[(kk + (lane >> 4)) * 130 + wn * 64 + 16 * j + (lane & 15)];
+    };
+    v4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = v4{0, 0, 0, 0};
+    auto mma = [&](const Fr& f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = FpMfma<F>::mma(f.a[i], f.b[j], acc[i][j]);
+    };
+
+    const int nk = (int)((K + FKS - 1) / FKS);
+    F ra[FNL], rb[FNL];
+    for (int s2 = 0; s2 < 2 && s2 < nk; ++s2) {
+        load(ra, rb, s2);
+        store(s2, ra, rb);
+    }
+    __syncthreads();
+    Fr fc, fn;
+    if (nk > 0) read(fc, 0, 0);
+    int b0 = 0;  // buffer of stage kt
+    for (int kt = 0; kt < nk; ++kt) {
+        const int b1 = b0 == FNB - 1 ? 0 : b0 + 1, b2 = b1 == FNB - 1 ? 0 : b1 + 1;
+        const bool more = kt + 2 < nk;
+        if (more) load(ra, rb, kt + 2);
+        read(fn, b0, 4);
+        mma(fc);
+        read(fc, b0, 8);
+        mma(fn);
+        read(fn, b0, 12);
+        mma(fc);
+        // stage kt+1 has been in LDS since the last barrier (unused junk past the last stage)
+        read(fc, b1, 0);
+        mma(fn);
+        if (more) store(b2, ra, rb);  // the buffer stage kt-1 used, retired at the last barrier
+        __syncthreads();
+        b0 = b1;
+    }
+
+    // + bias[g], each row to output[pair]
+    const F* bias = a.bias ? (const F*)a.bias + (int64_t)g * N : nullptr;
+    F* __restrict__ out = (F*)a.output;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t n = n0 + wn * 64 + 16 * j + (lane & 15);
+        if (n >= N) continue;
+        const F bv = bias ? bias[n] : (F)0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tr = wm * 64 + 16 * i + FpMfma<F>::row(lane, r);
+                if (tr < rows) out[(int64_t)orow_s[tr] * N + n] = acc[i][j][r] + bv;
+            }
     }
 }
 
@@ -1206,7 +1332,7 @@ size_t grouped_workspace_bytes(int64_t M, int64_t S, int64_t G) {
 
 namespace {
 // Routing kernels: counts, tile table and the pairs sorted by group in `ws`.
-hipError_t launch_routing(const GroupedArgs& a, void* ws, hipStream_t s) {
+hipError_t launch_routing(const GroupedArgs& a, void* ws, hipStream_t s, int bm) {
     const int64_t P = a.M * a.S;
     char* w = (char*)ws;
     const unsigned nchunk = (unsigned)((P + ROUTE_CHUNK - 1) / ROUTE_CHUNK);
@@ -1214,28 +1340,47 @@ hipError_t launch_routing(const GroupedArgs& a, void* ws, hipStream_t s) {
     if (nchunk) {
         hipLaunchKernelGGL(route_hist_kernel, dim3(nchunk), dim3(256), 0, s, a.idx, a.idx64, P, (int)a.G, w);
     }
-    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(ROUTE_THREADS), 0, s, P, (int)a.G, GBM, w);
+    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(ROUTE_THREADS), 0, s, P, (int)a.G, bm, w);
     if (nchunk) {
         hipLaunchKernelGGL(route_scatter_kernel, dim3(nchunk), dim3(256), 0, s, a.idx, a.idx64, P, (int)a.G, w);
     }
     return hipGetLastError();
 }
 bool al(const void* q, uintptr_t n) { return ((uintptr_t)q & (n - 1)) == 0; }
+
+// fp32 (dt 2) / fp64 (dt 3) grouped product: routing into 128-row tiles, then
+// grouped_fp_kernel; wq = 1 / 2: int8 / uint8 weights dequantised on load (fp32)
+hipError_t launch_grouped_fp(const GroupedArgs& a, int dt, int wq, void* ws, hipStream_t s) {
+    const int64_t P = a.M * a.S;
+    hipError_t e = launch_routing(a, ws, s, FT);
+    if (e != hipSuccess) return e;
+    if (P == 0 || a.N == 0) return hipSuccess;
+    const int64_t max_mtiles = P / FT + a.G;
+    const int64_t tiles_n = (a.N + FT - 1) / FT;
+    if (max_mtiles * tiles_n > 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(max_mtiles * tiles_n));
+    const char* wsc = (const char*)ws;
+    const int tn = (int)tiles_n;
+    if (dt == 3)
+        hipLaunchKernelGGL((grouped_fp_kernel<double, 0>), grid, dim3(256), 0, s, a, wsc, tn);
+    else if (wq == 0)
+        hipLaunchKernelGGL((grouped_fp_kernel<float, 0>), grid, dim3(256), 0, s, a, wsc, tn);
+    else if (wq == 1)
+        hipLaunchKernelGGL((grouped_fp_kernel<float, 1>), grid, dim3(256), 0, s, a, wsc, tn);
+    else
+        hipLaunchKernelGGL((grouped_fp_kernel<float, 2>), grid, dim3(256), 0, s, a, wsc, tn);
+    return hipGetLastError();
+}
 }  // namespace
 
 hipError_t launch_grouped_dq(const GroupedArgs& a, int dt, void* ws, hipStream_t s) {
     const int64_t P = a.M * a.S;
     if (a.G > MAX_G || P > 0x7fffffff || a.bs < 1) return hipErrorInvalidValue;
-    hipError_t e = launch_routing(a, ws, s);
+    const int qu8 = a.q_kind == 2;
+    if (dt == 2) return launch_grouped_fp(a, dt, qu8 ? 2 : 1, ws, s);
+    hipError_t e = launch_routing(a, ws, s, GBM);
     if (e != hipSuccess) return e;
     if (P == 0 || a.N == 0) return hipSuccess;
-    const int qu8 = a.q_kind == 2;
-    if (dt == 2) {
-        const int64_t nb = (a.N + 255) / 256;
-        if (nb > 65535) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(grouped_dq_f32_kernel, dim3((unsigned)P, (unsigned)nb), dim3(256), 0, s, a, qu8);
-        return hipGetLastError();
-    }
     const int64_t max_mtiles = P / GBM + a.G;
     const int64_t tiles_n = (a.N + GBN - 1) / GBN;
     if (max_mtiles * tiles_n > 0x7fffffff) return hipErrorInvalidValue;
@@ -1275,16 +1420,10 @@ hipError_t launch_grouped_dq(const GroupedArgs& a, int dt, void* ws, hipStream_t
 hipError_t launch_grouped(const GroupedArgs& a, int dt, void* ws, hipStream_t s) {
     const int64_t P = a.M * a.S;
     if (a.G > MAX_G || P > 0x7fffffff) return hipErrorInvalidValue;
-    hipError_t e = launch_routing(a, ws, s);
+    if (dt >= 2) return launch_grouped_fp(a, dt, 0, ws, s);
+    hipError_t e = launch_routing(a, ws, s, GBM);
     if (e != hipSuccess) return e;
     if (P == 0 || a.N == 0) return hipSuccess;
-    if (dt >= 2) {
-        const int64_t nb = (a.N + 255) / 256;
-        if (nb > 65535) return hipErrorInvalidValue;
-        if (dt == 2) hipLaunchKernelGGL(grouped_fp_kernel<float>, dim3((unsigned)P, (unsigned)nb), dim3(256), 0, s, a);
-        else hipLaunchKernelGGL(grouped_fp_kernel<double>, dim3((unsigned)P, (unsigned)nb), dim3(256), 0, s, a);
-        return hipGetLastError();
-    }
     const int64_t max_mtiles = P / GBM + a.G;
     const int64_t tiles_n = (a.N + GBN - 1) / GBN;
     if (max_mtiles * tiles_n > 0x7fffffff) return hipErrorInvalidValue;

@@ -144,3 +144,23 @@ def grouped_dq_int8_moe(seed=5, M=16384, K=4096, N=2048, G=64, S=8, bs=128):
     idx = distinct_groups(rng, M, S, G, np.int32)
     return dict(input=inp, qweights=q, scale=scale, zero_point=zp, block_size=bs, group_indices=idx, bias=bias,
                 dt="bf16")
+
+
+# fp32 / fp64 GroupedMatMul (the page's type list includes float and double):
+# a mid-size expert layer, 4096 tokens x 4 of 16 experts, K = N = 1024.
+GROUPED_FP_WORKLOAD = ("GroupedMatMul %s, M=4096 K=1024 N=1024 G=16 S=4 int32 indices, input N(0,1), "
+                       "weights N(0,0.02), bias U(-0.1,0.1), seed 7")
+
+
+def grouped_fp_moe(dt, seed=7, M=4096, K=1024, N=1024, G=16, S=4):
+    rng = np.random.default_rng(seed)
+    if dt == "f64":
+        inp = rng.standard_normal((M, K))
+        weights = rng.standard_normal((G, K, N)) * 0.02
+        bias = rng.uniform(-0.1, 0.1, (G, N))
+    else:
+        inp = store(normal(rng, (M, K)), dt)
+        weights = store(normal(rng, (G, K, N), 0.02), dt)
+        bias = store(uniform(rng, (G, N), -0.1, 0.1), dt)
+    idx = distinct_groups(rng, M, S, G, np.int32)
+    return dict(input=inp, weights=weights, group_indices=idx, bias=bias, dt=dt)

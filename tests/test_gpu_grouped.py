@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from onnx_matmul_family_amd import synth
-from tests.gpu_util import check_close, dev, host_f64
+from tests.gpu_util import check_close, check_routing, dev, host_f64, routing_from_workspace
 
 pytestmark = pytest.mark.gpu
 
@@ -160,3 +160,62 @@ def test_output_beyond_2gib_sampled():
     check_close(host_f64(got).reshape(-1), y, t, "bf16", "grouped, 2 GiB output, sampled rows")
     del out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dt", ["f32", "f64"])
+def test_fp_matrix_core_workload_full(dt):
+    """fp32 / fp64 on the matrix cores at the size the benchmark times
+    (4096 tokens x 4 of 16 experts, K = N = 1024): the routing into 128-row
+    tiles checked as a counting sort, every output element against the oracle."""
+    c = synth.grouped_fp_moe(dt)
+    M, S = c["group_indices"].shape
+    G, K, N = c["weights"].shape
+    tdt = torch.float64 if dt == "f64" else torch.float32
+    out = torch.full((M, S, N), float("nan"), dtype=tdt, device="cuda")
+    out, ws = om.grouped_matmul(dev(c["input"]), dev(c["weights"]), dev(c["group_indices"]), dev(c["bias"]),
+                                output=out)
+    bad, tiles, sorted_ids = routing_from_workspace(ws, M, S, G)
+    assert bad == 0
+    check_routing(c["group_indices"], tiles, sorted_ids, G, 128)
+    y, t = oracle.grouped_matmul(c["input"], c["weights"], c["group_indices"], c["bias"])
+    check_close(host_f64(out), y, t, dt, "grouped %s %dx%d, K=%d N=%d G=%d" % (dt, M, S, K, N, G))
+
+
+@pytest.mark.parametrize("dt", ["f32", "f64"])
+def test_fp_small_integers_exact(dt):
+    """Integer inputs in {-2..2} and an integer bias (|sums| far below 2^24):
+    every fp32 / fp64 partial sum is exact, so the results must be bit-exact.
+    Ragged K (K % 16 != 0), N (two 128-column tiles, the second partial) and a
+    hot group of several 128-row tiles next to one-row groups."""
+    rng = np.random.default_rng(31)
+    M, K, N, G, S = 700, 203, 200, 9, 2
+    inp = synth.store(synth.small_ints(rng, (M, K)), dt)
+    w = synth.store(synth.small_ints(rng, (G, K, N)), dt)
+    bias = synth.store(synth.small_ints(rng, (G, N), -8, 8), dt)
+    idx = np.zeros((M, S), np.int64)
+    idx[:, 1] = 4
+    idx[:3, 0] = [1, 7, 8]
+    out, bad = run(inp, w, idx, bias, dt)
+    assert bad == 0
+    y, _ = oracle.grouped_matmul(inp, w, idx, bias)
+    assert np.array_equal(host_f64(out), y)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f64"])
+def test_fp_invalid_indices_counted_rows_untouched(dt):
+    rng = np.random.default_rng(33)
+    M, K, N, G, S = 300, 64, 150, 5, 2
+    inp = synth.store(synth.normal(rng, (M, K)), dt)
+    w = synth.store(synth.normal(rng, (G, K, N), 0.05), dt)
+    idx = synth.distinct_groups(rng, M, S, G, np.int64)
+    idx[7, 0] = -3
+    idx[200, 1] = G
+    sentinel = torch.full((M, S, N), 7.0, dtype=torch.float64 if dt == "f64" else torch.float32, device="cuda")
+    out, ws = om.grouped_matmul(dev(inp), dev(w), dev(idx), None, output=sentinel)
+    assert om.grouped_matmul_check(ws) == 2
+    got = host_f64(out)
+    assert (got[7, 0] == 7.0).all() and (got[200, 1] == 7.0).all()
+    ok = np.ones((M, S), bool)
+    ok[7, 0] = ok[200, 1] = False
+    y, t = oracle.grouped_matmul(inp, w, np.where(ok, idx, 0), None)
+    check_close(got[ok], y[ok], t[ok], dt, "fp grouped next to invalid indices")

@@ -155,6 +155,27 @@ def test_empty_shapes():
     assert torch.equal(out0[:, 0].float(), b[idx0[:, 0].long()].float())
 
 
+@pytest.mark.parametrize("qdt", [np.int8, np.uint8])
+def test_f32_matrix_core_multi_tile(qdt):
+    """fp32 over int8 / uint8 weights on the matrix cores: several 128-row tiles
+    per group, ragged N and K, block 96 (not a multiple of the 16-deep stage),
+    zero points present: every element against the oracle."""
+    rng = np.random.default_rng(41)
+    M, K, N, G, S, bs = 900, 300, 260, 6, 3, 96
+    nkb = -(-K // bs)
+    inp = synth.store(synth.normal(rng, (M, K)), "f32")
+    lo, hi = (-128, 127) if qdt == np.int8 else (0, 255)
+    q = rng.integers(lo, hi + 1, (G, K, N)).astype(qdt)
+    sc = synth.uniform(rng, (G, nkb, N), 1e-3, 3e-3)
+    zp = rng.integers(-8 if qdt == np.int8 else 120, 9 if qdt == np.int8 else 137, (G, nkb, N)).astype(qdt)
+    bias = synth.uniform(rng, (G, N), -0.1, 0.1)
+    idx = synth.distinct_groups(rng, M, S, G, np.int32)
+    out, bad = run(inp, q, sc, zp, bs, idx, bias, "f32")
+    assert bad == 0
+    y, t = oracle.grouped_matmul_dequant(inp, q, sc, zp, bs, idx, bias, dt="f32")
+    check_close(host_f64(out), y, t, "f32", "grouped dq f32 multi-tile")
+
+
 def test_full_size_workload_tile_rows():
     """The benchmark's quantised-experts workload at full size: the routing
     checked as a counting sort, two complete output rows of every routed tile
