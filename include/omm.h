@@ -33,7 +33,15 @@
  *    row lengths that are multiples of 16 bytes take the vectorised path; other
  *    layouts are still computed correctly by an element-wise path.
  *  - Concurrent calls on different streams may run in parallel; they share
- *    nothing but the caller's buffers.
+ *    nothing but the caller's buffers (omm_gemm_noalloc excepted: see there).
+ *  - Scratch: omm_matmul and omm_gemm with bf16 / fp16 operands split K over
+ *    several workgroups for shapes with few output tiles and a long K
+ *    (decode-like rows, narrow outputs).  The fp32 partial products of such a
+ *    call (splits x batches x M x N x 4 bytes) live in stream-ordered device
+ *    memory the library takes with hipMallocAsync and returns with
+ *    hipFreeAsync on the caller's stream, around the call's kernels; if the
+ *    stream's memory pool cannot supply it the call returns OMM_ERR_HIP with
+ *    nothing launched.  No other entry point allocates device memory.
  */
 #ifndef OMM_H_
 #define OMM_H_
@@ -73,6 +81,7 @@ typedef struct omm_tensor {
 #define OMM_ERR_UNSUPPORTED (-5) /* valid for the operator but not implemented here          */
 #define OMM_ERR_WORKSPACE (-6)   /* grouped workspace NULL or smaller than required          */
 #define OMM_ERR_HIP (-7)         /* a HIP runtime call or kernel launch failed               */
+#define OMM_ERR_SCRATCH (-8)     /* omm_gemm_noalloc: the shape needs more than its scratch   */
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* omm_status_string(int status);
@@ -116,6 +125,29 @@ int omm_gemm_output_shape(const omm_tensor* A, const omm_tensor* B, int transA, 
                           int32_t* ndim, int64_t* shape);
 int omm_gemm(const omm_tensor* A, const omm_tensor* B, const omm_tensor* C, float alpha, float beta,
              int transA, int transB, omm_tensor* Y, void* stream);
+
+/* ------------------------------------------------------------------------
+ * omm_gemm for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, results and errors as omm_gemm, computed by the same kernels;
+ * the split-K partial products that omm_gemm takes from stream-ordered memory
+ * go instead to a static device array of OMM_GEMM_NOALLOC_SCRATCH_BYTES per
+ * GPU (reserved when the library's device code is loaded on that GPU, held
+ * until the process ends; its address is looked up on the first call that
+ * runs on the GPU).  The call allocates and frees nothing.
+ *   - A shape whose partials need more than the scratch (bf16 / fp16 split-K
+ *     with splits x M x N x 4 bytes > OMM_GEMM_NOALLOC_SCRATCH_BYTES) returns
+ *     OMM_ERR_SCRATCH with nothing launched.  Shapes that do not split K
+ *     (and every fp32 / fp64 shape) use no scratch.
+ *   - Every call on one GPU shares that GPU's array and leaves its last
+ *     contents there (each call writes every partial it reads, nothing needs
+ *     clearing).  Calls that overlap on one GPU -- on different streams, or
+ *     from several host threads -- race on the array: the caller serialises
+ *     them (one stream, or events).
+ */
+#define OMM_GEMM_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+int omm_gemm_noalloc(const omm_tensor* A, const omm_tensor* B, const omm_tensor* C, float alpha, float beta,
+                     int transA, int transB, omm_tensor* Y, void* stream);
 
 /* ------------------------------------------------------------------------
  * QLinearMatMul (version 10, Summary, Inputs, Type Constraints).

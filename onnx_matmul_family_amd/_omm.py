@@ -52,6 +52,7 @@ def lib():
         L.omm_matmul.argtypes = [P, P, P, vp]
         L.omm_gemm_output_shape.argtypes = [P, P, ci, ci, i32p, i64p]
         L.omm_gemm.argtypes = [P, P, P, cf, cf, ci, ci, P, vp]
+        L.omm_gemm_noalloc.argtypes = [P, P, P, cf, cf, ci, ci, P, vp]
         L.omm_qlinear_matmul_output_shape.argtypes = [P, P, i32p, i64p]
         L.omm_qlinear_matmul.argtypes = [P, P, P, P, P, P, P, P, P, vp]
         L.omm_grouped_matmul_workspace_size.restype = ctypes.c_size_t
@@ -129,6 +130,17 @@ def gemm(A, B, C=None, alpha=1.0, beta=1.0, transA=0, transB=0, Y=None, stream=N
     pC = ctypes.byref(describe(C)) if C is not None else None
     _check(L.omm_gemm(ctypes.byref(tA), ctypes.byref(tB), pC, float(alpha), float(beta), int(transA), int(transB),
                       ctypes.byref(tY), _stream(stream)), "omm_gemm")
+    return Y
+
+
+def gemm_noalloc(A, B, C, alpha, beta, transA, transB, Y, stream=None):
+    """Gemm into a preallocated Y through omm_gemm_noalloc: the library
+    allocates nothing (split-K partials in its static per-GPU scratch)."""
+    L = lib()
+    tA, tB, tY = describe(A), describe(B), describe(Y)
+    pC = ctypes.byref(describe(C)) if C is not None else None
+    _check(L.omm_gemm_noalloc(ctypes.byref(tA), ctypes.byref(tB), pC, float(alpha), float(beta), int(transA),
+                              int(transB), ctypes.byref(tY), _stream(stream)), "omm_gemm_noalloc")
     return Y
 
 

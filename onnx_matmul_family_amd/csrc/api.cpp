@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "omm.h"
@@ -171,10 +172,46 @@ int for_each_outer(const Batch& b, F&& launch) {
 
 bool is_dense_float(int dt) { return dt == OMM_BF16 || dt == OMM_F16 || dt == OMM_F32 || dt == OMM_F64; }
 
-hipError_t launch_dense(const DenseArgs& a, int dt, hipStream_t s) {
+hipError_t launch_dense(const DenseArgs& a, int dt, hipStream_t s, const omm::DenseScratch* scratch = nullptr) {
     if (dt == OMM_F32) return omm::launch_dense_f32(a, s);
     if (dt == OMM_F64) return omm::launch_dense_f64(a, s);
-    return omm::launch_dense16(a, dt == OMM_BF16 ? 0 : 1, s);
+    return omm::launch_dense16(a, dt == OMM_BF16 ? 0 : 1, s, scratch);
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch of omm_gemm_noalloc: one array per GPU, reserved when the
+// library's device code is loaded on that GPU and held until the process
+// ends.  On the host `scratch` only names the symbol; its device address on
+// each GPU comes from hipGetSymbolAddress with that GPU current, looked up on
+// the first call that runs on the GPU and kept in scratch_dev.
+static __device__ __align__(256) char scratch[OMM_GEMM_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_dev[MAX_DEVICES] = {};
+
+// device address of `scratch` on the GPU that runs `s`
+int scratch_address(hipStream_t s, void** out) {
+    int dev = -1;
+    if (s) {
+        if (hipStreamGetDevice(s, &dev) != hipSuccess) return OMM_ERR_HIP;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return OMM_ERR_HIP;
+    }
+    if (dev < 0 || dev >= MAX_DEVICES) return OMM_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_dev[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return OMM_ERR_HIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return OMM_ERR_HIP;
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess) return OMM_ERR_HIP;
+        if (e != hipSuccess || !p) return OMM_ERR_HIP;
+        scratch_dev[dev] = p;
+    }
+    *out = scratch_dev[dev];
+    return OMM_OK;
 }
 
 int check_out(const omm_tensor* Y, int ndim, const int64_t* shape) {
@@ -200,6 +237,7 @@ const char* omm_status_string(int status) {
         case OMM_ERR_UNSUPPORTED: return "valid for the operator but not implemented";
         case OMM_ERR_WORKSPACE: return "workspace missing or too small";
         case OMM_ERR_HIP: return "HIP runtime or launch failure";
+        case OMM_ERR_SCRATCH: return "split-K partials exceed the static scratch of omm_gemm_noalloc (32 MiB)";
     }
     return "unknown status";
 }
@@ -293,8 +331,15 @@ int omm_gemm_output_shape(const omm_tensor* A, const omm_tensor* B, int transA, 
     return OMM_OK;
 }
 
-int omm_gemm(const omm_tensor* A, const omm_tensor* B, const omm_tensor* C, float alpha, float beta, int transA,
-             int transB, omm_tensor* Y, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Gemm with split-K partials in stream-ordered memory (noalloc = false) or in
+// this GPU's static scratch (noalloc = true: nothing allocated, shapes needing
+// more than the scratch rejected before any launch).
+int gemm_impl(const omm_tensor* A, const omm_tensor* B, const omm_tensor* C, float alpha, float beta, int transA,
+              int transB, omm_tensor* Y, void* stream, bool noalloc) {
     int rc;
     if ((rc = check_tensor(A)) || (rc = check_tensor(B)) || (rc = check_tensor(Y))) return rc;
     if (C && (rc = check_tensor(C))) return rc;
@@ -337,7 +382,27 @@ int omm_gemm(const omm_tensor* A, const omm_tensor* B, const omm_tensor* C, floa
     a.beta = beta;
     a.a_kmajor = transA ? 0 : 1;
     a.b_kmajor = transB ? 1 : 0;
-    return hip_status(launch_dense(a, dt, (hipStream_t)stream));
+    if (!noalloc) return hip_status(launch_dense(a, dt, (hipStream_t)stream));
+    omm::DenseScratch sc{nullptr, OMM_GEMM_NOALLOC_SCRATCH_BYTES};
+    if (dt == OMM_BF16 || dt == OMM_F16) {
+        if (omm::dense16_scratch_bytes(a) > OMM_GEMM_NOALLOC_SCRATCH_BYTES) return OMM_ERR_SCRATCH;
+        if ((rc = scratch_address((hipStream_t)stream, &sc.ptr))) return rc;
+    }
+    return hip_status(launch_dense(a, dt, (hipStream_t)stream, &sc));
+}
+
+}  // namespace
+
+extern "C" {
+
+int omm_gemm(const omm_tensor* A, const omm_tensor* B, const omm_tensor* C, float alpha, float beta, int transA,
+             int transB, omm_tensor* Y, void* stream) {
+    return gemm_impl(A, B, C, alpha, beta, transA, transB, Y, stream, false);
+}
+
+int omm_gemm_noalloc(const omm_tensor* A, const omm_tensor* B, const omm_tensor* C, float alpha, float beta,
+                     int transA, int transB, omm_tensor* Y, void* stream) {
+    return gemm_impl(A, B, C, alpha, beta, transA, transB, Y, stream, true);
 }
 
 // ------------------------------------------------------------------ QLinearMatMul

@@ -789,8 +789,18 @@ hipError_t launch_layout(const DenseArgs& a, hipStream_t s) {
     return launch_cfg<BM, BN, DT, false, false, MODE>(a, s);
 }
 
-template <int DT>
-hipError_t launch_dt(const DenseArgs& a, hipStream_t s) {
+// The kernel choice for one launch and the split-K workspace it needs.
+struct Plan16 {
+    enum Kind { T16_FULL, T16_BIAS, T16_ANY, SKINNY_NMAJ, SKINNY1, SKINNY_SPLIT, SPLIT128, T128_VEC, T128_REG } kind;
+    int mr = 0;           // SKINNY_NMAJ: rows per workgroup pass (1, 2, 4)
+    int64_t splits = 0;   // SKINNY_SPLIT / SPLIT128: K ranges
+    int64_t kchunk = 0;   // their length
+    int64_t groups = 0;   // SKINNY_SPLIT: 64-column workgroups
+    size_t ws_bytes = 0;  // fp32 partial products, splits x batches x M x N
+};
+
+Plan16 plan16(const DenseArgs& a) {
+    Plan16 pl;
     // 16-byte loads need 16-byte aligned bases, row strides that are multiples
     // of 8 elements and a contiguous extent (K, M or N) that is a multiple of 8.
     auto al16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
@@ -808,9 +818,10 @@ hipError_t launch_dt(const DenseArgs& a, hipStream_t s) {
         // every tile full: epilogue without bounds checks (8-byte stores need
         // N and the row stride to be multiples of 4)
         const bool full = a.M % 256 == 0 && a.N % 256 == 0 && a.K % KSTEP == 0 && a.K > 0 && a.ldy % 4 == 0;
-        if (full && !a.C) return launch_layout<256, 256, DT, 2>(a, s);
-        if (full && a.c_sm == 0 && a.c_sn == 1 && ((uintptr_t)a.C & 7) == 0) return launch_layout<256, 256, DT, 3>(a, s);
-        return launch_layout<256, 256, DT, 1>(a, s);
+        if (full && !a.C) pl.kind = Plan16::T16_FULL;
+        else if (full && a.c_sm == 0 && a.c_sn == 1 && ((uintptr_t)a.C & 7) == 0) pl.kind = Plan16::T16_BIAS;
+        else pl.kind = Plan16::T16_ANY;
+        return pl;
     }
     const int64_t NB = a.nb0 * a.nb1;
     // Skinny (M <= 16) with both operands k-contiguous: stream B, split K.
@@ -824,17 +835,17 @@ hipError_t launch_dt(const DenseArgs& a, hipStream_t s) {
     if (vec && b_span && a_span && (a.M <= 2 || (a.M <= 4 && a.K <= 4096)) && a.a_kmajor && !a.b_kmajor &&
         a.K >= 1024 && NB <= 65535 &&
         (a.N + 15) / 16 * NB >= 256 && (a.N + 15) / 16 <= 0x7fffffff) {
-        const int64_t mr = a.M <= 1 ? 1 : a.M <= 2 ? 2 : 4;
+        const int mr = a.M <= 1 ? 1 : a.M <= 2 ? 2 : 4;
         if (a.K * mr * 2 <= 61440) {
-            if (mr == 1) return launch_skinny_nmaj<DT, 1>(a, s);
-            if (mr == 2) return launch_skinny_nmaj<DT, 2>(a, s);
-            return launch_skinny_nmaj<DT, 4>(a, s);
+            pl.kind = Plan16::SKINNY_NMAJ;
+            pl.mr = mr;
+            return pl;
         }
     }
     if (vec && b_span && a_span && a.M <= 16 && a.a_kmajor && a.b_kmajor && a.K >= 1024 && NB <= 65535 &&
         (a.N + 15) / 16 * NB >= 512 && (a.N + 15) / 16 <= 0x7fffffff) {
-        hipLaunchKernelGGL(skinny1_kernel<DT>, dim3((unsigned)((a.N + 15) / 16), (unsigned)NB), dim3(256), 0, s, a);
-        return hipGetLastError();
+        pl.kind = Plan16::SKINNY1;
+        return pl;
     }
     if (vec && b_span && a_span && a.M <= 16 && a.a_kmajor && a.b_kmajor && a.K >= 1024 && NB <= 65535) {
         const int64_t groups = (a.N + SK_COLS - 1) / SK_COLS;
@@ -843,21 +854,12 @@ hipError_t launch_dt(const DenseArgs& a, hipStream_t s) {
         const int64_t kchunk = std::min<int64_t>(((a.K + S - 1) / S + 255) / 256 * 256, SK_KMAX);
         S = (a.K + kchunk - 1) / kchunk;
         if (groups <= 0x7fffffff && S <= 65535) {
-            const int64_t elems = NB * a.M * a.N;
-            DenseArgs b = a;
-            b.kchunk = kchunk;
-            b.splits = (int)S;
-            hipError_t e = hipMallocAsync((void**)&b.ws, (size_t)(S * elems) * sizeof(float), s);
-            if (e != hipSuccess) return e;
-            hipLaunchKernelGGL(skinny_kernel<DT>, dim3((unsigned)groups, (unsigned)S, (unsigned)NB), dim3(256), 0, s, b);
-            e = hipGetLastError();
-            if (e == hipSuccess) {
-                hipLaunchKernelGGL(splitk_reduce_kernel<DT>, dim3((unsigned)((elems + 255) / 256)), dim3(256), 0, s,
-                                   b);
-                e = hipGetLastError();
-            }
-            const hipError_t f = hipFreeAsync(b.ws, s);
-            return e != hipSuccess ? e : f;
+            pl.kind = Plan16::SKINNY_SPLIT;
+            pl.groups = groups;
+            pl.splits = S;
+            pl.kchunk = kchunk;
+            pl.ws_bytes = (size_t)(S * NB * a.M * a.N) * sizeof(float);
+            return pl;
         }
     }
     // Few output tiles and a long K: split K over several workgroups per tile
@@ -868,30 +870,82 @@ hipError_t launch_dt(const DenseArgs& a, hipStream_t s) {
         if (S >= 2) {
             const int64_t kchunk = ((a.K + S - 1) / S + KSTEP - 1) / KSTEP * KSTEP;
             S = (a.K + kchunk - 1) / kchunk;
-            const int64_t elems = NB * a.M * a.N;
-            DenseArgs b = a;
-            b.kchunk = kchunk;
-            b.splits = (int)S;
-            hipError_t e = hipMallocAsync((void**)&b.ws, (size_t)(S * elems) * sizeof(float), s);
-            if (e != hipSuccess) return e;
-            e = launch_layout<128, 128, DT, 4>(b, s);
-            if (e == hipSuccess) {
-                hipLaunchKernelGGL(splitk_reduce_kernel<DT>, dim3((unsigned)((elems + 255) / 256)), dim3(256), 0, s,
-                                   b);
-                e = hipGetLastError();
-            }
-            const hipError_t f = hipFreeAsync(b.ws, s);
-            return e != hipSuccess ? e : f;
+            pl.kind = Plan16::SPLIT128;
+            pl.splits = S;
+            pl.kchunk = kchunk;
+            pl.ws_bytes = (size_t)(S * NB * a.M * a.N) * sizeof(float);
+            return pl;
         }
     }
-    if (vec) return launch_layout<128, 128, DT, 1>(a, s);
-    return launch_layout<128, 128, DT, 0>(a, s);
+    pl.kind = vec ? Plan16::T128_VEC : Plan16::T128_REG;
+    return pl;
+}
+
+// Launches the planned kernels; ws holds pl.ws_bytes when the plan splits K.
+template <int DT>
+hipError_t run16(const DenseArgs& a, const Plan16& pl, float* ws, hipStream_t s) {
+    const int64_t NB = a.nb0 * a.nb1;
+    switch (pl.kind) {
+        case Plan16::T16_FULL: return launch_layout<256, 256, DT, 2>(a, s);
+        case Plan16::T16_BIAS: return launch_layout<256, 256, DT, 3>(a, s);
+        case Plan16::T16_ANY: return launch_layout<256, 256, DT, 1>(a, s);
+        case Plan16::SKINNY_NMAJ:
+            if (pl.mr == 1) return launch_skinny_nmaj<DT, 1>(a, s);
+            if (pl.mr == 2) return launch_skinny_nmaj<DT, 2>(a, s);
+            return launch_skinny_nmaj<DT, 4>(a, s);
+        case Plan16::SKINNY1:
+            hipLaunchKernelGGL(skinny1_kernel<DT>, dim3((unsigned)((a.N + 15) / 16), (unsigned)NB), dim3(256), 0, s, a);
+            return hipGetLastError();
+        case Plan16::SKINNY_SPLIT:
+        case Plan16::SPLIT128: {
+            DenseArgs b = a;
+            b.kchunk = pl.kchunk;
+            b.splits = (int)pl.splits;
+            b.ws = ws;
+            hipError_t e;
+            if (pl.kind == Plan16::SKINNY_SPLIT) {
+                hipLaunchKernelGGL(skinny_kernel<DT>, dim3((unsigned)pl.groups, (unsigned)pl.splits, (unsigned)NB),
+                                   dim3(256), 0, s, b);
+                e = hipGetLastError();
+            } else {
+                e = launch_layout<128, 128, DT, 4>(b, s);
+            }
+            if (e != hipSuccess) return e;
+            const int64_t elems = NB * a.M * a.N;
+            hipLaunchKernelGGL(splitk_reduce_kernel<DT>, dim3((unsigned)((elems + 255) / 256)), dim3(256), 0, s, b);
+            return hipGetLastError();
+        }
+        case Plan16::T128_VEC: return launch_layout<128, 128, DT, 1>(a, s);
+        case Plan16::T128_REG: return launch_layout<128, 128, DT, 0>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+// scratch == nullptr: split-K partials in stream-ordered memory taken and
+// returned around the launch; otherwise the caller's scratch (its size checked
+// against the plan before anything is enqueued).
+template <int DT>
+hipError_t launch_dt(const DenseArgs& a, hipStream_t s, const DenseScratch* scratch) {
+    const Plan16 pl = plan16(a);
+    if (pl.ws_bytes == 0) return run16<DT>(a, pl, nullptr, s);
+    if (scratch) {
+        if (!scratch->ptr || pl.ws_bytes > scratch->bytes) return hipErrorInvalidValue;
+        return run16<DT>(a, pl, (float*)scratch->ptr, s);
+    }
+    float* ws = nullptr;
+    hipError_t e = hipMallocAsync((void**)&ws, pl.ws_bytes, s);
+    if (e != hipSuccess) return e;
+    e = run16<DT>(a, pl, ws, s);
+    const hipError_t f = hipFreeAsync(ws, s);
+    return e != hipSuccess ? e : f;
 }
 
 }  // namespace
 
-hipError_t launch_dense16(const DenseArgs& a, int dt, hipStream_t s) {
-    return dt == 0 ? launch_dt<0>(a, s) : launch_dt<1>(a, s);
+hipError_t launch_dense16(const DenseArgs& a, int dt, hipStream_t s, const DenseScratch* scratch) {
+    return dt == 0 ? launch_dt<0>(a, s, scratch) : launch_dt<1>(a, s, scratch);
 }
+
+size_t dense16_scratch_bytes(const DenseArgs& a) { return plan16(a).ws_bytes; }
 
 }  // namespace omm

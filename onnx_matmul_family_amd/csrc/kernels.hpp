@@ -69,8 +69,18 @@ struct GroupedArgs {
     int q_kind;          // 1 = int8, 2 = uint8
 };
 
-// dt: 0 = bf16, 1 = fp16
-hipError_t launch_dense16(const DenseArgs& a, int dt, hipStream_t s);
+// Device memory a caller lends a launch for split-K partial products.
+struct DenseScratch {
+    void* ptr;
+    size_t bytes;
+};
+
+// dt: 0 = bf16, 1 = fp16.  scratch == nullptr: split-K partials go to
+// stream-ordered memory (hipMallocAsync / hipFreeAsync on s); otherwise to
+// scratch, which must hold dense16_scratch_bytes(a).
+hipError_t launch_dense16(const DenseArgs& a, int dt, hipStream_t s, const DenseScratch* scratch = nullptr);
+// bytes of split-K partials launch_dense16 needs for a (0: no split)
+size_t dense16_scratch_bytes(const DenseArgs& a);
 hipError_t launch_dense_f32(const DenseArgs& a, hipStream_t s);
 hipError_t launch_dense_f64(const DenseArgs& a, hipStream_t s);
 hipError_t launch_qlinear(const QArgs& a, hipStream_t s);

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol():
 def test_status_strings_and_version():
     L = om.lib()
     assert L.omm_version() >= 100
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         s = om.status_string(code)
         assert s and s != "unknown status", code
     assert om.status_string(-99) == "unknown status"
@@ -94,6 +94,21 @@ def test_matmul_argument_errors():
     assert L.omm_matmul(ctypes.byref(T((4, 8), BF16, 0)), ctypes.byref(B), ctypes.byref(Y), None) == -1
     # empty output: valid, nothing launched
     assert L.omm_matmul(ctypes.byref(T((0, 8), BF16)), ctypes.byref(B), ctypes.byref(T((0, 5), BF16)), None) == 0
+
+
+def test_gemm_noalloc_rejects_oversized_scratch():
+    """A decode-like bf16 Gemm (16 rows, K = 131328, N = 8176) whose split-K
+    partials (65 K ranges x 16 x 8176 x 4 bytes) exceed the 32 MiB static
+    scratch: OMM_ERR_SCRATCH, found on the host before any launch."""
+    L = om.lib()
+    M, N, K = 16, 8176, 131328
+    A, B, Y = T((M, K), BF16), T((N, K), BF16), T((M, N), BF16)
+    assert 65 * M * N * 4 > 32 * 1024 * 1024
+    assert L.omm_gemm_noalloc(ctypes.byref(A), ctypes.byref(B), None, 1.0, 0.0, 0, 1, ctypes.byref(Y), None) == -8
+    assert "scratch" in om.status_string(-8)
+    # argument errors come first, as for omm_gemm
+    assert L.omm_gemm_noalloc(None, ctypes.byref(B), None, 1.0, 0.0, 0, 1, ctypes.byref(Y), None) == -1
+    assert L.omm_gemm_noalloc(ctypes.byref(A), ctypes.byref(B), None, 1.0, 0.0, 0, 0, ctypes.byref(Y), None) == -3
 
 
 @pytest.mark.parametrize("cshape,ok", [((), True), ((1,), True), ((5,), True), ((1, 5), True), ((4, 1), True),
