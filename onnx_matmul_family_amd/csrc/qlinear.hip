@@ -667,6 +667,368 @@ __global__ __launch_bounds__(NT) void qlinear_kernel(QArgs p, int tiles_m, int t
     }
 }
 
+// ---------------------------------------------------------------------------
+// 16x16x64 form for int8 x int8 whole tiles (v_mfma_i32_16x16x64_i8).  The
+// same 256x256 tile and 4 waves, each wave's 128x128 block as 8 x 8 MFMA
+// tiles of 16x16; a 128-byte stage is two k-blocks of 64, each 64 MFMAs, on
+// the pipeline of the bf16 / fp16 16x16x32 loop (fragments one k-block ahead,
+// the barrier between the two k-blocks, stage kt+2's DMA spread over the
+// second).  On gfx950 the chip holds a higher shader clock under the 16x16
+// MFMAs than under the 32x32 ones (measured on the bf16 loops).
+//   a fragment (rows mnb .. mnb+15, k-block kb): lane l reads the 16 bytes of
+//     row mnb + l%16 at k 64 kb + 16 (l/16) -- the bf16 read, byte for byte.
+//   b fragment (columns nb .. nb+15): lane l holds column nb + l%16 at the same
+//     16 k: two transposing 8-row reads, 16-lane group g on rows 64 kb + 16 g
+//     (+ 0..7, + 8..15).  The two groups of a half-wave sit 16 rows apart, so
+//     the b tile's 16-byte chunk c of row r lives at c ^ bswz(r), bswz(r) =
+//     2 (r % 8) + (r / 16) % 2: rows 16 apart take chunks of opposite parity
+//     and the half-wave touches every bank once.
+// The MFMAs are tied inline assembly (the accumulators stay in their AGPRs,
+// as in the bf16 loop); no VALU instruction writes a fragment register (they
+// come straight from LDS), so no wait states are needed before them.  The
+// byte sums for the zero points are the 32x32 kernel's: each fragment is
+// summed (v_xor + v_sad_u8) by one of the two waves that read it, one dword
+// after every other MFMA.
+namespace q16 {
+using namespace core16;
+
+constexpr int NF = 8;  // fragments per wave and operand per k-block
+
+__device__ __forceinline__ int bswz(int r) { return ((r & 7) << 1) | ((r >> 4) & 1); }
+
+// DMA of the n-contiguous b tile: 128 k rows x 256 bytes per stage.  Block b =
+// rows 4b .. 4b+3 (one instruction, 1 KiB); lane p -> row 4b + p/16, physical
+// chunk p%16, which takes logical chunk (p%16) ^ bswz(row).  A wave fills
+// blocks 8 w + j; bswz of their rows depends on j only.
+struct BDma {
+    static constexpr int PER_WAVE = 8;
+    const char* base;
+    int64_t step;
+    uint32_t ldb;
+    uint32_t lane_off[PER_WAVE];
+
+    __device__ void init(const void* b, int64_t ld, int64_t n0, int lane) {
+        ldb = (uint32_t)ld;
+        base = (const char*)b + n0;
+        step = (int64_t)KB * ld;
+#pragma unroll
+        for (int j = 0; j < PER_WAVE; ++j) {
+            const int row = 4 * j + (lane >> 4);
+            lane_off[j] = (uint32_t)(lane >> 4) * ldb + ((uint32_t)((lane & 15) ^ bswz(row)) << 4);
+        }
+    }
+    __device__ __forceinline__ DmaCtx ctx(char* lds, int kt, bool live = true) const {
+        return DmaCtx{make_rsrc(base + (live ? (int64_t)kt * step : 0), live), lds_addr(lds)};
+    }
+    template <bool CHECKED>
+    __device__ __forceinline__ void one(const DmaCtx& c, int kt, int wave, int j) const {
+        static_assert(!CHECKED, "whole tiles only");
+        const int b = wave * PER_WAVE + j;
+        dma16u(c.r, c.l0 + b * 1024, lane_off[j] + (uint32_t)(b * 4) * ldb);
+    }
+};
+
+struct Frags {
+    i32x4_t a[NF], b[NF];
+    // fragment R of k-block kb: R < 8 -> a[R], else b[R - 8]
+    template <int R>
+    __device__ __forceinline__ void read_one(const char* st, int kb, int lane, int wm, int wn) {
+        if constexpr (R < NF) {
+            a[R] = __builtin_bit_cast(i32x4_t, read_frag16<BMQ, true>(st, wm * 128 + 16 * R, kb, lane));
+        } else {
+            const int g = lane >> 4, i = lane & 15;
+            const int krow = 64 * kb + 16 * g + (i >> 1);
+            const int ncol = wn * 128 + 16 * (R - NF) + 8 * (i & 1);
+            const int off = A_BYTES + krow * BNQ + ((((ncol >> 4) ^ bswz(krow))) << 4) + (ncol & 15);
+            // rows krow + 8 share krow's swizzle (same r % 8, same 16-row half)
+            const i32x2_t lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32(OMM_LDS(i32x2_t, st + off));
+            const i32x2_t hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32(OMM_LDS(i32x2_t, st + off + 8 * BNQ));
+            b[R - NF] = i32x4_t{lo.x, lo.y, hi.x, hi.y};
+        }
+    }
+    __device__ __forceinline__ void read(const char* st, int kb, int lane, int wm, int wn) {
+        static_for<0, 2 * NF>([&](auto rc) { read_one<decltype(rc)::value>(st, kb, lane, wm, wn); });
+    }
+};
+
+template <bool Z>
+__device__ __forceinline__ void mfma_i8(i32x4_t& acc, const i32x4_t& a, const i32x4_t& b) {
+    if constexpr (Z)
+        asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+    else
+        asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void acc_fence(i32x4_t (&acc)[NF][NF]) {
+#pragma unroll
+    for (int i = 0; i < NF; ++i)
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"
+                     : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
+                       "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
+}
+
+// Position of fragment f in the read order of a k-block (frag_order(8, 8, .)).
+constexpr int read_pos(int f) {
+    for (int r = 0; r < 2 * NF; ++r)
+        if (frag_order(NF, NF, r) == f) return r;
+    return -1;
+}
+// The d-th (0..31) dword a wave of role R sums in a k-block: its 8 fragments
+// (a 4R .. 4R+3, b 4R .. 4R+3) in the order they were read, 4 dwords each.
+// Returns fragment id (0..7 a, 8..15 b) * 4 + dword.
+constexpr int sum_slot(int R, int d) {
+    int ids[8] = {}, n = 0;
+    for (int r = 0; r < 2 * NF; ++r) {
+        const int f = frag_order(NF, NF, r);
+        const int q = f < NF ? f : f - NF;
+        if (q / 4 == R) ids[n++] = f;
+    }
+    return ids[d / 4] * 4 + d % 4;
+}
+
+// One k-block: MFMA x on tile (x/8, x%8) of `cur`; the 16 fragment reads of
+// k-block kb of `lds` into `nxt` and this wave's DMA instructions D0 .. D1-1
+// of stage kt (into buffer X) spread evenly; one dword of byte sums after
+// every other MFMA.
+template <int R, bool Z, int D0, int D1, class SA, class SB>
+__device__ __forceinline__ void kblock(i32x4_t (&acc)[NF][NF], int (&rs)[4], int (&cs)[4], const Frags& cur,
+                                       Frags& nxt, const char* lds, int kb, char* X, const SA& sa, const SB& sb,
+                                       int kt, bool live, int lane, int wm, int wn, int wave) {
+    constexpr int NM = NF * NF, NR = 2 * NF, ND = D1 - D0, LA = SA::PER_WAVE;
+    DmaCtx ca, cb;
+    if constexpr (ND > 0) {
+        ca = sa.ctx(X, kt, live);
+        cb = sb.ctx(X + A_BYTES, kt, live);
+    }
+    static_for<0, NM>([&](auto xc) {
+        constexpr int x = decltype(xc)::value;
+        mfma_i8<Z>(acc[x / NF][x % NF], cur.b[x % NF], cur.a[x / NF]);
+        if constexpr (ND > 0)
+            static_for<D0 + (x * ND + NM - 1) / NM, D0 + ((x + 1) * ND + NM - 1) / NM>(
+                [&](auto dc) { dma_one<false, LA, decltype(dc)::value>(sa, sb, ca, cb, kt, wave); });
+        static_for<(x * NR + NM - 1) / NM, ((x + 1) * NR + NM - 1) / NM>([&](auto rc) {
+            nxt.template read_one<frag_order(NF, NF, decltype(rc)::value)>(lds, kb, lane, wm, wn);
+        });
+        if constexpr (x % 2 == 1) {
+            constexpr int slot = sum_slot(R, x / 2), f = slot / 4, w = slot % 4;
+            if constexpr (f < NF)
+                rs[f % 4] = bytesum1(cur.a[f][w], rs[f % 4]);
+            else
+                cs[(f - NF) % 4] = bytesum1(cur.b[f - NF][w], cs[(f - NF) % 4]);
+        }
+        fence_sched();
+    });
+}
+
+template <int R, bool Z, class SA, class SB>
+__device__ __forceinline__ void stage(i32x4_t (&acc)[NF][NF], int (&rs)[4], int (&cs)[4], Frags& fc, Frags& fn,
+                                      char* X, char* Y, const SA& sa, const SB& sb, int kt, int nk, int lane, int wm,
+                                      int wn, int wave) {
+    constexpr int LD = SA::PER_WAVE + SB::PER_WAVE;
+    fence_sched();
+    kblock<R, Z, 0, 0>(acc, rs, cs, fc, fn, X, 1, X, sa, sb, kt, false, lane, wm, wn, wave);
+    wait_vm<0>();     // this wave's DMA of stage kt+1 has landed
+    __syncthreads();  // ... every wave's; every read of X is done
+    fence_sched();
+    kblock<R, false, 0, LD>(acc, rs, cs, fn, fc, Y, 0, X, sa, sb, kt + 2, kt + 2 < nk, lane, wm, wn, wave);
+}
+
+// nk >= 1 stages; an odd count runs one more stage of zeros.  On return no
+// DMA is in flight and the accumulators are safe to read.
+template <int R, class SA, class SB>
+__device__ __forceinline__ void loop(i32x4_t (&acc)[NF][NF], int (&rs)[4], int (&cs)[4], char* __restrict__ s0,
+                                     char* __restrict__ s1, const SA& sa, const SB& sb, int nk, int lane, int wm,
+                                     int wn, int wave) {
+    constexpr int LA = SA::PER_WAVE, LD = SA::PER_WAVE + SB::PER_WAVE;
+    {
+        const DmaCtx a0 = sa.ctx(s0, 0, true), b0 = sb.ctx(s0 + A_BYTES, 0, true);
+        static_for<0, LD>([&](auto dc) { dma_one<false, LA, decltype(dc)::value>(sa, sb, a0, b0, 0, wave); });
+        const DmaCtx a1 = sa.ctx(s1, 1, nk > 1), b1 = sb.ctx(s1 + A_BYTES, 1, nk > 1);
+        static_for<0, LD>([&](auto dc) { dma_one<false, LA, decltype(dc)::value>(sa, sb, a1, b1, 1, wave); });
+    }
+    wait_vm<LD>();
+    __syncthreads();
+    Frags fc, fn;
+    fc.read(s0, 0, lane, wm, wn);
+    stage<R, true>(acc, rs, cs, fc, fn, s0, s1, sa, sb, 0, nk, lane, wm, wn, wave);
+    stage<R, false>(acc, rs, cs, fc, fn, s1, s0, sa, sb, 1, nk, lane, wm, wn, wave);
+    for (int kt = 2; kt < nk; kt += 2) {
+        stage<R, false>(acc, rs, cs, fc, fn, s0, s1, sa, sb, kt, nk, lane, wm, wn, wave);
+        stage<R, false>(acc, rs, cs, fc, fn, s1, s0, sa, sb, kt + 1, nk, lane, wm, wn, wave);
+    }
+    wait_vm<0>();
+    acc_fence(acc);
+}
+
+// c + a * b on 24-bit signed operands, low 32 bits (v_mad_i32_i24; the
+// compiler would otherwise issue two multiplies and a three-way add for two
+// of these)
+__device__ __forceinline__ int mad24(int a, int b, int c) {
+    int r;
+    asm("v_mad_i32_i24 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// Requantisation of the wave's 128 x 128 block (lane l, tile (i, j), register
+// e: row 16 i + l%16, column 16 j + 4 (l/16) + e) with the per-row / per-
+// column terms in LDS; the same arithmetic as q_epilogue_full.  (zy is added
+// after the rounding constant, not folded into it: x + (1.5 * 2^23 + zy)
+// would break ties towards an even sum, which differs from rint(x) + zy for
+// odd zy.)  The bytes go
+// through this wave's 16 KiB of `stage` (row r of 128 bytes, 16-byte chunk c
+// in slot c ^ (r / 2 % 8)) and leave as whole 128-byte row segments.
+template <bool MARK>
+__device__ __forceinline__ void epilogue(const QArgs& p, const i32x4_t (&acc)[NF][NF], uint8_t* __restrict__ y,
+                                         const uint32_t* U, const int* ZA, const float* SA, const uint32_t* CB,
+                                         const int* ZB, const float* SB, int64_t m0, int64_t n0, int lane, int wm,
+                                         int wn, float sy, float zyf, float lo, float hi, char* stage) {
+    constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
+    const float r = 1.0f / sy;
+    const float tlo = MAGIC + lo, thi = MAGIC + hi;
+    const int g = lane >> 4;
+    int Um[NF], nza[NF];
+    float sa[NF];
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+        const int mloc = wm * 128 + 16 * i + (lane & 15);
+        Um[i] = (int)U[mloc];
+        nza[i] = -ZA[mloc];
+        sa[i] = SA[mloc];
+    }
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+        const int nloc = wn * 128 + 16 * j + 4 * g;
+        const i32x4_t cb = *(const i32x4_t*)(CB + nloc);
+        const i32x4_t zb = *(const i32x4_t*)(ZB + nloc);
+        const f32x4_t sb = *(const f32x4_t*)(SB + nloc);
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+            uint32_t bytes[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                // |U| <= 2^23, |colsum| <= 2^22, |z| <= 128: exact 24-bit products
+                const int s32 = mad24(nza[i], cb[e], mad24(-zb[e], Um[i], acc[i][j][e]));
+                const float prod = sa[i] * sb[e];
+                float mult;
+                if constexpr (MARK) {
+                    const float q0 = prod * r;
+                    mult = __builtin_fmaf(__builtin_fmaf(-q0, sy, prod), r, q0);
+                } else {
+                    mult = prod / sy;
+                }
+                const float x = (float)s32 * mult;
+                const float t = __builtin_amdgcn_fmed3f((x + MAGIC) + zyf, tlo, thi);
+                bytes[e] = __float_as_uint(t);
+            }
+            const uint32_t lo2 = __builtin_amdgcn_perm(bytes[1], bytes[0], 0x0c0c0400u);
+            const uint32_t hi2 = __builtin_amdgcn_perm(bytes[3], bytes[2], 0x0c0c0400u);
+            const int row = 16 * i + (lane & 15);
+            *(uint32_t*)(stage + row * 128 + ((j ^ ((row >> 1) & 7)) << 4) + 4 * g) = lo2 | (hi2 << 16);
+        }
+    }
+    uint8_t* __restrict__ yb = y + (m0 + wm * 128) * p.ldy + n0 + wn * 128;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int row = 8 * k + (lane >> 3), c = lane & 7;
+        const u32x4_t d = *(const u32x4_t*)(stage + row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
+        *(u32x4_t*)(yb + (int64_t)row * p.ldy + 16 * c) = d;
+    }
+}
+
+}  // namespace q16
+
+// int8 x int8 -> int8 / uint8 on whole tiles (M, N multiples of 256, K of 128
+// up to 32768, 16-byte aligned operands, checked on the host), the 16x16x64 loop.
+__global__ __launch_bounds__(NT) void qlinear16_kernel(QArgs p, int tiles_m, int tiles_n) {
+    __shared__ __attribute__((aligned(1024))) char smem[STAGE];
+    __shared__ __attribute__((aligned(1024))) char smem1[STAGE];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int T = tiles_m * tiles_n;
+    const int w = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+    const int z = w / T;
+    int tm, tn;
+    grouped_order(w - z * T, tiles_m, tiles_n, 4, tm, tn);
+    const int64_t z0 = z / p.nb1, z1 = z - z0 * p.nb1;
+    const uint8_t* a = (const uint8_t*)p.a + z0 * p.a_bs0 + z1 * p.a_bs1;
+    const uint8_t* b = (const uint8_t*)p.b + z0 * p.b_bs0 + z1 * p.b_bs1;
+    uint8_t* y = (uint8_t*)p.y + z0 * p.y_bs0 + z1 * p.y_bs1;
+    const int64_t m0 = (int64_t)tm * BMQ, n0 = (int64_t)tn * BNQ;
+    const int64_t M = p.M, N = p.N, K = p.K;
+
+    // this thread's row (m0 + t) and column (n0 + t) parameters and the output
+    // scale / zero point, loaded now so that their latency hides behind the K loop
+    auto ldscale = [&](const void* q, int64_t i) {
+        return p.scale_f16 ? from_bits<1>(((const uint16_t*)q)[i]) : ((const float*)q)[i];
+    };
+    const int64_t apo = z0 * p.ap_bs0 + z1 * p.ap_bs1 + (m0 + t) * p.ap_sm;
+    const int64_t bpo = z0 * p.bp_bs0 + z1 * p.bp_bs1 + (n0 + t) * p.bp_sn;
+    const int za_t = ldzp(p.a_zp, apo, false), zb_t = ldzp(p.b_zp, bpo, false);
+    const float sa_t = ldscale(p.a_scale, apo), sb_t = ldscale(p.b_scale, bpo);
+    const float sy = ldscale(p.y_scale, 0);
+    const float zyf = (float)(p.y_u8 ? (int)((const uint8_t*)p.y_zp)[0] : (int)((const int8_t*)p.y_zp)[0]);
+
+    i32x4_t acc[q16::NF][q16::NF];
+    int rs[4] = {0, 0, 0, 0}, cs[4] = {0, 0, 0, 0};
+    const int nk = (int)(K / KB);
+    {
+        core16::DmaSrc<BMQ, true, 1> sa;
+        q16::BDma sb;
+        sa.init(a, p.lda, m0, M, K, lane);
+        sb.init(b, p.ldb, n0, lane);
+        if ((wm ^ wn) == 0)
+            q16::loop<0>(acc, rs, cs, smem, smem1, sa, sb, nk, lane, wm, wn, wave);
+        else
+            q16::loop<1>(acc, rs, cs, smem, smem1, sa, sb, nk, lane, wm, wn, wave);
+    }
+    // every lane summed 32 bytes (each +128) per stage into each of rs / cs
+    const int nk_run = (nk + 1) & ~1;
+    const uint32_t bias = 128u * 32u * (uint32_t)nk_run;
+    __syncthreads();  // every wave is done with the K buffers
+
+    // full row / column sums: the 4 lane groups hold 4 k-slices of each row /
+    // column.  The wave of role R = wm ^ wn summed a fragments 4R .. 4R+3 and
+    // b fragments 4R .. 4R+3.
+    int* rowsum = (int*)smem;
+    int* colsum = (int*)smem + 256;
+    const int role = wm ^ wn;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        uint32_t r = (uint32_t)rs[q] - bias;
+        r += (uint32_t)__shfl_xor((int)r, 16);
+        r += (uint32_t)__shfl_xor((int)r, 32);
+        if (lane < 16) rowsum[wm * 128 + 16 * (4 * role + q) + lane] = (int)r;
+        uint32_t c = (uint32_t)cs[q] - bias;
+        c += (uint32_t)__shfl_xor((int)c, 16);
+        c += (uint32_t)__shfl_xor((int)c, 32);
+        if (lane < 16) colsum[wn * 128 + 16 * (4 * role + q) + lane] = (int)c;
+    }
+    __syncthreads();
+
+    uint32_t* U = (uint32_t*)smem + 512;
+    int* ZA = (int*)smem + 768;
+    float* SA = (float*)smem + 1024;
+    uint32_t* CB = (uint32_t*)smem + 1280;
+    int* ZB = (int*)smem + 1536;
+    float* SB = (float*)smem + 1792;
+    auto tame = [](float v) {
+        const float av = __builtin_fabsf(v);
+        return av == 0.0f || (av >= 0x1p-30f && av <= 0x1p30f);
+    };
+    U[t] = (uint32_t)rowsum[t] - (uint32_t)K * (uint32_t)za_t;
+    ZA[t] = za_t;
+    SA[t] = sa_t;
+    CB[t] = (uint32_t)colsum[t];
+    ZB[t] = zb_t;
+    SB[t] = sb_t;
+    const int scales_ok = __syncthreads_and(tame(sa_t) && tame(sb_t) && sy != 0.0f && tame(sy));
+    const float lo = p.y_u8 ? 0.0f : -128.0f, hi = p.y_u8 ? 255.0f : 127.0f;
+    char* stg = smem1 + wave * (STAGE / 4);
+    if (scales_ok)
+        q16::epilogue<true>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi, stg);
+    else
+        q16::epilogue<false>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi, stg);
+}
+
 template <bool AU8, bool BU8, int MODE>
 hipError_t launch_q(const QArgs& a, hipStream_t s) {
     const int64_t tiles_m = (a.M + BMQ - 1) / BMQ, tiles_n = (a.N + BNQ - 1) / BNQ;
@@ -699,7 +1061,14 @@ hipError_t launch_qlinear(const QArgs& a, hipStream_t s) {
                      (a.K % (2 * KB) == 0 || (!a.a_u8 && !a.b_u8));
     if (!vec) return launch_q_types<0>(a, s);
     const bool full = a.M % BMQ == 0 && a.N % BNQ == 0 && a.K % KB == 0 && a.K > 0 && a.K <= 32768 &&
-                      a.ldy % 4 == 0;
+                      a.ldy % 16 == 0 && ((uintptr_t)a.y & 15) == 0 && a.y_bs0 % 16 == 0 && a.y_bs1 % 16 == 0;
+    if (full && !a.a_u8 && !a.b_u8) {
+        const int64_t tiles_m = a.M / BMQ, tiles_n = a.N / BNQ;
+        const int64_t total = tiles_m * tiles_n * a.nb0 * a.nb1;
+        if (total > 0x7fffffff) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(qlinear16_kernel, dim3((unsigned)total), dim3(NT), 0, s, a, (int)tiles_m, (int)tiles_n);
+        return hipGetLastError();
+    }
     return full ? launch_q_types<2>(a, s) : launch_q_types<1>(a, s);
 }
 

@@ -197,3 +197,34 @@ def test_full_tiles_scale_ranges(ta, tb, scales):
     assert np.array_equal(got, ref), (scales, np.argwhere(got != ref)[:5])
     if scales != "zeros":
         assert len(np.unique(got)) > 50  # the test is not trivially saturated
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 512, 128), (512, 768, 384), (256, 512, 640), (768, 256, 1152),
+                                   (256, 256, 32768)])
+def test_int8_whole_tiles_stage_counts(M, N, K):
+    """int8 x int8 on whole 256x256 tiles (the 16x16x64 kernel): one stage,
+    odd stage counts (the loop then runs one stage of zeros, whose bytes the
+    row / column sums must not count), several tile rows and columns, and the
+    largest K of that kernel; per-row a and per-column b parameters, uint8
+    output, compared in full and bit for bit."""
+    rng = np.random.default_rng(M + 3 * N + 7 * K)
+    a, b = rint(rng, (M, K), np.int8), rint(rng, (K, N), np.int8)
+    az, bz = rint(rng, (M, 1), np.int8, -16, 16), rint(rng, (1, N), np.int8, -16, 16)
+    asc = synth.uniform(rng, (M, 1), 0.002, 0.01)
+    bsc = synth.uniform(rng, (1, N), 0.002, 0.01)
+    ys = np.float32(0.05 * np.sqrt(K / 4096))
+    got, ref = run(a, asc, az, b, bsc, bz, ys, np.array(128, np.uint8))
+    assert np.array_equal(got, ref), np.argwhere(got != ref)[:5]
+    assert len(np.unique(got)) > 100
+
+
+def test_int8_whole_tiles_batched_broadcast():
+    """The whole-tile kernel over two batch levels (a broadcast over the second),
+    per-row / per-column parameters batched like their operands."""
+    rng = np.random.default_rng(8)
+    a, b = rint(rng, (2, 1, 256, 256), np.int8), rint(rng, (1, 3, 256, 512), np.int8)
+    az, bz = rint(rng, (2, 1, 256, 1), np.int8, -16, 16), rint(rng, (1, 3, 1, 512), np.int8, -16, 16)
+    asc, bsc = synth.uniform(rng, (2, 1, 256, 1), 0.002, 0.01), synth.uniform(rng, (1, 3, 1, 512), 0.002, 0.01)
+    got, ref = run(a, asc, az, b, bsc, bz, np.float32(0.02), np.array(-3, np.int8))
+    assert got.shape == (2, 3, 256, 512)
+    assert np.array_equal(got, ref), np.argwhere(got != ref)[:5]
