@@ -13,7 +13,8 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libomm.so")
+# OMM_LIB names another build of the same library (the sanitizer build of the host code)
+LIB_PATH = os.environ.get("OMM_LIB") or os.path.join(HERE, "libomm.so")
 
 MAX_DIMS = 8
 _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.float64: 3,

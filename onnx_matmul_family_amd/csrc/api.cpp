@@ -2,7 +2,10 @@
 // broadcast resolution and kernel dispatch.  Everything here runs on the host
 // before any launch; the kernels live in the .hip files.
 #include <hip/hip_runtime.h>
+#include <stdarg.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -11,6 +14,39 @@
 
 #include "omm.h"
 #include "kernels.hpp"
+
+namespace omm {
+
+bool log_enabled() {
+    static const bool on = [] {
+        const char* v = getenv("OMM_LOG");
+        return v && *v && strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
+void log_choice(const char* fmt, ...) {
+    if (!log_enabled()) return;
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    fprintf(stderr, "omm: %s\n", buf);
+}
+
+int tile_override() {
+    static const int t = [] {
+        const char* v = getenv("OMM_TILE");
+        if (!v) return 0;
+        if (strcmp(v, "256x256x64") == 0) return 256;
+        if (strcmp(v, "128x128x64") == 0) return 128;
+        return 0;
+    }();
+    return t;
+}
+
+}  // namespace omm
 
 using omm::DenseArgs;
 using omm::GroupedArgs;

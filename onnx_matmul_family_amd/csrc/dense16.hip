@@ -814,7 +814,12 @@ Plan16 plan16(const DenseArgs& a) {
                          (a.b_kmajor ? 256 * a.ldb * 2 : 64 * a.ldb * 2) < (1LL << 31);
     const bool vec = a_ok && b_ok && y_ok && span_ok;
     const int64_t big_tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256) * a.nb0 * a.nb1;
-    if (vec && big_tiles >= 256) {
+    const int forced = tile_override();
+    if (vec && forced == 128) {
+        pl.kind = Plan16::T128_VEC;
+        return pl;
+    }
+    if (vec && (big_tiles >= 256 || forced == 256)) {
         // every tile full: epilogue without bounds checks (8-byte stores need
         // N and the row stride to be multiples of 4)
         const bool full = a.M % 256 == 0 && a.N % 256 == 0 && a.K % KSTEP == 0 && a.K > 0 && a.ldy % 4 == 0;
@@ -924,9 +929,30 @@ hipError_t run16(const DenseArgs& a, const Plan16& pl, float* ws, hipStream_t s)
 // scratch == nullptr: split-K partials in stream-ordered memory taken and
 // returned around the launch; otherwise the caller's scratch (its size checked
 // against the plan before anything is enqueued).
+const char* plan_name(const Plan16& pl) {
+    switch (pl.kind) {
+        case Plan16::T16_FULL: return "256x256x64 tiles, 16x16x32 MFMA, DMA, whole tiles, no C";
+        case Plan16::T16_BIAS: return "256x256x64 tiles, 16x16x32 MFMA, DMA, whole tiles, bias row";
+        case Plan16::T16_ANY: return "256x256x64 tiles, 16x16x32 MFMA, DMA, ragged tiles / any C";
+        case Plan16::SKINNY_NMAJ: return "skinny rows against n-contiguous B (vector ALU, B streamed once)";
+        case Plan16::SKINNY1: return "skinny rows against k-contiguous B (16 columns per workgroup)";
+        case Plan16::SKINNY_SPLIT: return "skinny rows, K split over workgroups + fixed-order reduction";
+        case Plan16::SPLIT128: return "128x128x64 tiles, K split over workgroups + fixed-order reduction";
+        case Plan16::T128_VEC: return "128x128x64 tiles, 32x32x16 MFMA, DMA";
+        case Plan16::T128_REG: return "128x128x64 tiles, 32x32x16 MFMA, register-staged loads";
+    }
+    return "?";
+}
+
 template <int DT>
 hipError_t launch_dt(const DenseArgs& a, hipStream_t s, const DenseScratch* scratch) {
     const Plan16 pl = plan16(a);
+    if (log_enabled())
+        log_choice("%s M=%lld N=%lld K=%lld batches=%lld A %s B %s: %s%s splits=%lld scratch=%s", DT == 0 ? "bf16" : "fp16",
+                   (long long)a.M, (long long)a.N, (long long)a.K, (long long)(a.nb0 * a.nb1),
+                   a.a_kmajor ? "k-contiguous" : "m-contiguous", a.b_kmajor ? "k-contiguous" : "n-contiguous",
+                   plan_name(pl), tile_override() ? " (OMM_TILE)" : "", (long long)pl.splits,
+                   pl.ws_bytes == 0 ? "none" : scratch ? "static" : "stream-ordered");
     if (pl.ws_bytes == 0) return run16<DT>(a, pl, nullptr, s);
     if (scratch) {
         if (!scratch->ptr || pl.ws_bytes > scratch->bytes) return hipErrorInvalidValue;

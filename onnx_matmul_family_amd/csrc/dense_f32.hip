@@ -121,6 +121,8 @@ hipError_t launch_dense_f32(const DenseArgs& a, hipStream_t s) {
     const int64_t total = tiles_m * tiles_n * a.nb0 * a.nb1;
     if (total <= 0) return hipSuccess;
     if (total > 0x7fffffff) return hipErrorInvalidValue;
+    log_choice("fp32 M=%lld N=%lld K=%lld batches=%lld: 64x64x64 tiles, 32x32x2 fp32 MFMA, %lld workgroups",
+               (long long)a.M, (long long)a.N, (long long)a.K, (long long)(a.nb0 * a.nb1), (long long)total);
     hipLaunchKernelGGL(dense_f32_kernel, dim3((unsigned)total), dim3(256), 0, s, a, (int)tiles_m, (int)tiles_n);
     return hipGetLastError();
 }

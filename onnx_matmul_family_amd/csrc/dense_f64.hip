@@ -200,6 +200,8 @@ hipError_t launch_dense_f64(const DenseArgs& a, hipStream_t s) {
     if (total <= 0) return hipSuccess;
     if (total > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)total);
+    log_choice("fp64 M=%lld N=%lld K=%lld batches=%lld: 128x128x16 tiles, 16x16x4 fp64 MFMA, %lld workgroups",
+               (long long)a.M, (long long)a.N, (long long)a.K, (long long)(a.nb0 * a.nb1), (long long)total);
     if (a.a_kmajor && a.b_kmajor)
         hipLaunchKernelGGL((dense_f64_kernel<true, true>), grid, dim3(256), 0, s, a, (int)tiles_m, (int)tiles_n);
     else if (a.a_kmajor)

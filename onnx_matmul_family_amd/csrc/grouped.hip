@@ -1361,6 +1361,10 @@ hipError_t launch_grouped_fp(const GroupedArgs& a, int dt, int wq, void* ws, hip
     const dim3 grid((unsigned)(max_mtiles * tiles_n));
     const char* wsc = (const char*)ws;
     const int tn = (int)tiles_n;
+    log_choice("grouped %s%s M=%lld S=%lld K=%lld N=%lld G=%lld: 128x128x16 routed tiles, %s MFMA",
+               dt == 3 ? "fp64" : "fp32", wq ? " (int8/uint8 weights, dequantised on load)" : "", (long long)a.M,
+               (long long)a.S, (long long)a.K, (long long)a.N, (long long)a.G,
+               dt == 3 ? "16x16x4 fp64" : "16x16x4 fp32");
     if (dt == 3)
         hipLaunchKernelGGL((grouped_fp_kernel<double, 0>), grid, dim3(256), 0, s, a, wsc, tn);
     else if (wq == 0)
@@ -1395,6 +1399,10 @@ hipError_t launch_grouped_dq(const GroupedArgs& a, int dt, void* ws, hipStream_t
     const bool dma = fast && a.K % core16::KSTEP == 0 && a.N % 16 == 0 && al(a.weights, 16) &&
                      (!a.wzp || al(a.wzp, 16)) && core16::KSTEP * a.N < (1LL << 31) &&
                      a.nkb * a.N * 2 < (1LL << 31);
+    log_choice("grouped %s over %s weights, block %lld, M=%lld S=%lld K=%lld N=%lld G=%lld: 256x256x64 routed tiles, %s",
+               dt == 0 ? "bf16" : "fp16", qu8 ? "uint8" : "int8", (long long)a.bs, (long long)a.M, (long long)a.S,
+               (long long)a.K, (long long)a.N, (long long)a.G,
+               dma ? "weights by DMA, dequantised in LDS fragments" : fast ? "weights register-staged" : "element-wise");
     if (dma) {
         if (dt == 0) {
             if (qu8) hipLaunchKernelGGL((grouped16_dq_dma_kernel<0, true>), grid, dim3(256), 0, s, a, wsc, tn);
@@ -1433,6 +1441,9 @@ hipError_t launch_grouped(const GroupedArgs& a, int dt, void* ws, hipStream_t s)
                      a.K > 0;  // the DMA K loop runs at least one stage
     dim3 grid((unsigned)(max_mtiles * tiles_n));
     const char* wsc = (const char*)ws;
+    log_choice("grouped %s M=%lld S=%lld K=%lld N=%lld G=%lld: 256x256x64 routed tiles, %s", dt == 0 ? "bf16" : "fp16",
+               (long long)a.M, (long long)a.S, (long long)a.K, (long long)a.N, (long long)a.G,
+               vec ? "16x16x32 MFMA, DMA (gathered rows)" : "32x32x16 MFMA, element-wise loads");
     if (dt == 0) {
         if (vec) hipLaunchKernelGGL((grouped16_kernel<0, true>), grid, dim3(256), 0, s, a, wsc, (int)tiles_n);
         else hipLaunchKernelGGL((grouped16_kernel<0, false>), grid, dim3(256), 0, s, a, wsc, (int)tiles_n);

@@ -75,6 +75,15 @@ struct DenseScratch {
     size_t bytes;
 };
 
+// Host-side diagnostics and tuning, read from the environment once per process:
+//   OMM_LOG=1          every launch prints its kernel choice to stderr
+//   OMM_TILE=MxNxK     bf16 / fp16 MatMul / Gemm: force the 256x256x64 or the
+//                      128x128x64 tile path (bench sweeps; honoured where the
+//                      16-byte-load path applies, ignored otherwise)
+bool log_enabled();
+void log_choice(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+int tile_override();  // 0 (none), 256 or 128
+
 // dt: 0 = bf16, 1 = fp16.  scratch == nullptr: split-K partials go to
 // stream-ordered memory (hipMallocAsync / hipFreeAsync on s); otherwise to
 // scratch, which must hold dense16_scratch_bytes(a).
