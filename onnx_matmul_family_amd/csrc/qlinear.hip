@@ -859,6 +859,16 @@ __device__ __forceinline__ void loop(i32x4_t (&acc)[NF][NF], int (&rs)[4], int (
     acc_fence(acc);
 }
 
+// An accumulator register read where it is used (the register allocator
+// would otherwise copy most of the AGPRs into VGPRs right after the K loop and
+// run short of VGPRs for the epilogue).  The loop's closing fence provides the
+// wait states between the last MFMA and these reads.
+__device__ __forceinline__ int aread(int a) {
+    int v;
+    asm("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+    return v;
+}
+
 // c + a * b on 24-bit signed operands, low 32 bits (v_mad_i32_i24; the
 // compiler would otherwise issue two multiplies and a three-way add for two
 // of these)
@@ -906,7 +916,7 @@ __device__ __forceinline__ void epilogue(const QArgs& p, const i32x4_t (&acc)[NF
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 // |U| <= 2^23, |colsum| <= 2^22, |z| <= 128: exact 24-bit products
-                const int s32 = mad24(nza[i], cb[e], mad24(-zb[e], Um[i], acc[i][j][e]));
+                const int s32 = mad24(nza[i], cb[e], mad24(-zb[e], Um[i], aread(acc[i][j][e])));
                 const float prod = sa[i] * sb[e];
                 float mult;
                 if constexpr (MARK) {
@@ -923,6 +933,8 @@ __device__ __forceinline__ void epilogue(const QArgs& p, const i32x4_t (&acc)[NF
             const uint32_t hi2 = __builtin_amdgcn_perm(bytes[3], bytes[2], 0x0c0c0400u);
             const int row = 16 * i + (lane & 15);
             *(uint32_t*)(stage + row * 128 + ((j ^ ((row >> 1) & 7)) << 4) + 4 * g) = lo2 | (hi2 << 16);
+            // two 16x16 tiles at a time: their eight outputs' chains interleave
+            if (i % 2 == 1) fence_sched();
         }
     }
     uint8_t* __restrict__ yb = y + (m0 + wm * 128) * p.ldy + n0 + wn * 128;
@@ -936,37 +948,15 @@ __device__ __forceinline__ void epilogue(const QArgs& p, const i32x4_t (&acc)[NF
 
 }  // namespace q16
 
-// int8 x int8 -> int8 / uint8 on whole tiles (M, N multiples of 256, K of 128
-// up to 32768, 16-byte aligned operands, checked on the host), the 16x16x64 loop.
-__global__ __launch_bounds__(NT) void qlinear16_kernel(QArgs p, int tiles_m, int tiles_n) {
-    __shared__ __attribute__((aligned(1024))) char smem[STAGE];
-    __shared__ __attribute__((aligned(1024))) char smem1[STAGE];
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int T = tiles_m * tiles_n;
-    const int w = xcd_remap((int)blockIdx.x, (int)gridDim.x);
-    const int z = w / T;
-    int tm, tn;
-    grouped_order(w - z * T, tiles_m, tiles_n, 4, tm, tn);
-    const int64_t z0 = z / p.nb1, z1 = z - z0 * p.nb1;
-    const uint8_t* a = (const uint8_t*)p.a + z0 * p.a_bs0 + z1 * p.a_bs1;
-    const uint8_t* b = (const uint8_t*)p.b + z0 * p.b_bs0 + z1 * p.b_bs1;
-    uint8_t* y = (uint8_t*)p.y + z0 * p.y_bs0 + z1 * p.y_bs1;
-    const int64_t m0 = (int64_t)tm * BMQ, n0 = (int64_t)tn * BNQ;
-    const int64_t M = p.M, N = p.N, K = p.K;
-
-    // this thread's row (m0 + t) and column (n0 + t) parameters and the output
-    // scale / zero point, loaded now so that their latency hides behind the K loop
-    auto ldscale = [&](const void* q, int64_t i) {
-        return p.scale_f16 ? from_bits<1>(((const uint16_t*)q)[i]) : ((const float*)q)[i];
-    };
-    const int64_t apo = z0 * p.ap_bs0 + z1 * p.ap_bs1 + (m0 + t) * p.ap_sm;
-    const int64_t bpo = z0 * p.bp_bs0 + z1 * p.bp_bs1 + (n0 + t) * p.bp_sn;
-    const int za_t = ldzp(p.a_zp, apo, false), zb_t = ldzp(p.b_zp, bpo, false);
-    const float sa_t = ldscale(p.a_scale, apo), sb_t = ldscale(p.b_scale, bpo);
-    const float sy = ldscale(p.y_scale, 0);
-    const float zyf = (float)(p.y_u8 ? (int)((const uint8_t*)p.y_zp)[0] : (int)((const int8_t*)p.y_zp)[0]);
-
+// Everything after the set-up of qlinear16_kernel, for the waves of role R =
+// wm ^ wn (which fragments a wave sums is a template argument, and the
+// accumulators never meet a branch merge, which would copy all 256 of them).
+template <int R>
+__device__ __forceinline__ void qlinear16_tile(const QArgs& p, char* smem, char* smem1, const uint8_t* a,
+                                               const uint8_t* b, uint8_t* y, int64_t m0, int64_t n0, int za_t,
+                                               int zb_t, float sa_t, float sb_t, float sy, float zyf, int t,
+                                               int lane, int wave, int wm, int wn) {
+    const int64_t M = p.M, K = p.K;
     i32x4_t acc[q16::NF][q16::NF];
     int rs[4] = {0, 0, 0, 0}, cs[4] = {0, 0, 0, 0};
     const int nk = (int)(K / KB);
@@ -975,10 +965,7 @@ __global__ __launch_bounds__(NT) void qlinear16_kernel(QArgs p, int tiles_m, int
         q16::BDma sb;
         sa.init(a, p.lda, m0, M, K, lane);
         sb.init(b, p.ldb, n0, lane);
-        if ((wm ^ wn) == 0)
-            q16::loop<0>(acc, rs, cs, smem, smem1, sa, sb, nk, lane, wm, wn, wave);
-        else
-            q16::loop<1>(acc, rs, cs, smem, smem1, sa, sb, nk, lane, wm, wn, wave);
+        q16::loop<R>(acc, rs, cs, smem, smem1, sa, sb, nk, lane, wm, wn, wave);
     }
     // every lane summed 32 bytes (each +128) per stage into each of rs / cs
     const int nk_run = (nk + 1) & ~1;
@@ -986,21 +973,20 @@ __global__ __launch_bounds__(NT) void qlinear16_kernel(QArgs p, int tiles_m, int
     __syncthreads();  // every wave is done with the K buffers
 
     // full row / column sums: the 4 lane groups hold 4 k-slices of each row /
-    // column.  The wave of role R = wm ^ wn summed a fragments 4R .. 4R+3 and
-    // b fragments 4R .. 4R+3.
+    // column.  The wave of role R summed a fragments 4R .. 4R+3 and b
+    // fragments 4R .. 4R+3.
     int* rowsum = (int*)smem;
     int* colsum = (int*)smem + 256;
-    const int role = wm ^ wn;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         uint32_t r = (uint32_t)rs[q] - bias;
         r += (uint32_t)__shfl_xor((int)r, 16);
         r += (uint32_t)__shfl_xor((int)r, 32);
-        if (lane < 16) rowsum[wm * 128 + 16 * (4 * role + q) + lane] = (int)r;
+        if (lane < 16) rowsum[wm * 128 + 16 * (4 * R + q) + lane] = (int)r;
         uint32_t c = (uint32_t)cs[q] - bias;
         c += (uint32_t)__shfl_xor((int)c, 16);
         c += (uint32_t)__shfl_xor((int)c, 32);
-        if (lane < 16) colsum[wn * 128 + 16 * (4 * role + q) + lane] = (int)c;
+        if (lane < 16) colsum[wn * 128 + 16 * (4 * R + q) + lane] = (int)c;
     }
     __syncthreads();
 
@@ -1027,6 +1013,41 @@ __global__ __launch_bounds__(NT) void qlinear16_kernel(QArgs p, int tiles_m, int
         q16::epilogue<true>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi, stg);
     else
         q16::epilogue<false>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi, stg);
+}
+
+// int8 x int8 -> int8 / uint8 on whole tiles (M, N multiples of 256, K of 128
+// up to 32768, 16-byte aligned operands, checked on the host), the 16x16x64 loop.
+__global__ __launch_bounds__(NT) void qlinear16_kernel(QArgs p, int tiles_m, int tiles_n) {
+    __shared__ __attribute__((aligned(1024))) char smem[STAGE];
+    __shared__ __attribute__((aligned(1024))) char smem1[STAGE];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int T = tiles_m * tiles_n;
+    const int w = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+    const int z = w / T;
+    int tm, tn;
+    grouped_order(w - z * T, tiles_m, tiles_n, 4, tm, tn);
+    const int64_t z0 = z / p.nb1, z1 = z - z0 * p.nb1;
+    const uint8_t* a = (const uint8_t*)p.a + z0 * p.a_bs0 + z1 * p.a_bs1;
+    const uint8_t* b = (const uint8_t*)p.b + z0 * p.b_bs0 + z1 * p.b_bs1;
+    uint8_t* y = (uint8_t*)p.y + z0 * p.y_bs0 + z1 * p.y_bs1;
+    const int64_t m0 = (int64_t)tm * BMQ, n0 = (int64_t)tn * BNQ;
+
+    // this thread's row (m0 + t) and column (n0 + t) parameters and the output
+    // scale / zero point, loaded now so that their latency hides behind the K loop
+    auto ldscale = [&](const void* q, int64_t i) {
+        return p.scale_f16 ? from_bits<1>(((const uint16_t*)q)[i]) : ((const float*)q)[i];
+    };
+    const int64_t apo = z0 * p.ap_bs0 + z1 * p.ap_bs1 + (m0 + t) * p.ap_sm;
+    const int64_t bpo = z0 * p.bp_bs0 + z1 * p.bp_bs1 + (n0 + t) * p.bp_sn;
+    const int za_t = ldzp(p.a_zp, apo, false), zb_t = ldzp(p.b_zp, bpo, false);
+    const float sa_t = ldscale(p.a_scale, apo), sb_t = ldscale(p.b_scale, bpo);
+    const float sy = ldscale(p.y_scale, 0);
+    const float zyf = (float)(p.y_u8 ? (int)((const uint8_t*)p.y_zp)[0] : (int)((const int8_t*)p.y_zp)[0]);
+    if ((wm ^ wn) == 0)
+        qlinear16_tile<0>(p, smem, smem1, a, b, y, m0, n0, za_t, zb_t, sa_t, sb_t, sy, zyf, t, lane, wave, wm, wn);
+    else
+        qlinear16_tile<1>(p, smem, smem1, a, b, y, m0, n0, za_t, zb_t, sa_t, sb_t, sy, zyf, t, lane, wave, wm, wn);
 }
 
 template <bool AU8, bool BU8, int MODE>
@@ -1059,9 +1080,15 @@ hipError_t launch_qlinear(const QArgs& a, hipStream_t s) {
                      // the DMA path zero-pads a K tail and an odd stage count in LDS, and a
                      // flipped uint8 zero is not zero: uint8 needs an even number of full stages
                      (a.K % (2 * KB) == 0 || (!a.a_u8 && !a.b_u8));
-    if (!vec) return launch_q_types<0>(a, s);
-    const bool full = a.M % BMQ == 0 && a.N % BNQ == 0 && a.K % KB == 0 && a.K > 0 && a.K <= 32768 &&
+    const bool full = vec && a.M % BMQ == 0 && a.N % BNQ == 0 && a.K % KB == 0 && a.K > 0 && a.K <= 32768 &&
                       a.ldy % 16 == 0 && ((uintptr_t)a.y & 15) == 0 && a.y_bs0 % 16 == 0 && a.y_bs1 % 16 == 0;
+    log_choice("qlinear %s x %s -> %s M=%lld N=%lld K=%lld batches=%lld: 256x256x128 tiles, %s",
+               a.a_u8 ? "u8" : "i8", a.b_u8 ? "u8" : "i8", a.y_u8 ? "u8" : "i8", (long long)a.M, (long long)a.N,
+               (long long)a.K, (long long)(a.nb0 * a.nb1),
+               !vec ? "32x32x32 MFMA, register-staged loads"
+               : full && !a.a_u8 && !a.b_u8 ? "16x16x64 MFMA, DMA, whole tiles"
+               : full ? "32x32x32 MFMA, DMA, whole tiles" : "32x32x32 MFMA, DMA, ragged tiles");
+    if (!vec) return launch_q_types<0>(a, s);
     if (full && !a.a_u8 && !a.b_u8) {
         const int64_t tiles_m = a.M / BMQ, tiles_n = a.N / BNQ;
         const int64_t total = tiles_m * tiles_n * a.nb0 * a.nb1;
