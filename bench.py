@@ -12,7 +12,9 @@ multiply-adds counted like flops) divided by the step time.  Each workload is
 also timed on its own (median of HIP-event intervals around its call) and
 reported against the MI355X dense MFMA peak of its type under `per_config`;
 `cold_ms` there is the median of calls issued right after a 512 MiB write that
-evicts the last-level cache (operands start in HBM only).  `next_rows` times
+evicts the last-level cache (operands start in HBM only), and `graph_ms` the
+per-call time when the calls are replayed from a captured HIP graph (no host
+launch work between kernels; `graph_ms_per_step` likewise for a whole step).  `next_rows` times
 workloads outside the step the same way (GroupedMatMul over int8 weights with
 the dequantisation fused, an fp64 Gemm, uint8 QLinearMatMul, decode-like
 skinny Gemms against the HBM peak); they are not part of `value`.
@@ -120,6 +122,37 @@ def time_each(torch, fn, reps):
     torch.cuda.synchronize()
     ms = sorted(s.elapsed_time(e) for s, e in evs)
     return ms[len(ms) // 2], ms
+
+
+def capture(torch, fn, calls):
+    """A HIP graph of `calls` back-to-back calls of fn (captured on torch's graph
+    stream after one eager call there, as torch requires)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, calls, reps):
+    """Milliseconds per call: `reps` replays of a graph of `calls` calls between two
+    HIP events (no host launch work between the kernels)."""
+    g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / (reps * calls)
 
 
 def next_rows(torch, om, synth, dev, reps):
@@ -349,6 +382,7 @@ def main():
     ap.add_argument("--no-next", action="store_true",
                     help="skip the workloads outside the step (quantised experts), reported under next_rows")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the baseline")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timings")
     ap.add_argument("--only", default=None, help="comma-separated workload names")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 1 GiB device-to-device copies (reference for the HBM byte counters)")
@@ -409,6 +443,21 @@ def main():
         log("%-20s %9.4f ms  %8.1f T/s  %5.1f%% of %s peak" % (n, med, rate, 100 * rate / PEAK[w["dtype"]],
                                                                w["dtype"]))
 
+    # the same calls replayed from HIP graphs: per-call time without the host's
+    # launch work between kernels (what a captured serving loop sees); one graph
+    # per workload holds enough calls to fill about 0.2 ms
+    if not args.no_graph:
+        for p in per:
+            calls = max(1, int(0.2 / max(p["ms"], 1e-3)))
+            g = capture(torch, runs[p["workload"]], calls)
+            p["graph_ms"] = round(time_graph(torch, g, calls, max(3, args.reps // calls)), 4)
+            del g
+        g = capture(torch, step, 1)
+        graph_step_ms = time_graph(torch, g, 1, args.steps)
+        del g
+        log("graph replay: step %.3f ms; per call %s" % (graph_step_ms, ", ".join(
+            "%s %.4f" % (p["workload"], p["graph_ms"]) for p in per)))
+
     dom = max(per, key=lambda p: p["ms"])
     wd = W[dom["workload"]]
     ach = wd["ops"] / (dom["ms"] * 1e-3) / 1e12
@@ -425,6 +474,8 @@ def main():
                    "ops_per_step": total_ops},
         "roofline": roof, "per_config": per,
     }
+    if not args.no_graph:
+        out["graph_ms_per_step"] = round(graph_step_ms, 4)
     if not args.no_next and only is None:
         out["next_rows"] = next_rows(torch, om, synth, dev, args.reps)
     if not args.no_cpu:

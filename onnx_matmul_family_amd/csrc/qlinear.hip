@@ -886,7 +886,9 @@ __device__ __forceinline__ int mad24(int a, int b, int c) {
 // odd zy.)  The bytes go
 // through this wave's 16 KiB of `stage` (row r of 128 bytes, 16-byte chunk c
 // in slot c ^ (r / 2 % 8)) and leave as whole 128-byte row segments.
-template <bool MARK>
+// ZY0: y_zero_point is 0 (adding it is skipped; adding 0.0f is exact, so the
+// result is the same either way).
+template <bool MARK, bool ZY0>
 __device__ __forceinline__ void epilogue(const QArgs& p, const i32x4_t (&acc)[NF][NF], uint8_t* __restrict__ y,
                                          const uint32_t* U, const int* ZA, const float* SA, const uint32_t* CB,
                                          const int* ZB, const float* SB, int64_t m0, int64_t n0, int lane, int wm,
@@ -926,7 +928,7 @@ __device__ __forceinline__ void epilogue(const QArgs& p, const i32x4_t (&acc)[NF
                     mult = prod / sy;
                 }
                 const float x = (float)s32 * mult;
-                const float t = __builtin_amdgcn_fmed3f((x + MAGIC) + zyf, tlo, thi);
+                const float t = __builtin_amdgcn_fmed3f(ZY0 ? x + MAGIC : (x + MAGIC) + zyf, tlo, thi);
                 bytes[e] = __float_as_uint(t);
             }
             const uint32_t lo2 = __builtin_amdgcn_perm(bytes[1], bytes[0], 0x0c0c0400u);
@@ -1009,10 +1011,12 @@ __device__ __forceinline__ void qlinear16_tile(const QArgs& p, char* smem, char*
     const int scales_ok = __syncthreads_and(tame(sa_t) && tame(sb_t) && sy != 0.0f && tame(sy));
     const float lo = p.y_u8 ? 0.0f : -128.0f, hi = p.y_u8 ? 255.0f : 127.0f;
     char* stg = smem1 + wave * (STAGE / 4);
-    if (scales_ok)
-        q16::epilogue<true>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi, stg);
+    if (scales_ok && zyf == 0.0f)
+        q16::epilogue<true, true>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi, stg);
+    else if (scales_ok)
+        q16::epilogue<true, false>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi, stg);
     else
-        q16::epilogue<false>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi, stg);
+        q16::epilogue<false, false>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi, stg);
 }
 
 // int8 x int8 -> int8 / uint8 on whole tiles (M, N multiples of 256, K of 128

@@ -228,3 +228,25 @@ def test_int8_whole_tiles_batched_broadcast():
     got, ref = run(a, asc, az, b, bsc, bz, np.float32(0.02), np.array(-3, np.int8))
     assert got.shape == (2, 3, 256, 512)
     assert np.array_equal(got, ref), np.argwhere(got != ref)[:5]
+
+
+@pytest.mark.parametrize("yz", [0, 3])
+def test_int8_whole_tiles_exact_ties(yz):
+    """Exact rounding ties on the whole-tile kernel: row m of a holds
+    64 (2j + 1) entries of +1 (rows < 128) or -1 (rows >= 128), b is all ones,
+    scales 1, zero points 0 and y_scale 128, so x = acc / 128 = +-(j + 0.5)
+    exactly and round-half-even decides every output; y_zero_point 0 (the
+    epilogue that skips the add) and 3 (odd: the add follows the rounding)."""
+    M, N, K = 256, 256, 1024
+    a = np.zeros((M, K), np.int8)
+    for m in range(M):
+        j = m % 8
+        a[m, :64 * (2 * j + 1)] = 1 if m < 128 else -1
+    b = np.ones((K, N), np.int8)
+    z = np.array(0, np.int8)
+    got, ref = run(a, 1.0, z, b, 1.0, z, 128.0, np.array(yz, np.int8))
+    assert np.array_equal(got, ref), np.argwhere(got != ref)[:5]
+    # the ties really are ties: j + 0.5 rounds to the even neighbour
+    want = np.array([[int(np.rint(((1 if m < 128 else -1) * (j + 0.5)))) + yz for _ in range(1)]
+                     for m, j in ((m, m % 8) for m in range(M))])
+    assert np.array_equal(got[:, :1].astype(int), want)
