@@ -139,6 +139,9 @@ int omm_gemm(const omm_tensor* A, const omm_tensor* B, const omm_tensor* C, floa
  *     with splits x M x N x 4 bytes > OMM_GEMM_NOALLOC_SCRATCH_BYTES) returns
  *     OMM_ERR_SCRATCH with nothing launched.  Shapes that do not split K
  *     (and every fp32 / fp64 shape) use no scratch.
+ *   - The array's address on a GPU is looked up once (hipGetSymbolAddress);
+ *     a failure there returns OMM_ERR_HIP, a device ordinal of 64 or more
+ *     OMM_ERR_UNSUPPORTED.
  *   - Every call on one GPU shares that GPU's array and leaves its last
  *     contents there (each call writes every partial it reads, nothing needs
  *     clearing).  Calls that overlap on one GPU -- on different streams, or

@@ -7,8 +7,9 @@ generators (`synth`).  The binding is imported lazily so that the generators
 and the build step work on machines without a GPU.
 """
 
-_BINDING = ("matmul", "gemm", "gemm_noalloc", "qlinear_matmul", "grouped_matmul", "grouped_matmul_check",
-            "grouped_matmul_workspace_size", "describe", "lib", "status_string", "OmmError", "OmmTensor")
+_BINDING = ("matmul", "gemm", "gemm_noalloc", "qlinear_matmul", "grouped_matmul", "grouped_matmul_dequant",
+            "grouped_matmul_check", "grouped_matmul_workspace_size", "describe", "lib", "status_string", "OmmError",
+            "OmmTensor")
 
 
 def __getattr__(name):

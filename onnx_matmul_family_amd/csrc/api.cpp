@@ -234,7 +234,7 @@ int scratch_address(hipStream_t s, void** out) {
     } else if (hipGetDevice(&dev) != hipSuccess) {
         return OMM_ERR_HIP;
     }
-    if (dev < 0 || dev >= MAX_DEVICES) return OMM_ERR_UNSUPPORTED;
+    if (dev < 0 || dev >= MAX_DEVICES) return OMM_ERR_UNSUPPORTED;  // more GPUs than the table holds
     std::lock_guard<std::mutex> lock(scratch_mu);
     if (!scratch_dev[dev]) {
         int cur = -1;
@@ -421,8 +421,11 @@ int gemm_impl(const omm_tensor* A, const omm_tensor* B, const omm_tensor* C, flo
     if (!noalloc) return hip_status(launch_dense(a, dt, (hipStream_t)stream));
     omm::DenseScratch sc{nullptr, OMM_GEMM_NOALLOC_SCRATCH_BYTES};
     if (dt == OMM_BF16 || dt == OMM_F16) {
-        if (omm::dense16_scratch_bytes(a) > OMM_GEMM_NOALLOC_SCRATCH_BYTES) return OMM_ERR_SCRATCH;
-        if ((rc = scratch_address((hipStream_t)stream, &sc.ptr))) return rc;
+        const size_t need = omm::dense16_scratch_bytes(a);
+        if (need > OMM_GEMM_NOALLOC_SCRATCH_BYTES) return OMM_ERR_SCRATCH;
+        // shapes that split nothing never touch the array (launch_dense16 checks
+        // the pointer only when the plan needs scratch)
+        if (need > 0 && (rc = scratch_address((hipStream_t)stream, &sc.ptr))) return rc;
     }
     return hip_status(launch_dense(a, dt, (hipStream_t)stream, &sc));
 }
