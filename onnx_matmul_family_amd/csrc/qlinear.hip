@@ -1,5 +1,7 @@
-// QLinearMatMul (version 10) on gfx950: int8 MFMA (v_mfma_i32_32x32x32_i8)
-// with an exact int32 accumulator and the fused requantisation.
+// QLinearMatMul (version 10) on gfx950: int8 MFMA with an exact int32
+// accumulator and the fused requantisation -- v_mfma_i32_16x16x64_i8 on whole
+// 256x256 tiles (qlinear16_kernel), v_mfma_i32_32x32x32_i8 on ragged or
+// unaligned shapes (qlinear_kernel).
 //
 // Per output element the operator asks for
 //   acc = sum_k (a - za)(b - zb)                      (int32, wraps mod 2^32)
@@ -174,9 +176,9 @@ __device__ __forceinline__ void qloop(i32x16_t (&acc)[4][4], int (&rs)[4], int (
 // three-input bit operation (table 0x3c: src0 xor src1), which the compiler
 // does not fold into the xor of a later byte sum, so one copy of each
 // fragment stays live
-__device__ __forceinline__ void flip(i32x4_t& v) {
+__device__ __forceinline__ void flip(i32x4_t& v, uint32_t mask = 0x80808080u) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = (int)__builtin_amdgcn_bitop3_b32((uint32_t)v[e], 0x80808080u, 0u, 0x3c);
+    for (int e = 0; e < 4; ++e) v[e] = (int)__builtin_amdgcn_bitop3_b32((uint32_t)v[e], mask, 0u, 0x3c);
 }
 
 // sum of the 4 bytes of v taken as uint8
@@ -437,88 +439,8 @@ __device__ __forceinline__ void q_epilogue(const QArgs& p, const i32x16_t (&acc)
 //   acc  = sum ab - zb * U - za * colsum        (24-bit products, int32 wrap)
 //   mult = fp32(fp32(sa * sb) / sy)
 //   t    = (fp32(acc) * mult + 1.5*2^23) + zy, clamped to 1.5*2^23 + [lo, hi]
-// Adding 1.5*2^23 (an even integer, where fp32 spacing is 1) rounds the
-// product to the nearest integer, ties to even, exactly like rint; adding the
-// integer zy afterwards is exact; the clamp saturates, also for products too
-// large for the trick; the result is the low byte of t's bits.
-// MARK: the division as q0 = prod * r, r = fp32(1/sy) once, corrected by one
-// fused step q0 + fma(-q0, sy, prod) * r, which is the correctly rounded
-// quotient (Markstein) when nothing underflows or overflows; the caller takes
-// this branch only when every scale of the tile and sy lie in [2^-30, 2^30]
-// in magnitude (or are zero), which keeps every intermediate normal.
-// The bytes leave through LDS (stage: this wave's 16 KiB; row r of 128 bytes,
-// 16-byte chunk c in slot c ^ (r / 2 % 8)): 16-byte stores of whole 128-byte
-// row segments instead of 4-byte pieces.
-template <bool MARK>
-__device__ __forceinline__ void q_epilogue_full(const QArgs& p, const i32x16_t (&acc)[4][4], uint8_t* __restrict__ y,
-                                                const uint32_t* U, const int* ZA, const float* SA, const uint32_t* CB,
-                                                const int* ZB, const float* SB, int64_t m0, int64_t n0, int lane,
-                                                int wm, int wn, float sy, float zyf, float lo, float hi,
-                                                char* stage) {
-    constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
-    const float r = 1.0f / sy;
-    const float tlo = MAGIC + lo, thi = MAGIC + hi;
-    int Um[4], nza[4];
-    float sa[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int mloc = wm * 128 + 32 * i + (lane & 31);
-        Um[i] = (int)U[mloc];
-        nza[i] = -ZA[mloc];
-        sa[i] = SA[mloc];
-    }
-    const int h = lane >> 5;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int nloc = wn * 128 + 32 * j + 8 * q + 4 * (lane >> 5);
-            const i32x4_t cb = *(const i32x4_t*)(CB + nloc);
-            const i32x4_t zb = *(const i32x4_t*)(ZB + nloc);
-            const f32x4_t sb = *(const f32x4_t*)(SB + nloc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint32_t bytes[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    // |U| <= 2^23, |colsum| <= 2^22, |z| <= 255: exact 24-bit products
-                    const int s32 = (int)((uint32_t)acc[i][j][4 * q + e] + (uint32_t)__mul24(-zb[e], Um[i]) +
-                                          (uint32_t)__mul24(nza[i], cb[e]));
-                    const float prod = sa[i] * sb[e];
-                    float mult;
-                    if constexpr (MARK) {
-                        const float q0 = prod * r;
-                        mult = __builtin_fmaf(__builtin_fmaf(-q0, sy, prod), r, q0);
-                    } else {
-                        mult = prod / sy;
-                    }
-                    const float x = (float)s32 * mult;
-                    const float t = __builtin_amdgcn_fmed3f((x + MAGIC) + zyf, tlo, thi);
-                    bytes[e] = __float_as_uint(t);
-                }
-                // low bytes of the four results, in order, into one dword
-                const uint32_t lo2 = __builtin_amdgcn_perm(bytes[1], bytes[0], 0x0c0c0400u);
-                const uint32_t hi2 = __builtin_amdgcn_perm(bytes[3], bytes[2], 0x0c0c0400u);
-                const int r = 32 * i + (lane & 31), c = 2 * j + (q >> 1);
-                *(uint32_t*)(stage + r * 128 + ((c ^ ((r >> 1) & 7)) << 4) + ((q & 1) << 3) + (h << 2)) =
-                    lo2 | (hi2 << 16);
-            }
-        }
-    }
-    // whole 128-byte row segments: lane -> row 8 k + lane / 8, chunk lane % 8
-    uint8_t* __restrict__ yb = y + (m0 + wm * 128) * p.ldy + n0 + wn * 128;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const int r = 8 * k + (lane >> 3), c = lane & 7;
-        const u32x4_t d = *(const u32x4_t*)(stage + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
-        *(u32x4_t*)(yb + (int64_t)r * p.ldy + 16 * c) = d;
-    }
-}
-
 // MODE 0: register-staged loads, any shape.  MODE 1: DMA loads, ragged tiles
-// handled in the loads and the epilogue.  MODE 2: DMA loads, every tile full,
-// K a multiple of the stage and at most 32768 (checked on the host), fast
-// epilogue.
+// handled in the loads and the epilogue.  (Whole tiles go to qlinear16_kernel.)
 template <bool AU8, bool BU8, int MODE>
 __global__ __launch_bounds__(NT) void qlinear_kernel(QArgs p, int tiles_m, int tiles_n) {
     constexpr bool VEC = MODE != 0;
@@ -563,9 +485,7 @@ __global__ __launch_bounds__(NT) void qlinear_kernel(QArgs p, int tiles_m, int t
             else
                 qloop_dma<AU8, BU8, C, 1>(acc, rs, cs, smem, smem1, sa, sb, nk, lane, wm, wn, wave);
         };
-        if constexpr (MODE == 2)
-            run(std::false_type{});
-        else if (m0 + BMQ <= M && n0 + BNQ <= N && K % KB == 0)
+        if (m0 + BMQ <= M && n0 + BNQ <= N && K % KB == 0)
             run(std::false_type{});
         else
             run(std::true_type{});
@@ -647,28 +567,17 @@ __global__ __launch_bounds__(NT) void qlinear_kernel(QArgs p, int tiles_m, int t
 
     const float zyf = (float)(p.y_u8 ? (int)((const uint8_t*)p.y_zp)[0] : (int)((const int8_t*)p.y_zp)[0]);
     const float lo = p.y_u8 ? 0.0f : -128.0f, hi = p.y_u8 ? 255.0f : 127.0f;
-    if constexpr (MODE == 2) {
-        // the per-row / per-column terms live in smem; each wave stages its
-        // output block in its own quarter of smem1 (free since the K loop ended)
-        char* stage = smem1 + wave * (STAGE / 4);
-        if (scales_ok)
-            q_epilogue_full<true>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi, stage);
-        else
-            q_epilogue_full<false>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi, stage);
-    } else {
-        const bool vec_store = VEC && (N % 4 == 0) && (p.ldy % 4 == 0);
-        // |U| <= 256 K and |colsum| <= 128 K: below 2^23 for K <= 32768, where the
-        // 24-bit multiply-adds are exact
-        if (K <= 32768)
-            q_epilogue<true, VEC>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi, vec_store);
-        else
-            q_epilogue<false, VEC>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi,
-                                   vec_store);
-    }
+    const bool vec_store = VEC && (N % 4 == 0) && (p.ldy % 4 == 0);
+    // |U| <= 256 K and |colsum| <= 128 K: below 2^23 for K <= 32768, where the
+    // 24-bit multiply-adds are exact
+    if (K <= 32768)
+        q_epilogue<true, VEC>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi, vec_store);
+    else
+        q_epilogue<false, VEC>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi, vec_store);
 }
 
 // ---------------------------------------------------------------------------
-// 16x16x64 form for int8 x int8 whole tiles (v_mfma_i32_16x16x64_i8).  The
+// 16x16x64 form for whole tiles (v_mfma_i32_16x16x64_i8).  The
 // same 256x256 tile and 4 waves, each wave's 128x128 block as 8 x 8 MFMA
 // tiles of 16x16; a 128-byte stage is two k-blocks of 64, each 64 MFMAs, on
 // the pipeline of the bf16 / fp16 16x16x32 loop (fragments one k-block ahead,
@@ -684,11 +593,13 @@ __global__ __launch_bounds__(NT) void qlinear_kernel(QArgs p, int tiles_m, int t
 //     2 (r % 8) + (r / 16) % 2: rows 16 apart take chunks of opposite parity
 //     and the half-wave touches every bank once.
 // The MFMAs are tied inline assembly (the accumulators stay in their AGPRs,
-// as in the bf16 loop); no VALU instruction writes a fragment register (they
-// come straight from LDS), so no wait states are needed before them.  The
-// byte sums for the zero points are the 32x32 kernel's: each fragment is
-// summed (v_xor + v_sad_u8) by one of the two waves that read it, one dword
-// after every other MFMA.
+// as in the bf16 loop).  int8 fragments come straight from LDS, so no VALU
+// instruction writes one; uint8 fragments are flipped to int8 in their
+// registers on a fixed schedule that keeps every flip at least three MFMAs
+// ahead of the fragment's use (see the flip plan below).  The byte sums for
+// the zero points are the 32x32 kernel's: each fragment is summed (v_xor +
+// v_sad_u8) by one of the two waves that read it, one dword after every
+// other MFMA, always after its flip.
 namespace q16 {
 using namespace core16;
 
@@ -728,8 +639,13 @@ struct BDma {
     }
 };
 
+// U8: an operand may be uint8; ma / mb are 0x80808080 for a uint8 a / b and 0
+// for int8 (a flip with mask 0 leaves the fragment as it is)
+template <bool U8_>
 struct Frags {
+    static constexpr bool U8 = U8_;
     i32x4_t a[NF], b[NF];
+    uint32_t ma, mb;
     // fragment R of k-block kb: R < 8 -> a[R], else b[R - 8]
     template <int R>
     __device__ __forceinline__ void read_one(const char* st, int kb, int lane, int wm, int wn) {
@@ -748,6 +664,14 @@ struct Frags {
     }
     __device__ __forceinline__ void read(const char* st, int kb, int lane, int wm, int wn) {
         static_for<0, 2 * NF>([&](auto rc) { read_one<decltype(rc)::value>(st, kb, lane, wm, wn); });
+    }
+    // dword D of a uint8 fragment F (F < 8: a[F], else b[F - 8]) to int8 in place
+    template <int F, int D>
+    __device__ __forceinline__ void flip_dw() {
+        if constexpr (F < NF)
+            a[F][D] = (int)__builtin_amdgcn_bitop3_b32((uint32_t)a[F][D], ma, 0u, 0x3c);
+        else
+            b[F - NF][D] = (int)__builtin_amdgcn_bitop3_b32((uint32_t)b[F - NF][D], mb, 0u, 0x3c);
     }
 };
 
@@ -785,14 +709,67 @@ constexpr int sum_slot(int R, int d) {
     return ids[d / 4] * 4 + d % 4;
 }
 
+// uint8 operands: the DMA copies the bytes as they are, and each fragment is
+// mapped to int8 (x - 128: flip) in its registers, one dword after every MFMA
+// (a wave64 VALU instruction holds the issue for 4 of the MFMA's 16 cycles, so
+// more than a few between two MFMAs would delay the second).  Fragment r of
+// the read order (read after MFMA 4r of the k-block before) is flipped there,
+// after MFMAs 4r + 16 .. 4r + 19, for r < 12; the last four (a4 .. a7, first
+// used by MFMAs 32 .. 56) in their own k-block, after MFMAs 0 .. 15.  An MFMA
+// issued from inline assembly gets no wait states from the compiler after a
+// VALU write of its sources: every flip lands at least three MFMAs ahead of
+// the fragment's first use (MFMA x of a k-block uses a[x / 8] and b[x % 8]).
+constexpr int first_use(int f) { return f < NF ? NF * f : f - NF; }
+constexpr int NXT_FLIPS = 12;
+// fragment * 4 + dword of `cur` / `nxt` flipped after MFMA x, -1 if none
+constexpr int cur_flip(int x) { return x < 16 ? 4 * frag_order(NF, NF, NXT_FLIPS + x / 4) + x % 4 : -1; }
+constexpr int nxt_flip(int x) { return x >= 16 ? 4 * frag_order(NF, NF, (x - 16) / 4) + x % 4 : -1; }
+struct FlipPlan {
+    int cur[NF * NF], nxt[NF * NF];
+};
+constexpr FlipPlan make_flip_plan() {
+    FlipPlan p{};
+    for (int x = 0; x < NF * NF; ++x) {
+        p.cur[x] = cur_flip(x);
+        p.nxt[x] = nxt_flip(x);
+    }
+    return p;
+}
+constexpr FlipPlan FLIPS = make_flip_plan();
+constexpr bool flip_plan_ok() {
+    int seen[2 * NF * 4] = {};
+    int at[2 * NF * 4] = {};  // slot of the flip; nxt flips as slot - 64
+    for (int x = 0; x < NF * NF; ++x) {
+        if (FLIPS.cur[x] >= 0) {
+            ++seen[FLIPS.cur[x]];
+            at[FLIPS.cur[x]] = x;
+        }
+        if (FLIPS.nxt[x] >= 0) {
+            const int fd = FLIPS.nxt[x];
+            ++seen[fd];
+            at[fd] = x - NF * NF;
+            if (4 * read_pos(fd / 4) + 16 > x) return false;  // 16 MFMAs after the fragment's read
+        }
+    }
+    for (int fd = 0; fd < 2 * NF * 4; ++fd) {
+        if (seen[fd] != 1) return false;                      // every dword flipped once
+        if (first_use(fd / 4) - at[fd] - 1 < 3) return false;  // >= 3 MFMAs before the first use
+    }
+    for (int R = 0; R < 2; ++R)
+        for (int d = 0; d < 32; ++d)  // every byte sum (after MFMA 2d + 1) sees an int8 dword
+            if (at[sum_slot(R, d)] >= 2 * d + 1) return false;
+    return true;
+}
+static_assert(flip_plan_ok(), "uint8 flips: each dword once, >= 3 MFMAs ahead of its use, before its byte sum");
+
 // One k-block: MFMA x on tile (x/8, x%8) of `cur`; the 16 fragment reads of
 // k-block kb of `lds` into `nxt` and this wave's DMA instructions D0 .. D1-1
 // of stage kt (into buffer X) spread evenly; one dword of byte sums after
-// every other MFMA.
-template <int R, bool Z, int D0, int D1, class SA, class SB>
-__device__ __forceinline__ void kblock(i32x4_t (&acc)[NF][NF], int (&rs)[4], int (&cs)[4], const Frags& cur,
-                                       Frags& nxt, const char* lds, int kb, char* X, const SA& sa, const SB& sb,
-                                       int kt, bool live, int lane, int wm, int wn, int wave) {
+// every other MFMA; then the uint8 flips scheduled after MFMA x.
+template <int R, bool Z, int D0, int D1, class SA, class SB, class FR>
+__device__ __forceinline__ void kblock(i32x4_t (&acc)[NF][NF], int (&rs)[4], int (&cs)[4], FR& cur, FR& nxt,
+                                       const char* lds, int kb, char* X, const SA& sa, const SB& sb, int kt,
+                                       bool live, int lane, int wm, int wn, int wave) {
     constexpr int NM = NF * NF, NR = 2 * NF, ND = D1 - D0, LA = SA::PER_WAVE;
     DmaCtx ca, cb;
     if constexpr (ND > 0) {
@@ -815,12 +792,14 @@ __device__ __forceinline__ void kblock(i32x4_t (&acc)[NF][NF], int (&rs)[4], int
             else
                 cs[(f - NF) % 4] = bytesum1(cur.b[f - NF][w], cs[(f - NF) % 4]);
         }
+        if constexpr (FR::U8 && FLIPS.cur[x] >= 0) cur.template flip_dw<FLIPS.cur[x] / 4, FLIPS.cur[x] % 4>();
+        if constexpr (FR::U8 && FLIPS.nxt[x] >= 0) nxt.template flip_dw<FLIPS.nxt[x] / 4, FLIPS.nxt[x] % 4>();
         fence_sched();
     });
 }
 
-template <int R, bool Z, class SA, class SB>
-__device__ __forceinline__ void stage(i32x4_t (&acc)[NF][NF], int (&rs)[4], int (&cs)[4], Frags& fc, Frags& fn,
+template <int R, bool Z, class SA, class SB, class FR>
+__device__ __forceinline__ void stage(i32x4_t (&acc)[NF][NF], int (&rs)[4], int (&cs)[4], FR& fc, FR& fn,
                                       char* X, char* Y, const SA& sa, const SB& sb, int kt, int nk, int lane, int wm,
                                       int wn, int wave) {
     constexpr int LD = SA::PER_WAVE + SB::PER_WAVE;
@@ -834,10 +813,10 @@ __device__ __forceinline__ void stage(i32x4_t (&acc)[NF][NF], int (&rs)[4], int 
 
 // nk >= 1 stages; an odd count runs one more stage of zeros.  On return no
 // DMA is in flight and the accumulators are safe to read.
-template <int R, class SA, class SB>
+template <int R, bool U8, class SA, class SB>
 __device__ __forceinline__ void loop(i32x4_t (&acc)[NF][NF], int (&rs)[4], int (&cs)[4], char* __restrict__ s0,
-                                     char* __restrict__ s1, const SA& sa, const SB& sb, int nk, int lane, int wm,
-                                     int wn, int wave) {
+                                     char* __restrict__ s1, const SA& sa, const SB& sb, int nk, uint32_t ma,
+                                     uint32_t mb, int lane, int wm, int wn, int wave) {
     constexpr int LA = SA::PER_WAVE, LD = SA::PER_WAVE + SB::PER_WAVE;
     {
         const DmaCtx a0 = sa.ctx(s0, 0, true), b0 = sb.ctx(s0 + A_BYTES, 0, true);
@@ -847,8 +826,21 @@ __device__ __forceinline__ void loop(i32x4_t (&acc)[NF][NF], int (&rs)[4], int (
     }
     wait_vm<LD>();
     __syncthreads();
-    Frags fc, fn;
+    Frags<U8> fc, fn;
+    fc.ma = fn.ma = ma;
+    fc.mb = fn.mb = mb;
     fc.read(s0, 0, lane, wm, wn);
+    if constexpr (U8) {
+        // the fragments a k-block before would have flipped, flipped here; then
+        // wait states before the first MFMA reads them
+        static_for<0, NF * NF>([&](auto c) {
+            constexpr int fd = FLIPS.nxt[decltype(c)::value];
+            if constexpr (fd >= 0) fc.template flip_dw<fd / 4, fd % 4>();
+        });
+        fence_sched();
+        asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+        fence_sched();
+    }
     stage<R, true>(acc, rs, cs, fc, fn, s0, s1, sa, sb, 0, nk, lane, wm, wn, wave);
     stage<R, false>(acc, rs, cs, fc, fn, s1, s0, sa, sb, 1, nk, lane, wm, wn, wave);
     for (int kt = 2; kt < nk; kt += 2) {
@@ -880,12 +872,20 @@ __device__ __forceinline__ int mad24(int a, int b, int c) {
 
 // Requantisation of the wave's 128 x 128 block (lane l, tile (i, j), register
 // e: row 16 i + l%16, column 16 j + 4 (l/16) + e) with the per-row / per-
-// column terms in LDS; the same arithmetic as q_epilogue_full.  (zy is added
-// after the rounding constant, not folded into it: x + (1.5 * 2^23 + zy)
-// would break ties towards an even sum, which differs from rint(x) + zy for
-// odd zy.)  The bytes go
-// through this wave's 16 KiB of `stage` (row r of 128 bytes, 16-byte chunk c
-// in slot c ^ (r / 2 % 8)) and leave as whole 128-byte row segments.
+// column terms in LDS; the arithmetic of q_epilogue.  Adding 1.5 * 2^23 (an
+// even integer, where the fp32 spacing is 1) rounds the product to the
+// nearest integer, ties to even, exactly like rint; adding the integer zy
+// afterwards is exact; the clamp saturates, also for products too large for
+// the trick; the result is the low byte of t's bits.  (zy is added after the
+// rounding constant, not folded into it: x + (1.5 * 2^23 + zy) would break
+// ties towards an even sum, which differs from rint(x) + zy for odd zy.)
+// MARK: the division as q0 = prod * r, r = fp32(1 / sy) once, corrected by
+// one fused step q0 + fma(-q0, sy, prod) * r, which is the correctly rounded
+// quotient (Markstein) when nothing underflows or overflows; the caller takes
+// this branch only when every scale of the tile and sy lie in [2^-30, 2^30]
+// in magnitude (or are zero), which keeps every intermediate normal.  The
+// bytes go through this wave's 16 KiB of `stage` (row r of 128 bytes, 16-byte
+// chunk c in slot c ^ (r / 2 % 8)) and leave as whole 128-byte row segments.
 // ZY0: y_zero_point is 0 (adding it is skipped; adding 0.0f is exact, so the
 // result is the same either way).
 template <bool MARK, bool ZY0>
@@ -953,7 +953,7 @@ __device__ __forceinline__ void epilogue(const QArgs& p, const i32x4_t (&acc)[NF
 // Everything after the set-up of qlinear16_kernel, for the waves of role R =
 // wm ^ wn (which fragments a wave sums is a template argument, and the
 // accumulators never meet a branch merge, which would copy all 256 of them).
-template <int R>
+template <int R, bool U8>
 __device__ __forceinline__ void qlinear16_tile(const QArgs& p, char* smem, char* smem1, const uint8_t* a,
                                                const uint8_t* b, uint8_t* y, int64_t m0, int64_t n0, int za_t,
                                                int zb_t, float sa_t, float sb_t, float sy, float zyf, int t,
@@ -967,7 +967,8 @@ __device__ __forceinline__ void qlinear16_tile(const QArgs& p, char* smem, char*
         q16::BDma sb;
         sa.init(a, p.lda, m0, M, K, lane);
         sb.init(b, p.ldb, n0, lane);
-        q16::loop<R>(acc, rs, cs, smem, smem1, sa, sb, nk, lane, wm, wn, wave);
+        q16::loop<R, U8>(acc, rs, cs, smem, smem1, sa, sb, nk, p.a_u8 ? 0x80808080u : 0u,
+                         p.b_u8 ? 0x80808080u : 0u, lane, wm, wn, wave);
     }
     // every lane summed 32 bytes (each +128) per stage into each of rs / cs
     const int nk_run = (nk + 1) & ~1;
@@ -1019,8 +1020,11 @@ __device__ __forceinline__ void qlinear16_tile(const QArgs& p, char* smem, char*
         q16::epilogue<false, false>(p, acc, y, U, ZA, SA, CB, ZB, SB, m0, n0, lane, wm, wn, sy, zyf, lo, hi, stg);
 }
 
-// int8 x int8 -> int8 / uint8 on whole tiles (M, N multiples of 256, K of 128
-// up to 32768, 16-byte aligned operands, checked on the host), the 16x16x64 loop.
+// int8 / uint8 x int8 / uint8 -> int8 / uint8 on whole tiles (M, N multiples of
+// 256, K a multiple of 128 up to 32768 -- of 256 with a uint8 operand, whose
+// zero-padded stage would not flip to zero -- 16-byte aligned operands, checked
+// on the host), the 16x16x64 loop.  A uint8 zero point enters as zp - 128.
+template <bool U8>
 __global__ __launch_bounds__(NT) void qlinear16_kernel(QArgs p, int tiles_m, int tiles_n) {
     __shared__ __attribute__((aligned(1024))) char smem[STAGE];
     __shared__ __attribute__((aligned(1024))) char smem1[STAGE];
@@ -1044,14 +1048,14 @@ __global__ __launch_bounds__(NT) void qlinear16_kernel(QArgs p, int tiles_m, int
     };
     const int64_t apo = z0 * p.ap_bs0 + z1 * p.ap_bs1 + (m0 + t) * p.ap_sm;
     const int64_t bpo = z0 * p.bp_bs0 + z1 * p.bp_bs1 + (n0 + t) * p.bp_sn;
-    const int za_t = ldzp(p.a_zp, apo, false), zb_t = ldzp(p.b_zp, bpo, false);
+    const int za_t = ldzp(p.a_zp, apo, U8 && p.a_u8), zb_t = ldzp(p.b_zp, bpo, U8 && p.b_u8);
     const float sa_t = ldscale(p.a_scale, apo), sb_t = ldscale(p.b_scale, bpo);
     const float sy = ldscale(p.y_scale, 0);
     const float zyf = (float)(p.y_u8 ? (int)((const uint8_t*)p.y_zp)[0] : (int)((const int8_t*)p.y_zp)[0]);
     if ((wm ^ wn) == 0)
-        qlinear16_tile<0>(p, smem, smem1, a, b, y, m0, n0, za_t, zb_t, sa_t, sb_t, sy, zyf, t, lane, wave, wm, wn);
+        qlinear16_tile<0, U8>(p, smem, smem1, a, b, y, m0, n0, za_t, zb_t, sa_t, sb_t, sy, zyf, t, lane, wave, wm, wn);
     else
-        qlinear16_tile<1>(p, smem, smem1, a, b, y, m0, n0, za_t, zb_t, sa_t, sb_t, sy, zyf, t, lane, wave, wm, wn);
+        qlinear16_tile<1, U8>(p, smem, smem1, a, b, y, m0, n0, za_t, zb_t, sa_t, sb_t, sy, zyf, t, lane, wave, wm, wn);
 }
 
 template <bool AU8, bool BU8, int MODE>
@@ -1090,17 +1094,21 @@ hipError_t launch_qlinear(const QArgs& a, hipStream_t s) {
                a.a_u8 ? "u8" : "i8", a.b_u8 ? "u8" : "i8", a.y_u8 ? "u8" : "i8", (long long)a.M, (long long)a.N,
                (long long)a.K, (long long)(a.nb0 * a.nb1),
                !vec ? "32x32x32 MFMA, register-staged loads"
-               : full && !a.a_u8 && !a.b_u8 ? "16x16x64 MFMA, DMA, whole tiles"
-               : full ? "32x32x32 MFMA, DMA, whole tiles" : "32x32x32 MFMA, DMA, ragged tiles");
+               : full ? "16x16x64 MFMA, DMA, whole tiles" : "32x32x32 MFMA, DMA, ragged tiles");
     if (!vec) return launch_q_types<0>(a, s);
-    if (full && !a.a_u8 && !a.b_u8) {
+    if (full) {
+        // (vec holds K % 256 == 0 when an operand is uint8)
         const int64_t tiles_m = a.M / BMQ, tiles_n = a.N / BNQ;
         const int64_t total = tiles_m * tiles_n * a.nb0 * a.nb1;
         if (total > 0x7fffffff) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(qlinear16_kernel, dim3((unsigned)total), dim3(NT), 0, s, a, (int)tiles_m, (int)tiles_n);
+        const dim3 grid((unsigned)total);
+        if (a.a_u8 || a.b_u8)
+            hipLaunchKernelGGL((qlinear16_kernel<true>), grid, dim3(NT), 0, s, a, (int)tiles_m, (int)tiles_n);
+        else
+            hipLaunchKernelGGL((qlinear16_kernel<false>), grid, dim3(NT), 0, s, a, (int)tiles_m, (int)tiles_n);
         return hipGetLastError();
     }
-    return full ? launch_q_types<2>(a, s) : launch_q_types<1>(a, s);
+    return launch_q_types<1>(a, s);
 }
 
 }  // namespace omm

@@ -1,14 +1,15 @@
-"""Wait-state check of the 16x16x32 MFMAs issued from inline assembly.
+"""Wait-state check of the MFMAs issued from inline assembly.
 
-The bf16/fp16 16x16x32 K loops issue their MFMAs as inline assembly (so each
-accumulator stays in its AGPRs), which the compiler's hazard recognizer does
-not look into.  An MFMA needs a few wait states after a VALU instruction
-writes one of its source registers; the loops never produce such a write
-(operands come from LDS reads, accumulators are first written by the MFMAs
-themselves).  This test compiles the two kernel files for gfx950 and checks
-that no VALU instruction writes a source register of a 16x16x32 MFMA within
-4 wait states before it.  CPU only (hipcc cross-compiles); skipped without
-hipcc."""
+The bf16/fp16 16x16x32 and int8 16x16x64 K loops issue their MFMAs as inline
+assembly (so each accumulator stays in its AGPRs), which the compiler's
+hazard recognizer does not look into.  An MFMA needs a few wait states after
+a VALU instruction writes one of its source registers.  The bf16 loops never
+produce such a write (operands come from LDS reads, accumulators are first
+written by the MFMAs themselves); the int8 loop's uint8 operands are flipped
+to int8 in their registers at least three MFMAs ahead of their first use.
+This test compiles the three kernel files for gfx950 and checks that no VALU
+instruction writes a source register of such an MFMA within 4 wait states
+before it.  CPU only (hipcc cross-compiles); skipped without hipcc."""
 import os
 import re
 import shutil
@@ -40,10 +41,13 @@ def _instructions(asm):
     return out
 
 
+ASM_MFMA = ("v_mfma_f32_16x16x32", "v_mfma_i32_16x16x64_i8")
+
+
 def _violations(ins, window=4):
     bad, n = [], 0
     for i, line in enumerate(ins):
-        if not line.startswith("v_mfma_f32_16x16x32"):
+        if not line.startswith(ASM_MFMA):
             continue
         n += 1
         ops = [o.strip() for o in line.split(None, 1)[1].split(",")]
@@ -63,8 +67,9 @@ def _violations(ins, window=4):
 
 
 def _compile(src, out):
+    extra = ["-ffp-contract=off"] if src == "qlinear.hip" else []  # as the library build
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "--cuda-device-only", "-S",
+           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "--cuda-device-only", "-S"] + extra + [
            os.path.join(CSRC, src), "-o", out]
     subprocess.run(cmd, check=True, capture_output=True)
     with open(out) as f:
@@ -75,17 +80,20 @@ def test_checker_flags_a_planted_write():
     ins = ["v_mov_b32_e32 v5, v9", "v_mfma_f32_16x16x32_bf16 a[0:3], v[2:5], v[6:9], a[0:3]"]
     assert len(_violations(ins)[1]) == 1
     assert len(_violations(["s_nop 3"] + ins[:1] + ["s_nop 3"] + ins[1:])[1]) == 0
+    flip = ["v_bitop3_b32 v53, v57, s51, 0 bitop3:0x3c", "v_mfma_i32_16x16x32_i8 a[0:3], v[18:21], v[50:53], 0",
+            "v_mfma_i32_16x16x64_i8 a[4:7], v[18:21], v[50:53], 0"]
+    assert len(_violations(flip)[1]) == 1  # the 16x16x64 form at distance 1 (the 16x16x32 int8 form is not ours)
 
 
 @pytest.mark.skipif(HIPCC is None, reason="hipcc not available")
 def test_no_valu_write_of_mfma16_operands():
     with tempfile.TemporaryDirectory() as d:
-        srcs = ["dense16.hip", "grouped.hip"]
-        with ThreadPoolExecutor(2) as ex:
+        srcs = ["dense16.hip", "grouped.hip", "qlinear.hip"]
+        with ThreadPoolExecutor(3) as ex:
             asms = list(ex.map(lambda s: _compile(s, os.path.join(d, s + ".s")), srcs))
     total = 0
     for src, asm in zip(srcs, asms):
         n, bad = _violations(_instructions(asm))
         total += n
         assert not bad, "%s: %s" % (src, bad[:3])
-    assert total > 1000  # the 16x16x32 loops were found
+        assert n > 1000, src  # the inline-assembly loops were found

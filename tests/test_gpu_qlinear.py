@@ -250,3 +250,44 @@ def test_int8_whole_tiles_exact_ties(yz):
     want = np.array([[int(np.rint(((1 if m < 128 else -1) * (j + 0.5)))) + yz for _ in range(1)]
                      for m, j in ((m, m % 8) for m in range(M))])
     assert np.array_equal(got[:, :1].astype(int), want)
+
+
+@pytest.mark.parametrize("ta,tb,ty", [(np.uint8, np.uint8, np.uint8), (np.uint8, np.int8, np.int8),
+                                      (np.int8, np.uint8, np.uint8)])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (512, 768, 768), (256, 512, 384), (256, 256, 32768)])
+def test_uint8_whole_tiles_stage_counts(ta, tb, ty, M, N, K):
+    """uint8 and mixed operands on whole 256x256 tiles: the 16x16x64 kernel
+    flips uint8 fragments to int8 in registers (K a multiple of 256: the
+    fewest stages, several tiles, the largest K); K = 384 (an odd stage count)
+    takes the other kernel.  Zero points far from 0 on the uint8 side,
+    compared in full and bit for bit."""
+    rng = np.random.default_rng(M + 3 * N + 7 * K + 11 * (ta == np.uint8) + 13 * (tb == np.uint8))
+    a, b = rint(rng, (M, K), ta), rint(rng, (K, N), tb)
+    zl = lambda d: (100, 150) if d == np.uint8 else (-16, 16)
+    az, bz = rint(rng, (M, 1), ta, *zl(ta)), rint(rng, (1, N), tb, *zl(tb))
+    asc = synth.uniform(rng, (M, 1), 0.002, 0.01)
+    bsc = synth.uniform(rng, (1, N), 0.002, 0.01)
+    ys = np.float32(0.05 * np.sqrt(K / 4096))
+    got, ref = run(a, asc, az, b, bsc, bz, ys, np.array(128 if ty == np.uint8 else -2, ty))
+    assert np.array_equal(got, ref), np.argwhere(got != ref)[:5]
+    assert len(np.unique(got)) > 100
+
+
+@pytest.mark.parametrize("ta,tb", [(np.uint8, np.uint8), (np.uint8, np.int8), (np.int8, np.uint8)])
+def test_uint8_whole_tiles_exact_ties(ta, tb):
+    """The exact-tie construction of the int8 test with uint8 operands: a uint8
+    entry is the int8 one + 128 and its zero point 128, so a - a_zero_point
+    (and b - b_zero_point) are the same +-1 / 0 values and every output is a
+    rounding tie."""
+    M, N, K = 256, 256, 1024
+    a = np.zeros((M, K), np.int16)
+    for m in range(M):
+        j = m % 8
+        a[m, :64 * (2 * j + 1)] = 1 if m < 128 else -1
+    b = np.ones((K, N), np.int16)
+    off = lambda d: 128 if d == np.uint8 else 0
+    za, zb = np.array(off(ta), ta), np.array(off(tb), tb)
+    got, ref = run((a + off(ta)).astype(ta), 1.0, za, (b + off(tb)).astype(tb), 1.0, zb, 128.0, np.array(3, np.int8))
+    assert np.array_equal(got, ref), np.argwhere(got != ref)[:5]
+    want = np.array([int(np.rint((1 if m < 128 else -1) * (m % 8 + 0.5))) + 3 for m in range(M)])
+    assert np.array_equal(got[:, 0].astype(int), want)
