@@ -35,19 +35,24 @@ namespace {
 
 constexpr int ROUTE_THREADS = 1024;
 constexpr int GBM = 256, GBN = 256;  // grouped tile
-// Tile order of the bf16 / fp16 kernel: runs of 8 row tiles (about one
-// expert's rows when tokens spread evenly over the experts) times every column
-// tile, so the 32 tiles an XCD runs at once share about one expert's weight
-// panel and each panel streams from memory about once.  Measured on the
-// 64-expert routing: 1.5 % faster than runs of 4.
-constexpr int ORDER_ROWS = 8;
+// Tile order of every grouped kernel (run_tile): runs of row tiles that the
+// router aligns to the groups -- a group of at most RUN_MAX row tiles is one
+// run, a larger one is cut into balanced runs of at most RUN_ROWS -- each
+// walked column tile by column tile, so the 32 tiles an XCD runs at once
+// share the weight panels of one group.  Measured on the benchmark routing
+// (64 experts of 8 or 9 row tiles) against fixed runs of 8 (4 for the
+// quantised-expert kernels) that straddle two experts: 3-4 % faster for the
+// bf16, quantised-expert, fp32 and fp64 kernels; capping runs at 4 rows was
+// slower.
+constexpr int RUN_MAX = 12, RUN_ROWS = 8;
 constexpr int MAX_G = 8192;          // groups handled by the single-workgroup router
 
 // workspace layout (bytes, from a 256-byte aligned base)
 //   [0, 64)                   header: int32 num_tiles, int32 invalid_count
 //   [64, 64 + 4G)             per-group pair counts
 //   [64 + 4G, 64 + 8G)        per-group scatter cursors
-//   [tiles, + 16 TT)          tile table: int4 (group, first sorted pair, rows, 0), TT = P/BM_MIN + G + 1
+//   [tiles, + 16 TT)          tile table: int4 (group, first sorted pair, end of the group's pairs,
+//                             run: first row tile << 4 | rows - 1), TT = P/BM_MIN + G + 1
 //   [sorted, + 4P)            pair ids p = m*S + i in group order
 constexpr int BM_MIN = 128;
 constexpr int ROUTE_CHUNK = 1024;  // pairs per routing workgroup
@@ -61,6 +66,26 @@ __host__ __device__ inline int64_t off_sorted(int64_t P, int64_t G) {
 
 __device__ __forceinline__ int64_t load_idx(const void* idx, int64_t p, int idx64) {
     return idx64 ? ((const int64_t*)idx)[p] : (int64_t)((const int32_t*)idx)[p];
+}
+
+// (group, first sorted pair, rows) of a tile-table entry for bm-row tiles
+__device__ __forceinline__ int4 tile_entry(const int4& e, int bm) { return make_int4(e.x, e.y, min(bm, e.z - e.y), 0); }
+
+// Linear tile w of the run order: the row tile q = w / tiles_n lies in the
+// run that holds w (a run of h row tiles starting at row tile c0 covers
+// linear tiles c0 * tiles_n .. (c0 + h) * tiles_n - 1), whose tiles it walks
+// column by column.  Returns (group, first sorted pair, rows) of row tile tm
+// from q's entry alone (tiles of one run are consecutive bm-row slices of one
+// group), and its column tile.
+__device__ __forceinline__ int4 run_tile(const int4* tiles, int w, int tiles_n, int bm, int& tn) {
+    const int q = w / tiles_n;
+    const int4 e = tiles[q];
+    const int c0 = e.w >> 4, h = (e.w & 15) + 1;
+    const int r = w - c0 * tiles_n;
+    const int tm = c0 + r % h;
+    tn = r / h;
+    const int start = e.y + (tm - q) * bm;
+    return make_int4(e.x, start, min(bm, e.z - start), 0);
 }
 
 // exclusive scan of v[0..n) in LDS by one workgroup; returns the total
@@ -133,8 +158,13 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_scan_kernel(int64_t P, in
     int4* tiles = (int4*)(ws + off_tiles(G));
     int* cur = (int*)(ws + off_cursor(G));
     for (int g = t; g < G; g += ROUTE_THREADS) {
-        const int c = cnt[g], nt = (c + BM - 1) / BM;
-        for (int tt = 0; tt < nt; ++tt) tiles[tile0[g] + tt] = make_int4(g, row0[g] + tt * BM, min(BM, c - tt * BM), 0);
+        const int c = cnt[g], nt = (c + BM - 1) / BM, end = row0[g] + c;
+        const int nrun = nt <= RUN_MAX ? 1 : (nt + RUN_ROWS - 1) / RUN_ROWS;
+        for (int ru = 0; ru < nrun; ++ru) {
+            const int lo = (int)((int64_t)ru * nt / nrun), hi = (int)((int64_t)(ru + 1) * nt / nrun);
+            const int run = ((tile0[g] + lo) << 4) | (hi - lo - 1);
+            for (int tt = lo; tt < hi; ++tt) tiles[tile0[g] + tt] = make_int4(g, row0[g] + tt * BM, end, run);
+        }
         cur[g] = row0[g];
     }
     if (t == 0) ((int*)ws)[0] = ntiles;
@@ -254,9 +284,8 @@ __device__ __forceinline__ void grouped_epilogue(const f32x16_t (&acc)[4][4], co
 // One 256x256 tile of the grouped product with element-wise register-staged
 // loads (any alignment and shape; the DMA form is grouped_body16).
 template <int DT>
-__device__ __forceinline__ void grouped_body(const GroupedArgs& a, const char* ws, int tile, int tn, char* s0,
+__device__ __forceinline__ void grouped_body(const GroupedArgs& a, const char* ws, int4 te, int tn, char* s0,
                                              char* s1, int* orow_s) {
-    const int4 te = ((const int4*)(ws + off_tiles(a.G)))[tile];
     const int g = te.x, start = te.y, rows = te.z;
     const int* sorted = (const int*)(ws + off_sorted(a.M * a.S, a.G));
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -362,9 +391,8 @@ __device__ __forceinline__ void grouped_epilogue16(const f32x4_t (&acc)[8][8], c
 }
 
 template <int DT>
-__device__ __forceinline__ void grouped_body16(const GroupedArgs& a, const char* ws, int tile, int tn, char* s0,
+__device__ __forceinline__ void grouped_body16(const GroupedArgs& a, const char* ws, int4 te, int tn, char* s0,
                                                char* s1, int* orow_s, uint32_t* roff_s, uint16_t* bias_s) {
-    const int4 te = ((const int4*)(ws + off_tiles(a.G)))[tile];
     const int g = te.x, start = te.y, rows = te.z;
     const int* sorted = (const int*)(ws + off_sorted(a.M * a.S, a.G));
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -454,12 +482,12 @@ __global__ __launch_bounds__(256) void grouped16_kernel(GroupedArgs a, const cha
     const int per = total >> 3, extra = total & 7;
     if (l >= per + (x < extra ? 1 : 0)) return;
     const int w = x * per + min(x, extra) + l;
-    int tm, tn;
-    grouped_order(w, ntiles, tiles_n, ORDER_ROWS, tm, tn);
+    int tn;
+    const int4 te = run_tile((const int4*)(ws + off_tiles(a.G)), w, tiles_n, GBM, tn);
     if constexpr (VEC)
-        grouped_body16<DT>(a, ws, tm, tn, s0, s1, orow_s, roff_s, bias_s);
+        grouped_body16<DT>(a, ws, te, tn, s0, s1, orow_s, roff_s, bias_s);
     else
-        grouped_body<DT>(a, ws, tm, tn, s0, s1, orow_s);
+        grouped_body<DT>(a, ws, te, tn, s0, s1, orow_s);
 }
 
 // ---------------------------------------------------------------------------
@@ -1009,10 +1037,9 @@ __global__ __launch_bounds__(256) void grouped16_dq_dma_kernel(GroupedArgs a, co
     const int b = (int)blockIdx.x, x = b & 7, l = b >> 3;
     const int per = total >> 3, extra = total & 7;
     if (l >= per + (x < extra ? 1 : 0)) return;
-    int tm, tn;
-    grouped_order(x * per + min(x, extra) + l, ntiles, tiles_n, 4, tm, tn);
+    int tn;
 
-    const int4 te = ((const int4*)(ws + off_tiles(a.G)))[tm];
+    const int4 te = run_tile((const int4*)(ws + off_tiles(a.G)), x * per + min(x, extra) + l, tiles_n, GBM, tn);
     const int g = te.x, start = te.y, rows = te.z;
     const int* sorted = (const int*)(ws + off_sorted(a.M * a.S, a.G));
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -1079,10 +1106,9 @@ __global__ __launch_bounds__(256) void grouped16_dq_kernel(GroupedArgs a, const 
     const int b = (int)blockIdx.x, x = b & 7, l = b >> 3;
     const int per = total >> 3, extra = total & 7;
     if (l >= per + (x < extra ? 1 : 0)) return;
-    int tm, tn;
-    grouped_order(x * per + min(x, extra) + l, ntiles, tiles_n, 4, tm, tn);
+    int tn;
 
-    const int4 te = ((const int4*)(ws + off_tiles(a.G)))[tm];
+    const int4 te = run_tile((const int4*)(ws + off_tiles(a.G)), x * per + min(x, extra) + l, tiles_n, GBM, tn);
     const int g = te.x, start = te.y, rows = te.z;
     const int* sorted = (const int*)(ws + off_sorted(a.M * a.S, a.G));
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -1189,10 +1215,9 @@ __global__ __launch_bounds__(256) void grouped_fp_kernel(GroupedArgs a, const ch
     const int bid = (int)blockIdx.x, x = bid & 7, l = bid >> 3;
     const int per = total >> 3, extra = total & 7;
     if (l >= per + (x < extra ? 1 : 0)) return;
-    int tm, tn;
-    grouped_order(x * per + min(x, extra) + l, ntiles, tiles_n, ORDER_ROWS, tm, tn);
+    int tn;
 
-    const int4 te = ((const int4*)(ws + off_tiles(a.G)))[tm];
+    const int4 te = run_tile((const int4*)(ws + off_tiles(a.G)), x * per + min(x, extra) + l, tiles_n, FT, tn);
     const int g = te.x, start = te.y, rows = te.z;
     const int* sorted = (const int*)(ws + off_sorted(a.M * a.S, a.G));
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;

@@ -21,13 +21,15 @@ def sample_indices(total, n, seed):
     return np.unique(np.concatenate([s, [0, total - 1]]))
 
 
-def routing_from_workspace(ws, M, S, G):
+def routing_from_workspace(ws, M, S, G, BM=256):
     """The grouped routing's result as the grouped kernels read it from the
-    workspace: (tile table rows (group, first sorted pair, rows), sorted pair
-    ids).  Offsets as the library lays the workspace out: a 64-byte header
-    (tile count, invalid count), counts and cursors (int32 x G each), the tile
-    table at the next 256-byte boundary (room for P/128 + G + 1 entries of 4
-    int32), the sorted pair ids at the 256-byte boundary after it."""
+    workspace: (invalid count, tile table rows (group, first sorted pair,
+    rows), sorted pair ids, raw table (group, first pair, end of the group's
+    pairs, run)).  Offsets as the library lays the workspace out: a 64-byte
+    header (tile count, invalid count), counts and cursors (int32 x G each),
+    the tile table at the next 256-byte boundary (room for P/128 + G + 1
+    entries of 4 int32), the sorted pair ids at the 256-byte boundary after
+    it.  BM is the tile height the call routed for."""
     P = M * S
     off_tiles = (64 + 8 * G + 255) // 256 * 256
     cap = P // 128 + G + 1
@@ -36,14 +38,18 @@ def routing_from_workspace(ws, M, S, G):
     hdr = w[:8].view(np.int32)
     ntiles = int(hdr[0])
     assert 0 < ntiles <= cap
-    tiles = w[off_tiles:off_tiles + 16 * ntiles].view(np.int32).reshape(ntiles, 4)[:, :3]
+    raw = w[off_tiles:off_tiles + 16 * ntiles].view(np.int32).reshape(ntiles, 4).copy()
+    tiles = np.stack([raw[:, 0], raw[:, 1], np.minimum(BM, raw[:, 2] - raw[:, 1])], axis=1)
     sorted_ids = w[off_sorted:off_sorted + 4 * P].view(np.int32)
-    return int(hdr[1]), tiles, sorted_ids
+    return int(hdr[1]), tiles, sorted_ids, raw
 
 
-def check_routing(idx, tiles, sorted_ids, G, BM):
+def check_routing(idx, tiles, sorted_ids, G, BM, raw=None):
     """The routing is a counting sort of the pairs by group cut into BM-row
-    tiles (every index valid): tile count, permutation, group runs, tile bounds."""
+    tiles (every index valid): tile count, permutation, group runs, tile bounds.
+    With the raw table: each entry's group end, and the walk runs (first row
+    tile, height) cover each group's row tiles exactly, in order: one run for
+    a group of at most 12 row tiles, runs of at most 8 rows otherwise."""
     idx = np.asarray(idx).reshape(-1)
     counts = np.bincount(idx, minlength=G)
     assert len(tiles) == int(((counts + BM - 1) // BM).sum())
@@ -54,6 +60,22 @@ def check_routing(idx, tiles, sorted_ids, G, BM):
     for ti, (g, start, rows) in enumerate(tiles):
         assert 1 <= rows <= BM and starts[g] <= start and start + rows <= starts[g] + counts[g], (ti, g, start, rows)
     assert int(tiles[:, 2].sum()) == idx.size
+    if raw is None:
+        return
+    ntile = (counts + BM - 1) // BM
+    first = np.concatenate([[0], np.cumsum(ntile)[:-1]])
+    for g in range(G):
+        if ntile[g] == 0:
+            continue
+        ent = raw[first[g]:first[g] + ntile[g]]
+        assert np.all(ent[:, 2] == starts[g] + counts[g]), g
+        t = first[g]
+        while t < first[g] + ntile[g]:
+            c0, h = int(raw[t, 3]) >> 4, (int(raw[t, 3]) & 15) + 1
+            assert c0 == t and t + h <= first[g] + ntile[g], (g, t, c0, h)
+            assert np.all(raw[t:t + h, 3] == raw[t, 3]), (g, t)
+            assert h == ntile[g] if ntile[g] <= 12 else h <= 8, (g, h, ntile[g])
+            t += h
 
 
 def tile_row_pairs(tiles, sorted_ids, per_tile, BM):

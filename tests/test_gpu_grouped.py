@@ -88,6 +88,34 @@ def test_skewed_groups_bf16():
     check_close(host_f64(out), y, t, "bf16", "skewed groups")
 
 
+def test_group_runs_bf16():
+    """Groups of 16, 13 and 12 row tiles beside groups of 4 and an empty one:
+    the tile walk cuts the first two into runs of 8 + 8 and 6 + 7 and keeps
+    the 12 as one run; the routing's run table and every output checked."""
+    rng = np.random.default_rng(21)
+    M, K, N, G, S = 4000, 128, 512, 6, 3
+    inp = synth.store(synth.normal(rng, (M, K)), "bf16")
+    w = synth.store(synth.normal(rng, (G, K, N), 0.05), "bf16")
+    bias = synth.store(synth.uniform(rng, (G, N), -0.1, 0.1), "bf16")
+    idx = np.zeros((M, S), np.int32)
+    idx[:3200, 1], idx[3200:, 1] = 1, 2
+    idx[:3000, 2], idx[3000:, 2] = 3, 4
+    idx = idx[rng.permutation(M)]
+    out = torch.full((M, S, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    out, ws = om.grouped_matmul(dev(inp, "bf16"), dev(w, "bf16"), dev(idx), dev(bias, "bf16"), output=out)
+    assert om.grouped_matmul_check(ws) == 0
+    bad, tiles, sorted_ids, raw = routing_from_workspace(ws, M, S, G, 256)
+    assert bad == 0
+    check_routing(idx, tiles, sorted_ids, G, 256, raw)
+    first_rows = {g: [] for g in np.unique(raw[:, 0]).tolist()}
+    for t, e in enumerate(raw):
+        if (int(e[3]) >> 4) == t:
+            first_rows[int(e[0])].append((int(e[3]) & 15) + 1)
+    assert first_rows == {0: [8, 8], 1: [6, 7], 2: [4], 3: [12], 4: [4]}, first_rows
+    y, t = oracle.grouped_matmul(inp, w, idx, bias, dt="bf16")
+    check_close(host_f64(out), y, t, "bf16", "group runs")
+
+
 def test_invalid_indices_counted_rows_untouched():
     rng = np.random.default_rng(9)
     M, K, N, G, S = 50, 64, 96, 4, 2
@@ -174,9 +202,9 @@ def test_fp_matrix_core_workload_full(dt):
     out = torch.full((M, S, N), float("nan"), dtype=tdt, device="cuda")
     out, ws = om.grouped_matmul(dev(c["input"]), dev(c["weights"]), dev(c["group_indices"]), dev(c["bias"]),
                                 output=out)
-    bad, tiles, sorted_ids = routing_from_workspace(ws, M, S, G)
+    bad, tiles, sorted_ids, raw = routing_from_workspace(ws, M, S, G, 128)
     assert bad == 0
-    check_routing(c["group_indices"], tiles, sorted_ids, G, 128)
+    check_routing(c["group_indices"], tiles, sorted_ids, G, 128, raw)
     y, t = oracle.grouped_matmul(c["input"], c["weights"], c["group_indices"], c["bias"])
     check_close(host_f64(out), y, t, dt, "grouped %s %dx%d, K=%d N=%d G=%d" % (dt, M, S, K, N, G))
 

@@ -188,9 +188,9 @@ def test_full_size_workload_tile_rows():
                                         dev(c["zero_point"]), c["block_size"], dev(c["group_indices"]),
                                         dev(c["bias"], "bf16"), output=out)
     assert om.grouped_matmul_check(ws) == 0
-    bad, tiles, sorted_ids = routing_from_workspace(ws, M, S, G)
+    bad, tiles, sorted_ids, raw = routing_from_workspace(ws, M, S, G, 256)
     assert bad == 0
-    check_routing(c["group_indices"], tiles, sorted_ids, G, 256)
+    check_routing(c["group_indices"], tiles, sorted_ids, G, 256, raw)
     pairs = tile_row_pairs(tiles, sorted_ids, 2, 256)
     sel = np.concatenate([(pairs[:, None] * N + np.arange(N, dtype=np.int64)[None, :]).ravel(),
                           sample_indices(M * S * N, 4000, 11)])

@@ -103,9 +103,9 @@ def test_grouped_bf16_moe_tile_rows():
     idx = c["group_indices"].reshape(-1)
 
     # the routing: a counting sort of the pairs by group, cut into 256-row tiles
-    bad, tiles, sorted_ids = routing_from_workspace(ws, M, S, G)
+    bad, tiles, sorted_ids, raw = routing_from_workspace(ws, M, S, G, 256)
     assert bad == 0
-    check_routing(idx, tiles, sorted_ids, G, 256)
+    check_routing(idx, tiles, sorted_ids, G, 256, raw)
     # eight complete output rows per routed tile, over every row slot of a tile
     pairs = tile_row_pairs(tiles, sorted_ids, 8, 256)
     assert len(pairs) > 3000
