@@ -78,6 +78,15 @@ def check_routing(idx, tiles, sorted_ids, G, BM, raw=None):
             t += h
 
 
+def run_heights(raw):
+    """{group: [row tiles of each walk run, in order]} from the raw tile table."""
+    runs = {}
+    for t, e in enumerate(raw):
+        if (int(e[3]) >> 4) == t:
+            runs.setdefault(int(e[0]), []).append((int(e[3]) & 15) + 1)
+    return runs
+
+
 def tile_row_pairs(tiles, sorted_ids, per_tile, BM):
     """Pairs whose whole output rows a test compares: per_tile rows of every
     routed tile, at slots (j * BM / per_tile + 11 * tile) % BM, which walk every

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from onnx_matmul_family_amd import synth
-from tests.gpu_util import check_close, check_routing, dev, host_f64, routing_from_workspace
+from tests.gpu_util import check_close, check_routing, dev, host_f64, routing_from_workspace, run_heights
 
 pytestmark = pytest.mark.gpu
 
@@ -88,32 +88,38 @@ def test_skewed_groups_bf16():
     check_close(host_f64(out), y, t, "bf16", "skewed groups")
 
 
-def test_group_runs_bf16():
-    """Groups of 16, 13 and 12 row tiles beside groups of 4 and an empty one:
-    the tile walk cuts the first two into runs of 8 + 8 and 6 + 7 and keeps
-    the 12 as one run; the routing's run table and every output checked."""
+# expected walk runs (row tiles per run, per group) of the routing in
+# test_group_runs: a group of at most 12 row tiles is one run, a larger one
+# balanced runs of at most 8
+GROUP_RUNS = {256: {0: [8, 8], 1: [6, 7], 2: [4], 3: [12], 4: [4]},
+              128: {0: [8, 8, 8, 8], 1: [6, 6, 6, 7], 2: [7], 3: [8, 8, 8], 4: [8]}}
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32", "f64"])
+def test_group_runs(dt):
+    """Groups of 4000, 3200 and 3000 pairs beside smaller ones and an empty
+    group: several walk runs per group (256-row tiles for bf16, 128-row
+    tiles for fp32 / fp64); the routing's run table and every output checked."""
     rng = np.random.default_rng(21)
     M, K, N, G, S = 4000, 128, 512, 6, 3
-    inp = synth.store(synth.normal(rng, (M, K)), "bf16")
-    w = synth.store(synth.normal(rng, (G, K, N), 0.05), "bf16")
-    bias = synth.store(synth.uniform(rng, (G, N), -0.1, 0.1), "bf16")
+    BM = 256 if dt == "bf16" else 128
+    inp = synth.store(synth.normal(rng, (M, K)), dt)
+    w = synth.store(synth.normal(rng, (G, K, N), 0.05), dt)
+    bias = synth.store(synth.uniform(rng, (G, N), -0.1, 0.1), dt)
     idx = np.zeros((M, S), np.int32)
     idx[:3200, 1], idx[3200:, 1] = 1, 2
     idx[:3000, 2], idx[3000:, 2] = 3, 4
     idx = idx[rng.permutation(M)]
-    out = torch.full((M, S, N), float("nan"), dtype=torch.bfloat16, device="cuda")
-    out, ws = om.grouped_matmul(dev(inp, "bf16"), dev(w, "bf16"), dev(idx), dev(bias, "bf16"), output=out)
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32, "f64": torch.float64}[dt]
+    out = torch.full((M, S, N), float("nan"), dtype=tdt, device="cuda")
+    out, ws = om.grouped_matmul(dev(inp, dt), dev(w, dt), dev(idx), dev(bias, dt), output=out)
     assert om.grouped_matmul_check(ws) == 0
-    bad, tiles, sorted_ids, raw = routing_from_workspace(ws, M, S, G, 256)
+    bad, tiles, sorted_ids, raw = routing_from_workspace(ws, M, S, G, BM)
     assert bad == 0
-    check_routing(idx, tiles, sorted_ids, G, 256, raw)
-    first_rows = {g: [] for g in np.unique(raw[:, 0]).tolist()}
-    for t, e in enumerate(raw):
-        if (int(e[3]) >> 4) == t:
-            first_rows[int(e[0])].append((int(e[3]) & 15) + 1)
-    assert first_rows == {0: [8, 8], 1: [6, 7], 2: [4], 3: [12], 4: [4]}, first_rows
-    y, t = oracle.grouped_matmul(inp, w, idx, bias, dt="bf16")
-    check_close(host_f64(out), y, t, "bf16", "group runs")
+    check_routing(idx, tiles, sorted_ids, G, BM, raw)
+    assert run_heights(raw) == GROUP_RUNS[BM]
+    y, t = oracle.grouped_matmul(inp, w, idx, bias, dt=dt)
+    check_close(host_f64(out), y, t, dt, "group runs")
 
 
 def test_invalid_indices_counted_rows_untouched():

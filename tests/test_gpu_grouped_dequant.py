@@ -12,8 +12,8 @@ import torch
 
 import oracle
 from onnx_matmul_family_amd import synth
-from tests.gpu_util import (check_close, check_routing, dev, host_f64, routing_from_workspace, sample_indices,
-                            tile_row_pairs)
+from tests.gpu_util import (check_close, check_routing, dev, host_f64, routing_from_workspace, run_heights,
+                            sample_indices, tile_row_pairs)
 
 pytestmark = pytest.mark.gpu
 
@@ -174,6 +174,28 @@ def test_f32_matrix_core_multi_tile(qdt):
     assert bad == 0
     y, t = oracle.grouped_matmul_dequant(inp, q, sc, zp, bs, idx, bias, dt="f32")
     check_close(host_f64(out), y, t, "f32", "grouped dq f32 multi-tile")
+
+
+@pytest.mark.parametrize("dt,N", [("bf16", 512), ("bf16", 264), ("f32", 512)])
+def test_group_runs(dt, N):
+    """Groups of 4000 and 3200 pairs beside one of 800: several walk runs per
+    group on the weights-by-DMA kernel (N = 512), the register-staged one
+    (N = 264) and the fp32 kernel (128-row tiles); run table and every output."""
+    rng = np.random.default_rng(33)
+    M, K, G, S, bs = 4000, 128, 3, 2, 64
+    inp, q, scale, zp, _, bias = make(rng, M, K, N, G, S, bs, np.int8, True, dt)
+    idx = np.zeros((M, S), np.int32)
+    idx[:, 1] = np.where(np.arange(M) < 3200, 1, 2)
+    idx = idx[rng.permutation(M)]
+    BM = 128 if dt == "f32" else 256
+    out, ws = om.grouped_matmul_dequant(dev(inp, dt), dev(q), dev(scale, dt), dev(zp), bs, dev(idx), dev(bias, dt))
+    assert om.grouped_matmul_check(ws) == 0
+    bad, tiles, sorted_ids, raw = routing_from_workspace(ws, M, S, G, BM)
+    check_routing(idx, tiles, sorted_ids, G, BM, raw)
+    assert run_heights(raw) == ({0: [8, 8], 1: [6, 7], 2: [4]} if BM == 256 else
+                                {0: [8, 8, 8, 8], 1: [6, 6, 6, 7], 2: [7]})
+    y, t = oracle.grouped_matmul_dequant(inp, q, scale, zp, bs, idx, bias, dt=dt)
+    check_close(host_f64(out), y, t, dt, "quantised experts, group runs")
 
 
 def test_full_size_workload_tile_rows():
