@@ -11,7 +11,8 @@
 //      histograms of the M*S indices over the G groups folded into global
 //      counts (invalid indices are counted, not routed); exclusive scans of
 //      the counts and of the per-group tile counts into the tile table
-//      (group, first sorted pair, rows); the scatter of pair ids p = m*S + i
+//      (group, first sorted pair, end of the group's pairs, walk run); the
+//      scatter of pair ids p = m*S + i
 //      into group order, each workgroup reserving its range per group with
 //      one global atomic;
 //   2. grouped16_kernel: one 256x256 output tile per workgroup, rows gathered
@@ -19,11 +20,13 @@
 //      transposing LDS path), 16x16x32 MFMAs (32x32x16 on the element-wise
 //      path for unaligned operands), epilogue adds bias[g] in fp32, rounds
 //      once and writes each row to output[p].  The grid is the upper bound
-//      (M*S/BM + G) x (N/BN); the routed tiles are split evenly over the 8
-//      XCDs and each XCD's surplus workgroups exit.
+//      (M*S/BM + G) x (N/BN); the routed tiles, walked in runs aligned to the
+//      groups, are split evenly over the 8 XCDs and each XCD's surplus
+//      workgroups exit.
 //   Weight-only quantised experts (int8/uint8 weights with block scales) run
 //   the same routing and grouped16_dq_dma_kernel / grouped16_dq_kernel, which
-//   dequantise each weight tile on its way into the MFMAs.
+//   dequantise each weight tile on its way into the MFMAs; fp32 / fp64 run it
+//   with 128-row tiles and grouped_fp_kernel.
 // No host synchronisation between the two.  Each output row depends only on
 // its own pair, so the order of pairs inside a group never changes a value.
 #include "gemm16_core.hpp"
