@@ -743,7 +743,9 @@ template <int DT, int MR>
 hipError_t launch_skinny_nmaj(const DenseArgs& a, hipStream_t s) {
     const int64_t NB = a.nb0 * a.nb1;
     const size_t lds = (size_t)a.K * MR * 2;
-    if ((a.N + 31) / 32 * NB >= 512) {
+    // 32-column groups (64-byte row pieces) once there is one per CU: at M = 1,
+    // N = K = 8192 (256 groups) 30 against 35 us with 16-column groups
+    if ((a.N + 31) / 32 * NB >= 256) {
         hipLaunchKernelGGL((skinny_nmaj_kernel<DT, MR, 32>), dim3((unsigned)((a.N + 31) / 32), (unsigned)NB), dim3(256),
                            lds, s, a);
     } else {

@@ -322,8 +322,10 @@ def test_gemm_skinny_stream(dt, M, N, K):
 
 
 SKINNY_NMAJ = [  # MatMul with a few rows against B stored (K, N): the vector-ALU streaming kernel
+    # (16- or 32-column workgroups over all of K, or 64-column ones with K split over workgroups + reduction)
     ((1, 8192), (8192, 8192)), ((8192,), (8192, 4096)), ((3, 2048), (2048, 4104)), ((2, 1024), (1024, 8200)),
     ((2, 1, 1024), (2, 1024, 2048)), ((4, 4096), (4096, 4096)), ((4, 7680), (7680, 4096)),
+    ((2, 1, 4096), (2, 4096, 2048)),  # batched, K split over workgroups
 ]
 
 
