@@ -245,27 +245,27 @@ __global__ __launch_bounds__(NT) void dense16_kernel(DenseArgs p, int tiles_m, i
 
 // The same epilogue in the 16x16 accumulator layout (tile (i, j), register e
 // of lane l: row 16 i + l%16, column 16 j + 4 (l/16) + e of the wave's
-// 128 x 128 block); operands and output as the DMA path requires (Y 8-byte
-// aligned).
-template <int DT>
-__device__ __forceinline__ void epilogue_t16(const DenseArgs& p, const f32x4_t (&acc)[8][8], uint16_t* __restrict__ Y,
+// 16 TM x 16 TN block); operands and output as the DMA path requires (Y
+// 8-byte aligned).
+template <int DT, int TM, int TN>
+__device__ __forceinline__ void epilogue_t16(const DenseArgs& p, const f32x4_t (&acc)[TM][TN], uint16_t* __restrict__ Y,
                                              int64_t m0, int64_t n0, int lane, int wm, int wn) {
     const float alpha = p.alpha, beta = p.beta;
     const int64_t M = p.M, N = p.N;
     const uint16_t* __restrict__ Cp = (const uint16_t*)p.C;
     const bool vec_store = (N % 4 == 0) && (p.ldy % 4 == 0);
     const bool c_cols = Cp && p.c_sm == 0;  // C constant along m
-    const int64_t nl = n0 + wn * 128 + 4 * (lane >> 4);
-    const int64_t ml = m0 + wm * 128 + (lane & 15);
-    float cb[8][4];
+    const int64_t nl = n0 + wn * (16 * TN) + 4 * (lane >> 4);
+    const int64_t ml = m0 + wm * (16 * TM) + (lane & 15);
+    float cb[TN][4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) cb[j][e] = 0.0f;
     if (c_cols) {
         const bool c_vec = p.c_sn == 1 && (N % 4 == 0) && (((uintptr_t)Cp & 7) == 0);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < TN; ++j) {
             const int64_t n = nl + 16 * j;
             if (c_vec && n < N) {
                 const u32x2_t c2 = *(const u32x2_t*)(Cp + n);
@@ -280,18 +280,18 @@ __device__ __forceinline__ void epilogue_t16(const DenseArgs& p, const f32x4_t (
             }
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e) cb[j][e] *= beta;
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < TM; ++i) {
         const int64_t m = ml + 16 * i;
         if (m >= M) continue;
         uint16_t* __restrict__ yr = Y + m * p.ldy;
         if (Cp && !c_cols) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int64_t n = nl + 16 * j + e;
@@ -299,7 +299,7 @@ __device__ __forceinline__ void epilogue_t16(const DenseArgs& p, const f32x4_t (
                 }
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < TN; ++j) {
             const int64_t n = nl + 16 * j;
             if (n >= N) continue;
             float v[4];
@@ -319,17 +319,19 @@ __device__ __forceinline__ void epilogue_t16(const DenseArgs& p, const f32x4_t (
     }
 }
 
-// 256x256 tiles on the DMA path in the 16x16x32 MFMA form (mainloop_dma16):
-// MODE 2 / 3 as in dense16_kernel (every tile full, no C or a bias row C, the
-// LDS-staged epilogue); MODE 1 any shape and C (checked loads on ragged
-// tiles, epilogue_t16).  Same
+// BT x BT tiles (256, or 128 for shapes with too few 256-tiles to fill the
+// chip) on the DMA path in the 16x16x32 MFMA form (mainloop_dma16): MODE 2 / 3
+// as in dense16_kernel (every tile full, no C or a bias row C, the LDS-staged
+// epilogue; BT = 256 only); MODE 1 any shape and C (checked loads on ragged
+// tiles; 256-tiles leave through LDS where they can, else epilogue_t16).  Same
 // work per stage as the 32x32x16 form, but measured on gfx950 the chip holds a
 // higher shader clock under it (~1.55 against ~1.35 GHz on one box at 8192^3
 // with both operands k-major), which more than pays for its lower
 // matrix-pipe busy share.
-template <int DT, int MODE, bool AK, bool BKM>
+template <int DT, int MODE, bool AK, bool BKM, int BT>
 __global__ __launch_bounds__(NT) void dense16_t16_kernel(DenseArgs p, int tiles_m, int tiles_n) {
-    constexpr int BM = 256, BN = 256;
+    static_assert(BT == 256 || (BT == 128 && MODE == 1), "128-tiles: any-shape mode only");
+    constexpr int BM = BT, BN = BT;
     constexpr int STAGE = (BM + BN) * KSTEP * 2;
     __shared__ __attribute__((aligned(1024))) char smem0[STAGE];
     __shared__ __attribute__((aligned(1024))) char smem1[STAGE];
@@ -345,7 +347,7 @@ __global__ __launch_bounds__(NT) void dense16_t16_kernel(DenseArgs p, int tiles_
     const uint16_t* __restrict__ B = (const uint16_t*)p.B + z0 * p.b_bs0 + z1 * p.b_bs1;
     uint16_t* __restrict__ Y = (uint16_t*)p.Y + z0 * p.y_bs0 + z1 * p.y_bs1;
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-    f32x4_t acc[8][8];  // written by the first k-block (K > 0 on this path)
+    f32x4_t acc[BM / 32][BN / 32];  // written by the first k-block (K > 0 on this path)
     const int nk = (int)((p.K + KSTEP - 1) / KSTEP);
     DmaSrc<BM, AK> srcA;
     DmaSrc<BN, BKM> srcB;
@@ -356,27 +358,32 @@ __global__ __launch_bounds__(NT) void dense16_t16_kernel(DenseArgs p, int tiles_
         mainloop_dma16<BM, BN, DT, AK, BKM, false>(acc, smem0, smem1, srcA, srcB, nk, lane, wm, wn, wave);
     else
         mainloop_dma16<BM, BN, DT, AK, BKM, true>(acc, smem0, smem1, srcA, srcB, nk, lane, wm, wn, wave);
-    if constexpr (MODE == 1) {
+    if constexpr (BT == 128) {
+        epilogue_t16<DT, BM / 32, BN / 32>(p, acc, Y, m0, n0, lane, wm, wn);
+        return;
+    } else if constexpr (MODE == 1) {
         // whole tiles with no C or a bias row C leave through LDS as whole row
         // segments (16-byte stores: Y and its row stride 16-byte aligned); edge
         // tiles and a C that varies along m use the 4-value stores
         const bool staged = m0 + BM <= p.M && n0 + BN <= p.N && p.ldy % 8 == 0 && ((uintptr_t)Y & 15) == 0 &&
                             (!p.C || (p.c_sm == 0 && p.c_sn == 1 && ((uintptr_t)p.C & 7) == 0));
         if (!staged) {
-            epilogue_t16<DT>(p, acc, Y, m0, n0, lane, wm, wn);
+            epilogue_t16<DT, 8, 8>(p, acc, Y, m0, n0, lane, wm, wn);
             return;
         }
     }
-    __syncthreads();
-    char* stage = (wave < 2 ? smem0 : smem1) + (wave & 1) * (STAGE / 2);
-    const int64_t col0 = n0 + wn * (BN / 2);
-    uint16_t* yb = Y + (m0 + wm * (BM / 2)) * p.ldy + col0;
-    const int64_t ldy = p.ldy;
-    auto st = [&](int, int r, int c, const u32x4_t& d) { *(u32x4_t*)(yb + r * ldy + 8 * c) = d; };
-    if (MODE == 3 || (MODE == 1 && p.C))
-        wave_epilogue_lds16<DT, true>(acc, p.alpha, (const uint16_t*)p.C + col0, p.beta, stage, lane, st);
-    else
-        wave_epilogue_lds16<DT, false>(acc, p.alpha, nullptr, p.beta, stage, lane, st);
+    if constexpr (BT == 256) {
+        __syncthreads();
+        char* stage = (wave < 2 ? smem0 : smem1) + (wave & 1) * (STAGE / 2);
+        const int64_t col0 = n0 + wn * (BN / 2);
+        uint16_t* yb = Y + (m0 + wm * (BM / 2)) * p.ldy + col0;
+        const int64_t ldy = p.ldy;
+        auto st = [&](int, int r, int c, const u32x4_t& d) { *(u32x4_t*)(yb + r * ldy + 8 * c) = d; };
+        if (MODE == 3 || (MODE == 1 && p.C))
+            wave_epilogue_lds16<DT, true>(acc, p.alpha, (const uint16_t*)p.C + col0, p.beta, stage, lane, st);
+        else
+            wave_epilogue_lds16<DT, false>(acc, p.alpha, nullptr, p.beta, stage, lane, st);
+    }
 }
 
 
@@ -766,24 +773,24 @@ hipError_t launch_cfg(const DenseArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int DT, int MODE, bool AK, bool BKM>
+template <int DT, int MODE, bool AK, bool BKM, int BT>
 hipError_t launch_t16(const DenseArgs& a, hipStream_t s) {
-    const int64_t tiles_m = (a.M + 255) / 256, tiles_n = (a.N + 255) / 256;
+    const int64_t tiles_m = (a.M + BT - 1) / BT, tiles_n = (a.N + BT - 1) / BT;
     const int64_t total = tiles_m * tiles_n * a.nb0 * a.nb1;
     if (total <= 0) return hipSuccess;
     if (total > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((dense16_t16_kernel<DT, MODE, AK, BKM>), dim3((unsigned)total), dim3(NT), 0, s, a, (int)tiles_m,
-                       (int)tiles_n);
+    hipLaunchKernelGGL((dense16_t16_kernel<DT, MODE, AK, BKM, BT>), dim3((unsigned)total), dim3(NT), 0, s, a,
+                       (int)tiles_m, (int)tiles_n);
     return hipGetLastError();
 }
 
 template <int BM, int BN, int DT, int MODE>
 hipError_t launch_layout(const DenseArgs& a, hipStream_t s) {
-    if constexpr (BM == 256 && MODE >= 1 && MODE <= 3) {
-        if (a.a_kmajor && a.b_kmajor) return launch_t16<DT, MODE, true, true>(a, s);
-        if (a.a_kmajor) return launch_t16<DT, MODE, true, false>(a, s);
-        if (a.b_kmajor) return launch_t16<DT, MODE, false, true>(a, s);
-        return launch_t16<DT, MODE, false, false>(a, s);
+    if constexpr ((BM == 256 && MODE >= 1 && MODE <= 3) || (BM == 128 && MODE == 1)) {
+        if (a.a_kmajor && a.b_kmajor) return launch_t16<DT, MODE, true, true, BM>(a, s);
+        if (a.a_kmajor) return launch_t16<DT, MODE, true, false, BM>(a, s);
+        if (a.b_kmajor) return launch_t16<DT, MODE, false, true, BM>(a, s);
+        return launch_t16<DT, MODE, false, false, BM>(a, s);
     }
     if (a.a_kmajor && a.b_kmajor) return launch_cfg<BM, BN, DT, true, true, MODE>(a, s);
     if (a.a_kmajor && !a.b_kmajor) return launch_cfg<BM, BN, DT, true, false, MODE>(a, s);
@@ -940,7 +947,7 @@ const char* plan_name(const Plan16& pl) {
         case Plan16::SKINNY1: return "skinny rows against k-contiguous B (16 columns per workgroup)";
         case Plan16::SKINNY_SPLIT: return "skinny rows, K split over workgroups + fixed-order reduction";
         case Plan16::SPLIT128: return "128x128x64 tiles, K split over workgroups + fixed-order reduction";
-        case Plan16::T128_VEC: return "128x128x64 tiles, 32x32x16 MFMA, DMA";
+        case Plan16::T128_VEC: return "128x128x64 tiles, 16x16x32 MFMA, DMA";
         case Plan16::T128_REG: return "128x128x64 tiles, 32x32x16 MFMA, register-staged loads";
     }
     return "?";

@@ -750,6 +750,12 @@ __device__ __forceinline__ void acc_fence(f32x4_t (&acc)[TM][8]) {
                      : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
                        "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
 }
+template <int TM>
+__device__ __forceinline__ void acc_fence(f32x4_t (&acc)[TM][4]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]));
+}
 template <int R, bool KMAJ>
 __device__ __forceinline__ u32x4_t read_frag16(const char* lds, int mnb, int s, int lane) {
     if constexpr (KMAJ) {

@@ -125,6 +125,28 @@ def test_ragged_256_tiles_k_tail_exact(dt, tA, tB, cform):
                                                                       want[tuple(bad[0])])
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("tA,tB", [(0, 1), (0, 0), (1, 0), (1, 1)])
+@pytest.mark.parametrize("cform", list(C_FORMS))
+def test_ragged_128_tiles_k_tail_exact(dt, tA, tB, cform):
+    """Fewer than 256 tiles of 256x256 (here 4 x 5): 128x128 tiles on the same
+    16x16x32 DMA kernel, ragged in M, N and K (1000 x 1064 x 1032: 16 stages
+    of 64 + 8), every C form, small integers: bit for bit, every element."""
+    rng = np.random.default_rng(700 + 8 * tA + 4 * tB + list(C_FORMS).index(cform))
+    M, N, K = 1000, 1064, 1032
+    A = synth.store(synth.small_ints(rng, (K, M) if tA else (M, K), -1, 1), dt)
+    B = synth.store(synth.small_ints(rng, (N, K) if tB else (K, N), -1, 1), dt)
+    C = synth.store(synth.small_ints(rng, C_FORMS[cform](M, N), -8, 8), dt)
+    Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16 if dt == "bf16" else torch.float16, device="cuda")
+    om.gemm(dev(A, dt), dev(B, dt), dev(C, dt), 1.0, 1.0, tA, tB, Y)
+    torch.cuda.synchronize()
+    y, _ = oracle.gemm(A, B, C, 1.0, 1.0, tA, tB, dt=dt)
+    got, want = host_f32(Y), rne(y, dt)
+    bad = np.argwhere(~(got == want))
+    assert bad.size == 0, "%d differ, first at %s: got %r want %r" % (len(bad), tuple(bad[0]), got[tuple(bad[0])],
+                                                                      want[tuple(bad[0])])
+
+
 @pytest.mark.parametrize("tA,tB", [(0, 1), (0, 0), (1, 0), (1, 1)])
 def test_ragged_256_tiles_long_k_tail_exact(tA, tB):
     """The same kernel with K = 4104 (64 whole stages and a tail of 8, an odd
