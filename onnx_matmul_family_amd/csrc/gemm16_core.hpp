@@ -866,11 +866,12 @@ __device__ __forceinline__ void mainloop_dma16(f32x4_t (&acc)[BM / 32][BN / 32],
     acc_fence(acc);
 }
 
-// Epilogue of one wave's 128 x 128 block in the 16x16 accumulator layout
+// Epilogue of one wave's 16 TM x 128 block in the 16x16 accumulator layout
 // (tile (i, j), register e of lane l: row 16 i + l%16, column 16 j + 4 (l/16) + e),
-// through the same LDS staging and row-segment stores as wave_epilogue_lds_f.
-template <int DT, bool BIAS, class StoreRow>
-__device__ __forceinline__ void wave_epilogue_lds16(const f32x4_t (&acc)[8][8], float alpha, const uint16_t* bias,
+// through the same LDS staging and row-segment stores as wave_epilogue_lds_f
+// (store(k, r, c, d): row r = 4 k + l/16 of the block, 16-byte chunk c).
+template <int DT, bool BIAS, int TM, class StoreRow>
+__device__ __forceinline__ void wave_epilogue_lds16(const f32x4_t (&acc)[TM][8], float alpha, const uint16_t* bias,
                                                     float beta, char* stage, int lane, StoreRow&& store) {
     constexpr int ROWB = 256, NCH = 16;
     const int g = lane >> 4, h = g & 1;
@@ -890,7 +891,7 @@ __device__ __forceinline__ void wave_epilogue_lds16(const f32x4_t (&acc)[8][8], 
         }
         const int c = 2 * j + (g >> 1);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < TM; ++i) {
             const int r = 16 * i + (lane & 15);
             float v[4];
 #pragma unroll
@@ -902,7 +903,7 @@ __device__ __forceinline__ void wave_epilogue_lds16(const f32x4_t (&acc)[8][8], 
         }
     }
 #pragma unroll
-    for (int k = 0; k < 32; ++k) {
+    for (int k = 0; k < 4 * TM; ++k) {
         const int r = 4 * k + (lane >> 4), c = lane & 15;
         const u32x4_t d = *(const u32x4_t*)(stage + r * ROWB + ((c ^ (r % NCH)) << 4));
         store(k, r, c, d);

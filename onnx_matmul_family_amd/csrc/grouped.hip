@@ -15,7 +15,8 @@
 //      scatter of pair ids p = m*S + i
 //      into group order, each workgroup reserving its range per group with
 //      one global atomic;
-//   2. grouped16_kernel: one 256x256 output tile per workgroup, rows gathered
+//   2. grouped16_kernel: one 256x256 output tile per workgroup (128x256 for a
+//      group's last tile of at most 128 rows), rows gathered
 //      from input[p / S], B = weights[g] (n contiguous, read through the
 //      transposing LDS path), 16x16x32 MFMAs (32x32x16 on the element-wise
 //      path for unaligned operands), epilogue adds bias[g] in fp32, rounds
@@ -337,8 +338,8 @@ __device__ __forceinline__ void grouped_body(const GroupedArgs& a, const char* w
 // leave through LDS as whole row segments; a ragged column tile (N % 8 == 0
 // here, so a lane's 4 columns are all in range or all out) stores 4 values
 // per row.
-template <int DT>
-__device__ __forceinline__ void grouped_epilogue16(const f32x4_t (&acc)[8][8], const GroupedArgs& a, int g, int rows,
+template <int DT, int TM>
+__device__ __forceinline__ void grouped_epilogue16(const f32x4_t (&acc)[TM][8], const GroupedArgs& a, int g, int rows,
                                                    int start, const int* sorted, int64_t n0, int lane, int wave,
                                                    char* s0, char* s1, const int* orow_s) {
     using namespace core16;
@@ -349,7 +350,7 @@ __device__ __forceinline__ void grouped_epilogue16(const f32x4_t (&acc)[8][8], c
         char* stage = (wave < 2 ? s0 : s1) + (wave & 1) * (GBM * KSTEP * 2);
         const int64_t col0 = n0 + wn * (GBN / 2);
         uint16_t* out = (uint16_t*)a.output + col0;
-        const int* orow_w = orow_s + wm * (GBM / 2);
+        const int* orow_w = orow_s + wm * (16 * TM);
         auto st = [&](int, int r, int c, const u32x4_t& d) {
             const int o = orow_w[r];
             if (o >= 0) *(u32x4_t*)(out + (int64_t)o * N + 8 * c) = d;
@@ -364,10 +365,10 @@ __device__ __forceinline__ void grouped_epilogue16(const f32x4_t (&acc)[8][8], c
     const uint16_t* __restrict__ bias = a.bias ? (const uint16_t*)a.bias + (int64_t)g * N : nullptr;
     uint16_t* __restrict__ out = (uint16_t*)a.output;
     const int64_t nl = n0 + wn * 128 + 4 * (lane >> 4);
-    int orow[8];
+    int orow[TM];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = wm * 128 + 16 * i + (lane & 15);
+    for (int i = 0; i < TM; ++i) {
+        const int r = wm * (16 * TM) + 16 * i + (lane & 15);
         orow[i] = r < rows ? sorted[start + r] : -1;
     }
 #pragma unroll
@@ -383,7 +384,7 @@ __device__ __forceinline__ void grouped_epilogue16(const f32x4_t (&acc)[8][8], c
             bv[3] = from_bits<DT>((uint16_t)(b2.y >> 16));
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < TM; ++i) {
             if (orow[i] < 0) continue;
             u32x2_t o;
             o.x = pack2<DT>(acc[i][j][0] + bv[0], acc[i][j][1] + bv[1]);
@@ -393,7 +394,9 @@ __device__ __forceinline__ void grouped_epilogue16(const f32x4_t (&acc)[8][8], c
     }
 }
 
-template <int DT>
+// BM = 256, or 128 for a group's last tile of at most 128 rows (4 row blocks
+// of 16 per wave: about half the MFMAs and A traffic of a 256-row tile).
+template <int DT, int BM>
 __device__ __forceinline__ void grouped_body16(const GroupedArgs& a, const char* ws, int4 te, int tn, char* s0,
                                                char* s1, int* orow_s, uint32_t* roff_s, uint16_t* bias_s) {
     const int g = te.x, start = te.y, rows = te.z;
@@ -404,52 +407,56 @@ __device__ __forceinline__ void grouped_body16(const GroupedArgs& a, const char*
     const int64_t n0 = (int64_t)tn * GBN;
 
     using namespace core16;
-    f32x4_t acc[8][8];  // written by the first k-block
+    static_assert(BM == 256 || BM == 128, "tile height");
+    f32x4_t acc[BM / 32][8];  // written by the first k-block
     const int nk = (int)((K + KSTEP - 1) / KSTEP);
     const uint16_t* wg = (const uint16_t*)a.weights + (int64_t)g * K * N;
     const int srow = t < rows ? sorted[start + t] : -1;  // output row (token * S + slot) of tile row t
-    orow_s[t] = srow;
+    if (t < BM) orow_s[t] = srow;
     // Whole-tile epilogue with 32-bit row offsets: the tile's bias columns and
     // its output row byte offsets are staged in LDS now, so the epilogue
     // neither waits on global loads nor branches per row.  Row r of wave
-    // block wm goes to roff_s[128 wm + 32 (r % 4) + r / 4 % 32]: the 32 rows a
-    // lane stores are contiguous.
+    // block wm (BM / 2 rows) goes to roff_s[(BM / 2) wm + (BM / 8) (r % 4) + r / 4]:
+    // the BM / 8 rows a lane stores are contiguous.
     const bool fast = n0 + GBN <= N && ((uintptr_t)a.output & 15) == 0 && (int64_t)a.M * S * N * 2 < (1LL << 31);
     if (fast) {
-        const int rr = t & 127;
-        roff_s[(t & 128) + 32 * (rr & 3) + (rr >> 2)] = srow >= 0 ? (uint32_t)srow * (uint32_t)(N * 2) : DMA_OOB;
+        const int rr = t % (BM / 2);
+        if (t < BM)
+            roff_s[(t / (BM / 2)) * (BM / 2) + (BM / 8) * (rr & 3) + (rr >> 2)] =
+                srow >= 0 ? (uint32_t)srow * (uint32_t)(N * 2) : DMA_OOB;
         if (a.bias && t < GBN / 4)
             *(u32x2_t*)(bias_s + 4 * t) = *(const u32x2_t*)((const uint16_t*)a.bias + (int64_t)g * N + n0 + 4 * t);
     }
-    GatherDma<GBM> srcA;
+    GatherDma<BM> srcA;
     srcA.base = (const char*)a.input;
     srcA.K = K;
     srcA.lane = lane;
 #pragma unroll
-    for (int j = 0; j < GatherDma<GBM>::PER_WAVE; ++j) {
-        const int r = GatherDma<GBM>::row_of(wave, j, lane);
-        srcA.roff[j] = r < rows ? (uint32_t)((int64_t)(sorted[start + r] / S) * K * 2) + (GatherDma<GBM>::chunk(j, lane) << 4)
+    for (int j = 0; j < GatherDma<BM>::PER_WAVE; ++j) {
+        const int r = GatherDma<BM>::row_of(wave, j, lane);
+        srcA.roff[j] = r < rows ? (uint32_t)((int64_t)(sorted[start + r] / S) * K * 2) + (GatherDma<BM>::chunk(j, lane) << 4)
                                 : DMA_OOB;
     }
     DmaSrc<GBN, false> srcB;
     srcB.init(wg, N, n0, N, K, lane);
-    if (rows == GBM && n0 + GBN <= N && K % KSTEP == 0)
-        mainloop_dma16<GBM, GBN, DT, true, false, false>(acc, s0, s1, srcA, srcB, nk, lane, wm, wn, wave);
+    // (rows past the tile's end read zeros through their out-of-range offsets either way)
+    if ((BM == GBM ? rows == GBM : true) && n0 + GBN <= N && K % KSTEP == 0)
+        mainloop_dma16<BM, GBN, DT, true, false, false>(acc, s0, s1, srcA, srcB, nk, lane, wm, wn, wave);
     else
-        mainloop_dma16<GBM, GBN, DT, true, false, true>(acc, s0, s1, srcA, srcB, nk, lane, wm, wn, wave);
+        mainloop_dma16<BM, GBN, DT, true, false, true>(acc, s0, s1, srcA, srcB, nk, lane, wm, wn, wave);
 
     if (fast) {
         __syncthreads();  // every wave is done reading the last stage
-        char* stage = (wave < 2 ? s0 : s1) + (wave & 1) * (GBM * KSTEP * 2);
+        char* stage = (wave < 2 ? s0 : s1) + (wave & 1) * (GBM * KSTEP * 2);  // 16 BM bytes x 128 rows fit
         const uint64_t ob = (uint64_t)((uint16_t*)a.output + n0 + wn * (GBN / 2));
         const uint64_t obu = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)ob) |
                              ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(ob >> 32)) << 32);
         const __amdgpu_buffer_rsrc_t out =
             __builtin_amdgcn_make_buffer_rsrc((void*)obu, (short)0, 0x7fffffff, 0x00020000);
-        uint32_t ro[32];
-        const u32x4_t* rw = (const u32x4_t*)(roff_s + 128 * wm + 32 * (lane >> 4));
+        uint32_t ro[BM / 8];
+        const u32x4_t* rw = (const u32x4_t*)(roff_s + (BM / 2) * wm + (BM / 8) * (lane >> 4));
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < BM / 32; ++i) {
             const u32x4_t v = rw[i];
             ro[4 * i] = v.x;
             ro[4 * i + 1] = v.y;
@@ -465,7 +472,7 @@ __device__ __forceinline__ void grouped_body16(const GroupedArgs& a, const char*
             wave_epilogue_lds16<DT, false>(acc, 1.0f, nullptr, 1.0f, stage, lane, st);
         return;
     }
-    grouped_epilogue16<DT>(acc, a, g, rows, start, sorted, n0, lane, wave, s0, s1, orow_s);
+    grouped_epilogue16<DT, BM / 32>(acc, a, g, rows, start, sorted, n0, lane, wave, s0, s1, orow_s);
 }
 
 template <int DT, bool VEC>
@@ -487,9 +494,12 @@ __global__ __launch_bounds__(256) void grouped16_kernel(GroupedArgs a, const cha
     const int w = x * per + min(x, extra) + l;
     int tn;
     const int4 te = run_tile((const int4*)(ws + off_tiles(a.G)), w, tiles_n, GBM, tn);
-    if constexpr (VEC)
-        grouped_body16<DT>(a, ws, te, tn, s0, s1, orow_s, roff_s, bias_s);
-    else
+    if constexpr (VEC) {
+        if (te.z <= GBM / 2)
+            grouped_body16<DT, GBM / 2>(a, ws, te, tn, s0, s1, orow_s, roff_s, bias_s);
+        else
+            grouped_body16<DT, GBM>(a, ws, te, tn, s0, s1, orow_s, roff_s, bias_s);
+    } else
         grouped_body<DT>(a, ws, te, tn, s0, s1, orow_s);
 }
 
