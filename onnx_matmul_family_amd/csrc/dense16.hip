@@ -791,11 +791,12 @@ hipError_t launch_layout(const DenseArgs& a, hipStream_t s) {
         if (a.a_kmajor) return launch_t16<DT, MODE, true, false, BM>(a, s);
         if (a.b_kmajor) return launch_t16<DT, MODE, false, true, BM>(a, s);
         return launch_t16<DT, MODE, false, false, BM>(a, s);
+    } else {  // (an else, so that the 32x32 kernel is not instantiated for these modes)
+        if (a.a_kmajor && a.b_kmajor) return launch_cfg<BM, BN, DT, true, true, MODE>(a, s);
+        if (a.a_kmajor && !a.b_kmajor) return launch_cfg<BM, BN, DT, true, false, MODE>(a, s);
+        if (!a.a_kmajor && a.b_kmajor) return launch_cfg<BM, BN, DT, false, true, MODE>(a, s);
+        return launch_cfg<BM, BN, DT, false, false, MODE>(a, s);
     }
-    if (a.a_kmajor && a.b_kmajor) return launch_cfg<BM, BN, DT, true, true, MODE>(a, s);
-    if (a.a_kmajor && !a.b_kmajor) return launch_cfg<BM, BN, DT, true, false, MODE>(a, s);
-    if (!a.a_kmajor && a.b_kmajor) return launch_cfg<BM, BN, DT, false, true, MODE>(a, s);
-    return launch_cfg<BM, BN, DT, false, false, MODE>(a, s);
 }
 
 // The kernel choice for one launch and the split-K workspace it needs.
