@@ -9,7 +9,9 @@ written by the MFMAs themselves); the int8 loop's uint8 operands are flipped
 to int8 in their registers at least three MFMAs ahead of their first use.
 This test compiles the three kernel files for gfx950 and checks that no VALU
 instruction writes a source register of such an MFMA within 4 wait states
-before it.  CPU only (hipcc cross-compiles); skipped without hipcc."""
+before it.  Only MFMAs between the compiler's inline-assembly markers are
+checked: those from MFMA builtins (the skinny kernels') are spaced out by the
+compiler itself.  CPU only (hipcc cross-compiles); skipped without hipcc."""
 import os
 import re
 import shutil
@@ -33,21 +35,32 @@ def _regs(tok):
 
 
 def _instructions(asm):
-    out = []
+    """Instruction lines, and the indices of those that come from inline
+    assembly (between the compiler's ;;#ASMSTART / ;;#ASMEND markers)."""
+    out, in_asm, inside = [], set(), False
     for line in asm.splitlines():
         s = line.strip()
-        if s and not s.startswith((";", ".", "_")) and not s.endswith(":"):
+        if s.startswith(";;#ASMSTART"):
+            inside = True
+        elif s.startswith(";;#ASMEND"):
+            inside = False
+        elif s and not s.startswith((";", ".", "_")) and not s.endswith(":"):
+            if inside:
+                in_asm.add(len(out))
             out.append(s)
-    return out
+    return out, in_asm
 
 
 ASM_MFMA = ("v_mfma_f32_16x16x32", "v_mfma_i32_16x16x64_i8")
 
 
-def _violations(ins, window=4):
+def _violations(ins, window=4, only=None):
+    """MFMAs (of the forms this library issues from inline assembly; with
+    `only`, just those at these indices) with a VALU write of one of their
+    source registers within `window` wait states before them."""
     bad, n = [], 0
     for i, line in enumerate(ins):
-        if not line.startswith(ASM_MFMA):
+        if not line.startswith(ASM_MFMA) or (only is not None and i not in only):
             continue
         n += 1
         ops = [o.strip() for o in line.split(None, 1)[1].split(",")]
@@ -83,6 +96,11 @@ def test_checker_flags_a_planted_write():
     flip = ["v_bitop3_b32 v53, v57, s51, 0 bitop3:0x3c", "v_mfma_i32_16x16x32_i8 a[0:3], v[18:21], v[50:53], 0",
             "v_mfma_i32_16x16x64_i8 a[4:7], v[18:21], v[50:53], 0"]
     assert len(_violations(flip)[1]) == 1  # the 16x16x64 form at distance 1 (the 16x16x32 int8 form is not ours)
+    # only MFMAs from inline assembly are checked: a builtin's MFMA is the compiler's to space out
+    asm = "\n".join(["v_mov_b32_e32 v5, v9", ins[1], ";;#ASMSTART", ins[1], ";;#ASMEND"])
+    code, in_asm = _instructions(asm)
+    assert in_asm == {2}
+    assert [b[2] for b in _violations(code, only=in_asm)[1]] == [1]
 
 
 @pytest.mark.skipif(HIPCC is None, reason="hipcc not available")
@@ -93,7 +111,8 @@ def test_no_valu_write_of_mfma16_operands():
             asms = list(ex.map(lambda s: _compile(s, os.path.join(d, s + ".s")), srcs))
     total = 0
     for src, asm in zip(srcs, asms):
-        n, bad = _violations(_instructions(asm))
+        ins, in_asm = _instructions(asm)
+        n, bad = _violations(ins, only=in_asm)
         total += n
         assert not bad, "%s: %s" % (src, bad[:3])
         assert n > 1000, src  # the inline-assembly loops were found

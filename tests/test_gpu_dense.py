@@ -322,6 +322,7 @@ def test_gemm_split_k(dt, sa, sb, tA, tB):
 
 SKINNY = [  # M, N, K: M <= 16 rows against B stored (N, K) -> the B-streaming skinny kernels
     (1, 8192, 8192), (5, 8200, 3000), (16, 8192, 1024),                        # single pass (>= 512 x 16 columns)
+    (12, 8200, 3000), (9, 8240, 2056),               # single pass, 32-column workgroups, ragged N and K
     (16, 4096, 4104), (3, 100, 1000), (7, 4100, 2056), (16, 64, 1024), (1, 1, 20000),  # K split over workgroups
 ]
 
@@ -387,6 +388,22 @@ def test_gemm_skinny_exact(M):
     Y = om.gemm(dev(A, "bf16"), dev(B, "bf16"), None, 1.0, 0.0, 0, 1)
     torch.cuda.synchronize()
     y, _ = oracle.gemm(A, B, None, 1.0, 0.0, 0, 1, dt="bf16")
+    assert np.array_equal(host_f64(Y), y)
+
+
+@pytest.mark.parametrize("M", [1, 8, 9, 16])
+def test_gemm_skinny_single_pass_exact(M):
+    """The single-pass kernel on both sides of its 8-row switch (16 or 32
+    columns per workgroup), a ragged last column group and a K tail: small
+    integers, so both sides sum exactly and round once to bf16: bit-exact."""
+    rng = np.random.default_rng(40 + M)
+    K, N = 2056, 8216
+    A = synth.store(rng.integers(-1, 2, (M, K)).astype(np.float32) * (np.arange(K) % 8 == 0), "bf16")
+    B = synth.store(rng.integers(-1, 2, (N, K)).astype(np.float32), "bf16")
+    C = synth.store(rng.integers(-8, 9, (N,)).astype(np.float32), "bf16")
+    Y = om.gemm(dev(A, "bf16"), dev(B, "bf16"), dev(C, "bf16"), 1.0, 2.0, 0, 1)
+    torch.cuda.synchronize()
+    y, _ = oracle.gemm(A, B, C, 1.0, 2.0, 0, 1, dt="bf16")
     assert np.array_equal(host_f64(Y), y)
 
 
