@@ -665,7 +665,12 @@ __global__ __launch_bounds__(256) void skinny_nmaj_kernel(DenseArgs p) {
     const int64_t g0 = groups * wave / 4, g1 = groups * (wave + 1) / 4;
     const int ng = (int)(g1 - g0);
     const __amdgpu_buffer_rsrc_t rsb = sk_rsrc((const uint16_t*)p.B + z0 * p.b_bs0 + z1 * p.b_bs1);
-    const int64_t kb = g0 * RPI + r;  // this lane's first row
+    // this lane's first row; K fits in LDS, so rows are 32-bit
+    const int kb = (int)(g0 * RPI) + r, Ki = (int)K;
+    // step i reads row kb + RPI i: inside the wave's range and below K for
+    // i < il (0 for masked columns); offsets advance by a fixed stride
+    const int il = !nok || kb >= Ki ? 0 : min(ng, (Ki - kb + RPI - 1) / RPI);
+    const uint32_t boff = (uint32_t)(((int64_t)kb * p.ldb + n) * 2), bstep = (uint32_t)(RPI * p.ldb * 2);
 
     float acc[MR][8];
 #pragma unroll
@@ -674,17 +679,13 @@ __global__ __launch_bounds__(256) void skinny_nmaj_kernel(DenseArgs p) {
         for (int e = 0; e < 8; ++e) acc[m][e] = 0.0f;
     auto load = [&](u32x4_t (&rb)[U], int i0) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t k = kb + (int64_t)RPI * (i0 + u);
-            const bool ok = nok && i0 + u < ng && k < K;
-            rb[u] = sk_load(rsb, ok ? (uint32_t)((k * p.ldb + n) * 2) : SK_OOB);
-        }
+        for (int u = 0; u < U; ++u) rb[u] = sk_load(rsb, i0 + u < il ? boff + bstep * (uint32_t)(i0 + u) : SK_OOB);
     };
     auto fma_rows = [&](const u32x4_t (&rb)[U], int i0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             // rows past this wave's range or K hold B = 0: read any valid A row
-            const int64_t k = min(kb + (int64_t)RPI * (i0 + u), K - 1);
+            const int k = min(kb + RPI * (i0 + u), Ki - 1);
             float av[MR];
             if constexpr (MR == 1) {
                 av[0] = from_bits<DT>(At[k]);
@@ -783,7 +784,10 @@ __global__ __launch_bounds__(256) void skinny_nmaj_kernel(DenseArgs p) {
 template <int DT, int MR>
 hipError_t launch_skinny_nmaj(const DenseArgs& a, hipStream_t s) {
     const int64_t NB = a.nb0 * a.nb1;
-    const size_t lds = (size_t)a.K * MR * 2;
+    // at least 60 KB of LDS per workgroup, so that at most two share a CU
+    // (its ~100 VGPRs would let four in; measured at M = 1, N = 28672,
+    // K = 8192: 0.135 ms with four resident, 0.108 with three, 0.105 with two)
+    const size_t lds = std::max<size_t>((size_t)a.K * MR * 2, 61440);
     // 32-column groups (64-byte row pieces) once there is one per CU: at M = 1,
     // N = K = 8192 (256 groups) 30 against 35 us with 16-column groups
     if ((a.N + 31) / 32 * NB >= 256) {
