@@ -525,8 +525,8 @@ __global__ __launch_bounds__(256) void skinny_kernel(DenseArgs p) {
     }
 }
 
-// Single-pass variant for enough columns (one workgroup per 16 or 32 columns
-// fills the chip): a workgroup owns 16 CG columns, each of its NW waves takes
+// Single-pass variant (one launch, no workspace): a workgroup owns 16 CG
+// columns, each of its NW waves (4, or 8 when there are few workgroups) takes
 // one contiguous K range for all of them; A fragments come straight from
 // global memory too (the A rows, at most 16, are small and stay in L2); the
 // NW partial tiles are added in LDS in a fixed order and wave 0 applies
@@ -895,8 +895,14 @@ Plan16 plan16(const DenseArgs& a) {
             return pl;
         }
     }
+    // Single pass (no workspace, one launch) with at least 512 groups of 16
+    // columns, or fewer groups of 8 waves each while K is short enough that
+    // one workgroup streams its columns' K in about the time the split-K path
+    // takes (measured per call: 9.6-11.6 us for 128-256 groups at K <= 8192
+    // and 20.8 us for 256 groups at K = 14336, against 29-30 us split-K)
+    const int64_t g16 = (a.N + 15) / 16;
     if (vec && b_span && a_span && a.M <= 16 && a.a_kmajor && a.b_kmajor && a.K >= 1024 && NB <= 65535 &&
-        (a.N + 15) / 16 * NB >= 512 && (a.N + 15) / 16 <= 0x7fffffff) {
+        g16 <= 0x7fffffff && (g16 * NB >= 512 || a.K <= 8192 || (g16 * NB >= 256 && a.K <= 16384))) {
         pl.kind = Plan16::SKINNY1;
         return pl;
     }
@@ -947,10 +953,15 @@ hipError_t run16(const DenseArgs& a, const Plan16& pl, float* ws, hipStream_t s)
             if (pl.mr == 2) return launch_skinny_nmaj<DT, 2>(a, s);
             return launch_skinny_nmaj<DT, 4>(a, s);
         case Plan16::SKINNY1:
-            // more than 8 rows: 32 columns per workgroup of 4 waves (measured
-            // 10-20% ahead with B in the last-level cache, even with it in HBM);
-            // else 16 columns per workgroup of 4 waves
-            if (a.M > 8 && (a.N + 31) / 32 * NB >= 256)
+            // fewer than 512 groups of 16 columns: 8 waves per workgroup, so a
+            // CU keeps as many loads in flight as two workgroups of 4 would;
+            // else, more than 8 rows: 32 columns per workgroup of 4 waves
+            // (measured 10-20% ahead with B in the last-level cache, even
+            // with it in HBM); else 16 columns per workgroup of 4 waves
+            if ((a.N + 15) / 16 * NB < 512)
+                hipLaunchKernelGGL((skinny1_kernel<DT, 1, 8, true>), dim3((unsigned)((a.N + 15) / 16), (unsigned)NB),
+                                   dim3(512), 0, s, a);
+            else if (a.M > 8 && (a.N + 31) / 32 * NB >= 256)
                 hipLaunchKernelGGL((skinny1_kernel<DT, 2, 4, true>), dim3((unsigned)((a.N + 31) / 32), (unsigned)NB),
                                    dim3(256), 0, s, a);
             else

@@ -323,7 +323,8 @@ def test_gemm_split_k(dt, sa, sb, tA, tB):
 SKINNY = [  # M, N, K: M <= 16 rows against B stored (N, K) -> the B-streaming skinny kernels
     (1, 8192, 8192), (5, 8200, 3000), (16, 8192, 1024),                        # single pass (>= 512 x 16 columns)
     (12, 8200, 3000), (9, 8240, 2056),               # single pass, 32-column workgroups, ragged N and K
-    (16, 4096, 4104), (3, 100, 1000), (7, 4100, 2056), (16, 64, 1024), (1, 1, 20000),  # K split over workgroups
+    (16, 4096, 4104), (7, 4100, 2056), (16, 64, 1024), (2, 4104, 14336),  # single pass, 8 waves per workgroup
+    (3, 100, 1000), (1, 1, 20000), (16, 1000, 9000), (4, 2056, 16392),  # K split over workgroups
 ]
 
 
@@ -378,12 +379,13 @@ def test_gemm_skinny_nmajor_epilogue_exact():
     assert np.array_equal(host_f64(Y), y)
 
 
+@pytest.mark.parametrize("K", [2048, 12288])  # single pass (8 waves) / K split over workgroups
 @pytest.mark.parametrize("M", [1, 5, 16])
-def test_gemm_skinny_exact(M):
+def test_gemm_skinny_exact(M, K):
     """Small integers (entries in {-1, 0, 1}, |partial sums| <= 256): bit-exact."""
     rng = np.random.default_rng(M)
-    K, N = 2048, 320
-    A = synth.store(rng.integers(-1, 2, (M, K)).astype(np.float32) * (np.arange(K) % 8 == 0), "bf16")
+    N = 320
+    A = synth.store(rng.integers(-1, 2, (M, K)).astype(np.float32) * (np.arange(K) % (K // 256) == 0), "bf16")
     B = synth.store(rng.integers(-1, 2, (N, K)).astype(np.float32), "bf16")
     Y = om.gemm(dev(A, "bf16"), dev(B, "bf16"), None, 1.0, 0.0, 0, 1)
     torch.cuda.synchronize()
