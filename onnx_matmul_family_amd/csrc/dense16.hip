@@ -643,13 +643,14 @@ __global__ __launch_bounds__(64 * NW) void skinny1_kernel(DenseArgs p) {
 // 8 columns over its rows (the work per B byte is MR/2 multiply-adds, well
 // under the ALU rate at the HBM rate).  A is held in LDS transposed to (K,
 // MR) so one small LDS read per row gives all MR values.  A workgroup owns CW
-// columns over the whole of K, split in 4 ranges over its waves; the partial
-// sums are reduced across the lanes that share columns (shuffles) and across
-// the waves in LDS in a fixed order; wave 0 applies the epilogue.
-template <int DT, int MR, int CW>
-__global__ __launch_bounds__(256) void skinny_nmaj_kernel(DenseArgs p) {
+// columns over the whole of K, split in NW ranges over its waves (4, or 8
+// when there are few workgroups); the partial sums are reduced across the
+// lanes that share columns (shuffles) and across the waves in LDS in a fixed
+// order; wave 0 applies the epilogue.
+template <int DT, int MR, int CW, int NW>
+__global__ __launch_bounds__(64 * NW) void skinny_nmaj_kernel(DenseArgs p) {
     extern __shared__ __attribute__((aligned(16))) uint16_t At[];  // (K, MR)
-    __shared__ float red[3][CW / 8][MR][8];
+    __shared__ float red[NW - 1][CW / 8][MR][8];
     constexpr int LPR = CW / 8, RPI = 64 / LPR, U = 8;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int64_t z = blockIdx.y, z0 = z / p.nb1, z1 = z - z0 * p.nb1;
@@ -662,7 +663,7 @@ __global__ __launch_bounds__(256) void skinny_nmaj_kernel(DenseArgs p) {
     const int64_t n = (int64_t)cg * CW + 8 * c;
     const bool nok = n < N;  // N % 8 == 0: whole chunks
     const int64_t groups = (K + RPI - 1) / RPI;
-    const int64_t g0 = groups * wave / 4, g1 = groups * (wave + 1) / 4;
+    const int64_t g0 = groups * wave / NW, g1 = groups * (wave + 1) / NW;
     const int ng = (int)(g1 - g0);
     const __amdgpu_buffer_rsrc_t rsb = sk_rsrc((const uint16_t*)p.B + z0 * p.b_bs0 + z1 * p.b_bs1);
     // this lane's first row; K fits in LDS, so rows are 32-bit
@@ -718,16 +719,16 @@ __global__ __launch_bounds__(256) void skinny_nmaj_kernel(DenseArgs p) {
         constexpr int UA = 4;
         const __amdgpu_buffer_rsrc_t rsa = sk_rsrc(A);
         const int64_t kc = K / 8, total = kc * MR;
-        for (int64_t c0 = 0; c0 < total; c0 += 256 * UA) {
+        for (int64_t c0 = 0; c0 < total; c0 += 64 * NW * UA) {
             u32x4_t v[UA];
 #pragma unroll
             for (int u = 0; u < UA; ++u) {
-                const int64_t c = c0 + t + 256 * u, m = c / kc, q = c - m * kc;
+                const int64_t c = c0 + t + 64 * NW * u, m = c / kc, q = c - m * kc;
                 v[u] = sk_load(rsa, c < total && m < M ? (uint32_t)((m * p.lda + 8 * q) * 2) : SK_OOB);
             }
 #pragma unroll
             for (int u = 0; u < UA; ++u) {
-                const int64_t c = c0 + t + 256 * u, m = c / kc, q = c - m * kc;
+                const int64_t c = c0 + t + 64 * NW * u, m = c / kc, q = c - m * kc;
                 if (c < total) {
                     if constexpr (MR == 1) {
                         *(u32x4_t*)(At + 8 * q) = v[u];
@@ -773,7 +774,7 @@ __global__ __launch_bounds__(256) void skinny_nmaj_kernel(DenseArgs p) {
         for (int e = 0; e < 8; ++e) {
             float v = acc[m][e];
 #pragma unroll
-            for (int w = 0; w < 3; ++w) v += red[w][c][m][e];
+            for (int w = 0; w < NW - 1; ++w) v += red[w][c][m][e];
             v *= p.alpha;
             if (Cp) v += p.beta * from_bits<DT>(Cp[m * p.c_sm + (n + e) * p.c_sn]);
             Y[m * p.ldy + n + e] = to_bits<DT>(v);
@@ -789,13 +790,16 @@ hipError_t launch_skinny_nmaj(const DenseArgs& a, hipStream_t s) {
     // K = 8192: 0.135 ms with four resident, 0.108 with three, 0.105 with two)
     const size_t lds = std::max<size_t>((size_t)a.K * MR * 2, 61440);
     // 32-column groups (64-byte row pieces) once there is one per CU: at M = 1,
-    // N = K = 8192 (256 groups) 30 against 35 us with 16-column groups
+    // N = K = 8192 (256 groups) 30 against 35 us with 16-column groups; fewer
+    // than 256 groups of 16 columns: 8 waves per workgroup
+    const int64_t g16 = (a.N + 15) / 16;
     if ((a.N + 31) / 32 * NB >= 256) {
-        hipLaunchKernelGGL((skinny_nmaj_kernel<DT, MR, 32>), dim3((unsigned)((a.N + 31) / 32), (unsigned)NB), dim3(256),
-                           lds, s, a);
+        hipLaunchKernelGGL((skinny_nmaj_kernel<DT, MR, 32, 4>), dim3((unsigned)((a.N + 31) / 32), (unsigned)NB),
+                           dim3(256), lds, s, a);
+    } else if (g16 * NB >= 256) {
+        hipLaunchKernelGGL((skinny_nmaj_kernel<DT, MR, 16, 4>), dim3((unsigned)g16, (unsigned)NB), dim3(256), lds, s, a);
     } else {
-        hipLaunchKernelGGL((skinny_nmaj_kernel<DT, MR, 16>), dim3((unsigned)((a.N + 15) / 16), (unsigned)NB), dim3(256),
-                           lds, s, a);
+        hipLaunchKernelGGL((skinny_nmaj_kernel<DT, MR, 16, 8>), dim3((unsigned)g16, (unsigned)NB), dim3(512), lds, s, a);
     }
     return hipGetLastError();
 }
@@ -878,16 +882,19 @@ Plan16 plan16(const DenseArgs& a) {
     }
     const int64_t NB = a.nb0 * a.nb1;
     // Skinny (M <= 16) with both operands k-contiguous: stream B, split K.
-    // Skinny (M <= 4) against n-contiguous B, enough columns to fill the chip
-    // with 16-column workgroups, A (K x MR x 2 bytes) within 60 KB of LDS.
+    // Skinny (M <= 4) against n-contiguous B, A (K x MR x 2 bytes) within 60 KB
+    // of LDS, with enough columns to fill the chip with 16-column workgroups
+    // or K short enough for fewer workgroups of 8 waves.
     // (buffer offsets are 32-bit: one batch entry of B below 2 GiB)
     const bool b_span = (a.b_kmajor ? a.N * a.ldb : a.K * a.ldb) * 2 < (1LL << 31);
     const bool a_span = a.M * a.lda * 2 < (1LL << 31);
     // (measured: ahead of the split-K path for M <= 2 at any K and for M <= 4
-    // up to K = 4096; behind it for 3-4 rows and longer K)
+    // up to K = 4096; behind it for 3-4 rows and longer K; with fewer than
+    // 256 groups and K <= 8192, M = 1-4, N = 512-2048: 9.1-16.1 us per call
+    // against 22-23 us split-K)
     if (vec && b_span && a_span && (a.M <= 2 || (a.M <= 4 && a.K <= 4096)) && a.a_kmajor && !a.b_kmajor &&
         a.K >= 1024 && NB <= 65535 &&
-        (a.N + 15) / 16 * NB >= 256 && (a.N + 15) / 16 <= 0x7fffffff) {
+        ((a.N + 15) / 16 * NB >= 256 || a.K <= 8192) && (a.N + 15) / 16 <= 0x7fffffff) {
         const int mr = a.M <= 1 ? 1 : a.M <= 2 ? 2 : 4;
         if (a.K * mr * 2 <= 61440) {
             pl.kind = Plan16::SKINNY_NMAJ;

@@ -346,10 +346,13 @@ def test_gemm_skinny_stream(dt, M, N, K):
 
 
 SKINNY_NMAJ = [  # MatMul with a few rows against B stored (K, N): the vector-ALU streaming kernel
-    # (16- or 32-column workgroups over all of K, or 64-column ones with K split over workgroups + reduction)
+    # 16- or 32-column workgroups of 4 waves over all of K
     ((1, 8192), (8192, 8192)), ((8192,), (8192, 4096)), ((3, 2048), (2048, 4104)), ((2, 1024), (1024, 8200)),
-    ((2, 1, 1024), (2, 1024, 2048)), ((4, 4096), (4096, 4096)), ((4, 7680), (7680, 4096)),
-    ((2, 1, 4096), (2, 4096, 2048)),  # batched, K split over workgroups
+    ((2, 1, 1024), (2, 1024, 2048)), ((4, 4096), (4096, 4096)), ((2, 1, 4096), (2, 4096, 2048)),
+    # fewer column groups: 16-column workgroups of 8 waves (ragged last group, a batch)
+    ((1, 4096), (4096, 2048)), ((2, 8192), (8192, 1032)), ((4, 4096), (4096, 520)), ((2, 1, 8192), (2, 8192, 1000)),
+    # 3-4 rows, K > 4096, and few columns with long K: K split over workgroups + reduction
+    ((4, 7680), (7680, 4096)), ((1, 12288), (12288, 1024)),
 ]
 
 
@@ -366,10 +369,11 @@ def test_matmul_skinny_nmajor(dt, sa, sb):
     check_close(host_f64(Y), y, t, dt, "skinny n-major %s %s x %s" % (dt, sa, sb))
 
 
-def test_gemm_skinny_nmajor_epilogue_exact():
+@pytest.mark.parametrize("N", [4096, 1032])  # 4 waves per workgroup / 8 (few column groups)
+def test_gemm_skinny_nmajor_epilogue_exact(N):
     """Gemm transB=0 with 2 rows, C per row and column, small integers: bit-exact."""
     rng = np.random.default_rng(12)
-    M, K, N = 2, 4096, 4096
+    M, K = 2, 4096
     A = synth.store(rng.integers(-1, 2, (M, K)).astype(np.float32) * (np.arange(K) % 16 == 0), "bf16")
     B = synth.store(rng.integers(-1, 2, (K, N)).astype(np.float32), "bf16")
     C = synth.store(rng.integers(-8, 9, (M, N)).astype(np.float32), "bf16")
