@@ -904,12 +904,12 @@ Plan16 plan16(const DenseArgs& a) {
     }
     // Single pass (no workspace, one launch) with at least 512 groups of 16
     // columns, or fewer groups of 8 waves each while K is short enough that
-    // one workgroup streams its columns' K in about the time the split-K path
-    // takes (measured per call: 9.6-11.6 us for 128-256 groups at K <= 8192
-    // and 20.8 us for 256 groups at K = 14336, against 29-30 us split-K)
+    // one workgroup streams its columns' K in less time than the split-K path
+    // takes (measured per call: 10-13 us at K <= 8192 and 15-21 us at
+    // K = 9000-16384, against 26-30 us split-K; 33 against 26 us at K = 28672)
     const int64_t g16 = (a.N + 15) / 16;
     if (vec && b_span && a_span && a.M <= 16 && a.a_kmajor && a.b_kmajor && a.K >= 1024 && NB <= 65535 &&
-        g16 <= 0x7fffffff && (g16 * NB >= 512 || a.K <= 8192 || (g16 * NB >= 256 && a.K <= 16384))) {
+        g16 <= 0x7fffffff && (g16 * NB >= 512 || a.K <= 16384)) {
         pl.kind = Plan16::SKINNY1;
         return pl;
     }

@@ -323,8 +323,8 @@ def test_gemm_split_k(dt, sa, sb, tA, tB):
 SKINNY = [  # M, N, K: M <= 16 rows against B stored (N, K) -> the B-streaming skinny kernels
     (1, 8192, 8192), (5, 8200, 3000), (16, 8192, 1024),                        # single pass (>= 512 x 16 columns)
     (12, 8200, 3000), (9, 8240, 2056),               # single pass, 32-column workgroups, ragged N and K
-    (16, 4096, 4104), (7, 4100, 2056), (16, 64, 1024), (2, 4104, 14336),  # single pass, 8 waves per workgroup
-    (3, 100, 1000), (1, 1, 20000), (16, 1000, 9000), (4, 2056, 16392),  # K split over workgroups
+    (16, 4096, 4104), (7, 4100, 2056), (16, 64, 1024), (2, 4104, 14336), (16, 1000, 9000),  # single pass, 8 waves
+    (3, 100, 1000), (1, 1, 20000), (16, 1000, 20000), (4, 2056, 16392),  # K split over workgroups
 ]
 
 
@@ -383,7 +383,7 @@ def test_gemm_skinny_nmajor_epilogue_exact(N):
     assert np.array_equal(host_f64(Y), y)
 
 
-@pytest.mark.parametrize("K", [2048, 12288])  # single pass (8 waves) / K split over workgroups
+@pytest.mark.parametrize("K", [2048, 20480])  # single pass (8 waves) / K split over workgroups
 @pytest.mark.parametrize("M", [1, 5, 16])
 def test_gemm_skinny_exact(M, K):
     """Small integers (entries in {-1, 0, 1}, |partial sums| <= 256): bit-exact."""

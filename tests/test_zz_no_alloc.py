@@ -53,8 +53,8 @@ def test_noalloc_matches_gemm_twice(dt):
     y, t = oracle.gemm(A, B, C, 0.5, -1.5, 0, 0, dt=dt)
     check_close(host_f64(Y1), y, 0.5 * t + 1.5 * np.abs(oracle.decode(C, dt))[None, :], dt, "noalloc split-K")
     # 2: smaller, decode-like (16 rows, B stored (N, K), few columns and K past
-    # the single-pass kernel's range) -> the skinny split-K kernel (24 x 16 x 1000 fp32)
-    A, B, C = case(rng, dt, 16, 1000, 12288, 1, (16, 1000))
+    # the single-pass kernel's range) -> the skinny split-K kernel (32 x 16 x 1000 fp32)
+    A, B, C = case(rng, dt, 16, 1000, 20480, 1, (16, 1000))
     Y0, Y1 = run_both(A, B, C, dt, 1.0, 1.0, 1)
     assert torch.equal(Y0.view(torch.int16), Y1.view(torch.int16))
     y, t = oracle.gemm(A, B, C, 1.0, 1.0, 0, 1, dt=dt)
