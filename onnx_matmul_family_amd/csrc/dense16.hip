@@ -526,19 +526,16 @@ __global__ __launch_bounds__(256) void skinny_kernel(DenseArgs p) {
 }
 
 // Single-pass variant (one launch, no workspace): a workgroup owns 16 CG
-// columns, each of its NW waves (4, or 8 when there are few workgroups) takes
-// one contiguous K range for all of them; A fragments come straight from
-// global memory too (the A rows, at most 16, are small and stay in L2); the
-// NW partial tiles are added in LDS in a fixed order and wave 0 applies
-// alpha * acc + beta * C and stores Y.  No workspace and no second kernel.
+// columns, each of its NW waves (4 or 8) takes one contiguous K range for all
+// of them; A fragments come straight from global memory too (the A rows, at
+// most 16, are small and stay in L2); the NW partial tiles are added in LDS
+// in a fixed order and wave 0 applies alpha * acc + beta * C and stores Y.
 // CG = 2 lets each A fragment feed two MFMAs, so the workgroup reads A once
 // per 32 columns: the choice once A has more than 8 rows, where A's reads
 // are as many as B's.  SB keeps each batch of loads issued ahead of the
 // MFMAs on the other batch (scheduling barriers), which the CG = 2 form
-// needs to keep both batches in flight.
-constexpr int SK1_U = 8;  // k-steps per batch of loads
-
-template <int DT, int CG, int NW, bool SB>
+// needs to keep both batches in flight.  SK1_U: k-steps per batch of loads.
+template <int DT, int CG, int NW, bool SB, int SK1_U>
 __global__ __launch_bounds__(64 * NW) void skinny1_kernel(DenseArgs p) {
     __shared__ float red[NW - 1][CG][64][4];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -964,16 +961,19 @@ hipError_t run16(const DenseArgs& a, const Plan16& pl, float* ws, hipStream_t s)
             // CU keeps as many loads in flight as two workgroups of 4 would;
             // else, more than 8 rows: 32 columns per workgroup of 4 waves
             // (measured 10-20% ahead with B in the last-level cache, even
-            // with it in HBM); else 16 columns per workgroup of 4 waves
+            // with it in HBM); else 16 columns per workgroup of 8 waves with
+            // batches of 4 k-steps (69 VGPRs, three workgroups per CU; with B
+            // from HBM 6-9% ahead of 4 waves with batches of 8 at N = K = 8192
+            // and N = 28672)
             if ((a.N + 15) / 16 * NB < 512)
-                hipLaunchKernelGGL((skinny1_kernel<DT, 1, 8, true>), dim3((unsigned)((a.N + 15) / 16), (unsigned)NB),
+                hipLaunchKernelGGL((skinny1_kernel<DT, 1, 8, true, 8>), dim3((unsigned)((a.N + 15) / 16), (unsigned)NB),
                                    dim3(512), 0, s, a);
             else if (a.M > 8 && (a.N + 31) / 32 * NB >= 256)
-                hipLaunchKernelGGL((skinny1_kernel<DT, 2, 4, true>), dim3((unsigned)((a.N + 31) / 32), (unsigned)NB),
+                hipLaunchKernelGGL((skinny1_kernel<DT, 2, 4, true, 8>), dim3((unsigned)((a.N + 31) / 32), (unsigned)NB),
                                    dim3(256), 0, s, a);
             else
-                hipLaunchKernelGGL((skinny1_kernel<DT, 1, 4, false>), dim3((unsigned)((a.N + 15) / 16), (unsigned)NB),
-                                   dim3(256), 0, s, a);
+                hipLaunchKernelGGL((skinny1_kernel<DT, 1, 8, false, 4>), dim3((unsigned)((a.N + 15) / 16), (unsigned)NB),
+                                   dim3(512), 0, s, a);
             return hipGetLastError();
         case Plan16::SKINNY_SPLIT:
         case Plan16::SPLIT128: {
