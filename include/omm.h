@@ -33,15 +33,21 @@
  *    row lengths that are multiples of 16 bytes take the vectorised path; other
  *    layouts are still computed correctly by an element-wise path.
  *  - Concurrent calls on different streams may run in parallel; they share
- *    nothing but the caller's buffers (omm_gemm_noalloc excepted: see there).
+ *    nothing but the caller's buffers (omm_gemm_noalloc and the split-K
+ *    workspace below excepted).
  *  - Scratch: omm_matmul and omm_gemm with bf16 / fp16 operands split K over
  *    several workgroups for shapes with few output tiles and a long K
  *    (decode-like rows, narrow outputs).  The fp32 partial products of such a
- *    call (splits x batches x M x N x 4 bytes) live in stream-ordered device
- *    memory the library takes with hipMallocAsync and returns with
- *    hipFreeAsync on the caller's stream, around the call's kernels; if the
- *    stream's memory pool cannot supply it the call returns OMM_ERR_HIP with
- *    nothing launched.  No other entry point allocates device memory.
+ *    call (splits x batches x M x N x 4 bytes) live in a workspace the
+ *    library keeps per GPU until the process ends: taken with hipMallocAsync
+ *    on the calling stream and, when a call needs more, freed with
+ *    hipFreeAsync and taken again larger on that stream.  An event recorded
+ *    after each such call makes the next one (on any stream) wait for it, so
+ *    split-K calls on one GPU run one after another.  Under HIP graph capture
+ *    the partials instead live in stream-ordered memory taken and returned
+ *    around the call's kernels.  If the memory pool cannot supply the
+ *    workspace the call returns OMM_ERR_HIP with nothing launched.  No other
+ *    entry point allocates device memory.
  */
 #ifndef OMM_H_
 #define OMM_H_

@@ -15,6 +15,7 @@
 // The K loops are the shared MFMA core (gemm16_core.hpp); this file adds the
 // batch / tile mapping and the alpha-beta-C epilogues.
 #include <algorithm>
+#include <mutex>
 
 #include "gemm16_core.hpp"
 #include "kernels.hpp"
@@ -1018,6 +1019,46 @@ const char* plan_name(const Plan16& pl) {
     return "?";
 }
 
+// Split-K partials outside graph capture: one workspace per GPU, kept for
+// the life of the process and grown on demand (stream-ordered: the old buffer
+// is freed and the new one taken on the calling stream), and an event that
+// orders every call using it after the previous one, whatever its stream.
+// This replaces a hipMallocAsync / hipFreeAsync pair per call, whose host
+// cost (~15 us in hipFreeAsync) exceeded the kernels' time on small shapes.
+// Under graph capture the partials stay in per-call stream-ordered memory.
+struct SplitWorkspace {
+    std::mutex mu;
+    float* ptr = nullptr;
+    size_t bytes = 0;
+    hipEvent_t last = nullptr;
+};
+constexpr int WS_DEVICES = 64;
+SplitWorkspace split_ws[WS_DEVICES];
+
+template <int DT>
+hipError_t run_split_cached(const DenseArgs& a, const Plan16& pl, hipStream_t s, SplitWorkspace& w) {
+    std::lock_guard<std::mutex> lock(w.mu);
+    hipError_t e;
+    if (!w.last && (e = hipEventCreateWithFlags(&w.last, hipEventDisableTiming)) != hipSuccess) {
+        w.last = nullptr;
+        return e;
+    }
+    if ((e = hipStreamWaitEvent(s, w.last, 0)) != hipSuccess) return e;
+    if (pl.ws_bytes > w.bytes) {
+        if (w.ptr && (e = hipFreeAsync(w.ptr, s)) != hipSuccess) return e;
+        w.ptr = nullptr;
+        w.bytes = 0;
+        if ((e = hipMallocAsync((void**)&w.ptr, pl.ws_bytes, s)) != hipSuccess) {
+            w.ptr = nullptr;
+            return e;
+        }
+        w.bytes = pl.ws_bytes;
+    }
+    e = run16<DT>(a, pl, w.ptr, s);
+    const hipError_t f = hipEventRecord(w.last, s);
+    return e != hipSuccess ? e : f;
+}
+
 template <int DT>
 hipError_t launch_dt(const DenseArgs& a, hipStream_t s, const DenseScratch* scratch) {
     const Plan16 pl = plan16(a);
@@ -1032,9 +1073,15 @@ hipError_t launch_dt(const DenseArgs& a, hipStream_t s, const DenseScratch* scra
         if (!scratch->ptr || pl.ws_bytes > scratch->bytes) return hipErrorInvalidValue;
         return run16<DT>(a, pl, (float*)scratch->ptr, s);
     }
-    float* ws = nullptr;
-    hipError_t e = hipMallocAsync((void**)&ws, pl.ws_bytes, s);
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(s, &cs);
     if (e != hipSuccess) return e;
+    int dev = -1;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if (cs == hipStreamCaptureStatusNone && dev >= 0 && dev < WS_DEVICES)
+        return run_split_cached<DT>(a, pl, s, split_ws[dev]);
+    float* ws = nullptr;
+    if ((e = hipMallocAsync((void**)&ws, pl.ws_bytes, s)) != hipSuccess) return e;
     e = run16<DT>(a, pl, ws, s);
     const hipError_t f = hipFreeAsync(ws, s);
     return e != hipSuccess ? e : f;

@@ -84,9 +84,10 @@ bool log_enabled();
 void log_choice(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
 int tile_override();  // 0 (none), 256 or 128
 
-// dt: 0 = bf16, 1 = fp16.  scratch == nullptr: split-K partials go to
-// stream-ordered memory (hipMallocAsync / hipFreeAsync on s); otherwise to
-// scratch, which must hold dense16_scratch_bytes(a).
+// dt: 0 = bf16, 1 = fp16.  scratch == nullptr: split-K partials go to the
+// library's per-GPU workspace (grown stream-ordered on s, calls ordered by an
+// event), or under graph capture to stream-ordered memory taken and returned
+// on s; otherwise to scratch, which must hold dense16_scratch_bytes(a).
 hipError_t launch_dense16(const DenseArgs& a, int dt, hipStream_t s, const DenseScratch* scratch = nullptr);
 // bytes of split-K partials launch_dense16 needs for a (0: no split)
 size_t dense16_scratch_bytes(const DenseArgs& a);

@@ -413,6 +413,35 @@ def test_gemm_skinny_single_pass_exact(M):
     assert np.array_equal(host_f64(Y), y)
 
 
+def test_split_k_workspace_two_streams_exact():
+    """Split-K calls (tile path, skinny path, n-contiguous B) issued on two
+    streams without waits between them, the workspace growing on the way:
+    every output bit-exact (small integers, exact fp32 sums) against the
+    oracle.  The library orders calls that share its split-K workspace."""
+    rng = np.random.default_rng(951)
+    cases = [  # (M, N, K, transB): workspace sizes grow and shrink along the list
+        (8, 4096, 4096, 0), (24, 4096, 4096, 1), (16, 1000, 20480, 1), (4, 2056, 16392, 1), (32, 2048, 8192, 0),
+        (8, 4096, 4096, 0), (16, 1000, 20480, 1),
+    ]
+    data, outs = [], []
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for i, (M, N, K, tB) in enumerate(cases):
+        step = max(1, K // 256)
+        A = synth.store(rng.integers(-1, 2, (M, K)).astype(np.float32) * (np.arange(K) % step == 0), "bf16")
+        B = synth.store(rng.integers(-1, 2, (N, K) if tB else (K, N)).astype(np.float32), "bf16")
+        data.append((A, B, tB))
+        dA, dB = dev(A, "bf16"), dev(B, "bf16")
+        torch.cuda.synchronize()
+        with torch.cuda.stream(streams[i % 2]):
+            Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+            om.gemm(dA, dB, None, 1.0, 0.0, 0, tB, Y)
+        outs.append((Y, dA, dB))
+    torch.cuda.synchronize()
+    for (A, B, tB), (Y, _, _) in zip(data, outs):
+        y, _ = oracle.gemm(A, B, None, 1.0, 0.0, 0, tB, dt="bf16")
+        assert np.array_equal(host_f64(Y), y), (A.shape, B.shape, tB)
+
+
 def test_matmul_split_k_decode_batch_exact():
     """A batch of single-token rows against one weight matrix (batch folds into
     M = 8): split-K, small integers, fp16 output exact."""
