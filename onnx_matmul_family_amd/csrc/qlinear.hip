@@ -1,7 +1,8 @@
 // QLinearMatMul (version 10) on gfx950: int8 MFMA with an exact int32
 // accumulator and the fused requantisation -- v_mfma_i32_16x16x64_i8 on whole
 // 256x256 tiles (qlinear16_kernel), v_mfma_i32_32x32x32_i8 on ragged or
-// unaligned shapes (qlinear_kernel).
+// unaligned shapes (qlinear_kernel); at most 4 rows of a stream b on the
+// vector ALU instead (qlinear_skinny_kernel).
 //
 // Per output element the operator asks for
 //   acc = sum_k (a - za)(b - zb)                      (int32, wraps mod 2^32)
@@ -1079,6 +1080,194 @@ hipError_t launch_q_types(const QArgs& a, hipStream_t s) {
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Decode-like QLinearMatMul: at most 4 rows of a against b stored (K, N), one
+// batch.  The whole cost is one read of b, so b is streamed once on the vector
+// ALU instead of in 256x256 MFMA tiles (of which such a shape has a handful):
+// a workgroup owns 16 columns; each lane of its NW waves reads the 16 bytes
+// of one b row per step (64 rows per wave instruction, the waves on disjoint
+// K ranges) and keeps, per column, the int32 sums of a[m,k] * b[k,n] over its
+// rows (24-bit multiply-adds, exact) and of b[k,n] itself.  a is staged in LDS
+// transposed to (K, MR) bytes and its row sums taken on the way.  Lanes and waves
+// are then summed (integer, so the order does not matter) and the outputs
+// requantised exactly as in q_epilogue, bytes taken as they are (uint8 as
+// 0..255 with their own zero points: (a - za)(b - zb) is unchanged).
+constexpr int QSK_NW = 8;
+// steps of 64 rows per wave: K <= 8192 gives at most 16, all loaded at once
+constexpr int QSK_STEPS = 16;
+
+__device__ __forceinline__ u32x4_t qsk_load(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+}
+
+template <bool U8>
+__device__ __forceinline__ int qsk_byte(uint32_t w, int e) {
+    return U8 ? (int)((w >> (8 * e)) & 0xffu) : (int)(int8_t)(w >> (8 * e));
+}
+
+// Each phase waits for memory once: the lane's b rows (all its steps), its
+// share of a, and, for the lanes that write an output, that output's
+// parameters are all requested before the first wait.
+template <int MR, bool AU8, bool BU8>
+__global__ __launch_bounds__(64 * QSK_NW) void qlinear_skinny_kernel(QArgs p) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t At[];  // (K, MR) bytes
+    __shared__ int red[QSK_NW][MR + 1][16];
+    __shared__ int rowsum[MR];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const uint8_t* __restrict__ A = (const uint8_t*)p.a;
+    // neighbouring column groups share b's 128-byte lines: keep them on one XCD
+    const int64_t n0 = (int64_t)xcd_remap((int)blockIdx.x, (int)gridDim.x) * 16;
+
+    // b: this wave's rows in steps of 64 (groups split as evenly as whole
+    // groups allow); step i of the lane reads row kb + 64 i, below K for i < il
+    const int64_t groups = (K + 63) / 64;
+    const int g0 = (int)(groups * wave / QSK_NW), g1 = (int)(groups * (wave + 1) / QSK_NW);
+    const int ns = g1 - g0;  // <= QSK_STEPS
+    const int kb = 64 * g0 + lane, Ki = (int)K;
+    const int il = kb >= Ki ? 0 : min(ns, (Ki - kb + 63) / 64);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.b), (short)0, 0x7fffffff,
+                                                                        0x00020000);
+    const uint32_t boff = (uint32_t)((int64_t)kb * p.ldb + n0), bstep = (uint32_t)(64 * p.ldb);
+    u32x4_t v[QSK_STEPS];
+#pragma unroll
+    for (int i = 0; i < QSK_STEPS; ++i) v[i] = qsk_load(rb, i < il ? boff + bstep * (uint32_t)i : 0x80000000u);
+
+    // a: 16-byte pieces (at most 4 per thread for K <= 8192); rows >= M are 0
+    constexpr int QA = 4;
+    const int kc = Ki / 16;
+    u32x4_t va[QA];
+#pragma unroll
+    for (int u = 0; u < QA; ++u) {
+        const int c = t + 64 * QSK_NW * u, m = c / kc, q = c - m * kc;
+        va[u] = c < kc * MR && m < M ? *(const u32x4_t*)(A + m * p.lda + 16 * q) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+
+    // the output parameters of lane (m, e) of wave 0
+    const int om = lane >> 4, oe = lane & 15;
+    const bool writer = wave == 0 && lane < 16 * MR && om < M && n0 + oe < N;
+    int za = 0, zb = 0, zy = 0;
+    float sa = 0.0f, sb = 0.0f, sy = 1.0f;
+    if (writer) {
+        auto ldscale = [&](const void* q, int64_t i) {
+            return p.scale_f16 ? from_bits<1>(((const uint16_t*)q)[i]) : ((const float*)q)[i];
+        };
+        za = AU8 ? (int)((const uint8_t*)p.a_zp)[om * p.ap_sm] : (int)((const int8_t*)p.a_zp)[om * p.ap_sm];
+        zb = BU8 ? (int)((const uint8_t*)p.b_zp)[(n0 + oe) * p.bp_sn]
+                 : (int)((const int8_t*)p.b_zp)[(n0 + oe) * p.bp_sn];
+        sa = ldscale(p.a_scale, om * p.ap_sm);
+        sb = ldscale(p.b_scale, (n0 + oe) * p.bp_sn);
+        sy = ldscale(p.y_scale, 0);
+        zy = p.y_u8 ? (int)((const uint8_t*)p.y_zp)[0] : (int)((const int8_t*)p.y_zp)[0];
+    }
+
+    // a -> LDS transposed (K, MR), row sums from the same bytes
+    if (t < MR) rowsum[t] = 0;
+    __syncthreads();
+    {
+        int part[MR];
+#pragma unroll
+        for (int m = 0; m < MR; ++m) part[m] = 0;
+#pragma unroll
+        for (int u = 0; u < QA; ++u) {
+            const int c = t + 64 * QSK_NW * u, m = c / kc, q = c - m * kc;
+            if (c < kc * MR) {
+                const uint32_t w[4] = {va[u].x, va[u].y, va[u].z, va[u].w};
+                int sum = 0;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    At[(16 * q + e) * MR + m] = (uint8_t)(w[e >> 2] >> (8 * (e & 3)));
+                    sum += qsk_byte<AU8>(w[e >> 2], e & 3);
+                }
+#pragma unroll
+                for (int mm = 0; mm < MR; ++mm)
+                    if (mm == m) part[mm] += sum;
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) part[m] += __shfl_xor(part[m], off);
+            if (lane == 0) atomicAdd(&rowsum[m], part[m]);
+        }
+    }
+    __syncthreads();
+
+    // per column: sum over the lane's rows of a[m,k] b[k,n] (24-bit products,
+    // exact) and of b[k,n]; rows past the range read as zero bytes
+    int acc[MR][16], cs[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        cs[e] = 0;
+#pragma unroll
+        for (int m = 0; m < MR; ++m) acc[m][e] = 0;
+    }
+#pragma unroll
+    for (int i = 0; i < QSK_STEPS; ++i) {
+        if (i < ns) {
+            const int k = min(kb + 64 * i, Ki - 1);
+            int av[MR];
+#pragma unroll
+            for (int m = 0; m < MR; ++m) av[m] = qsk_byte<AU8>(At[k * MR + m], 0);
+            const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int bv = qsk_byte<BU8>(w[e >> 2], e & 3);
+                cs[e] += bv;
+#pragma unroll
+                for (int m = 0; m < MR; ++m) acc[m][e] = __mul24(av[m], bv) + acc[m][e];
+            }
+        }
+    }
+    // sum over the wave's lanes, then over the waves (integers: any order)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            cs[e] += __shfl_xor(cs[e], off);
+#pragma unroll
+            for (int m = 0; m < MR; ++m) acc[m][e] += __shfl_xor(acc[m][e], off);
+        }
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            red[wave][MR][e] = cs[e];
+#pragma unroll
+            for (int m = 0; m < MR; ++m) red[wave][m][e] = acc[m][e];
+        }
+    }
+    __syncthreads();
+    if (!writer) return;
+    int sab = 0, cb = 0;
+#pragma unroll
+    for (int w = 0; w < QSK_NW; ++w) {
+        sab += red[w][om][oe];
+        cb += red[w][MR][oe];
+    }
+    // requantised as in q_epilogue, with the bytes and zero points as stored:
+    // sum (a - za)(b - zb) = sab - zb * (rowsum - K za) - za * cb   (mod 2^32)
+    const uint32_t U = (uint32_t)rowsum[om] - (uint32_t)K * (uint32_t)za;
+    const int32_t s32 = (int32_t)((uint32_t)sab - (uint32_t)zb * U - (uint32_t)za * (uint32_t)cb);
+    const float prod = sa * sb;
+    const float mult = prod / sy;
+    const float x = (float)s32 * mult;
+    const float lo = p.y_u8 ? 0.0f : -128.0f, hi = p.y_u8 ? 255.0f : 127.0f;
+    const float r = __builtin_amdgcn_fmed3f(__builtin_rintf(x) + (float)zy, lo, hi);
+    ((uint8_t*)p.y)[om * p.ldy + n0 + oe] = (uint8_t)(int)r;
+}
+
+template <int MR>
+hipError_t launch_qlinear_skinny(const QArgs& a, hipStream_t s) {
+    const dim3 grid((unsigned)(a.N / 16)), block(64 * QSK_NW);
+    const size_t lds = (size_t)a.K * MR;
+    if (a.a_u8 && a.b_u8) hipLaunchKernelGGL((qlinear_skinny_kernel<MR, true, true>), grid, block, lds, s, a);
+    else if (a.a_u8) hipLaunchKernelGGL((qlinear_skinny_kernel<MR, true, false>), grid, block, lds, s, a);
+    else if (a.b_u8) hipLaunchKernelGGL((qlinear_skinny_kernel<MR, false, true>), grid, block, lds, s, a);
+    else hipLaunchKernelGGL((qlinear_skinny_kernel<MR, false, false>), grid, block, lds, s, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_qlinear(const QArgs& a, hipStream_t s) {
     auto al16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
     const bool vec = al16(a.a) && al16(a.b) && ((uintptr_t)a.y & 3) == 0 && a.lda % 16 == 0 && a.ldb % 16 == 0 &&
@@ -1090,11 +1279,24 @@ hipError_t launch_qlinear(const QArgs& a, hipStream_t s) {
                      (a.K % (2 * KB) == 0 || (!a.a_u8 && !a.b_u8));
     const bool full = vec && a.M % BMQ == 0 && a.N % BNQ == 0 && a.K % KB == 0 && a.K > 0 && a.K <= 32768 &&
                       a.ldy % 16 == 0 && ((uintptr_t)a.y & 15) == 0 && a.y_bs0 % 16 == 0 && a.y_bs1 % 16 == 0;
-    log_choice("qlinear %s x %s -> %s M=%lld N=%lld K=%lld batches=%lld: 256x256x128 tiles, %s",
-               a.a_u8 ? "u8" : "i8", a.b_u8 ? "u8" : "i8", a.y_u8 ? "u8" : "i8", (long long)a.M, (long long)a.N,
-               (long long)a.K, (long long)(a.nb0 * a.nb1),
-               !vec ? "32x32x32 MFMA, register-staged loads"
-               : full ? "16x16x64 MFMA, DMA, whole tiles" : "32x32x32 MFMA, DMA, ragged tiles");
+    // decode-like: at most 4 rows, one batch, a (K x 4 bytes) within 32 KB of
+    // LDS; a and b read as 16-byte pieces (b in whole 16-column groups, with
+    // 32-bit offsets)
+    const bool skinny = al16(a.a) && al16(a.b) && a.lda % 16 == 0 && a.ldb % 16 == 0 && a.K % 16 == 0 &&
+                        a.N % 16 == 0 && a.M <= 4 && a.nb0 * a.nb1 == 1 && a.K >= 256 && a.K <= 8192 &&
+                        a.K * a.ldb < (1LL << 31) && a.N / 16 <= 0x7fffffff;
+    log_choice("qlinear %s x %s -> %s M=%lld N=%lld K=%lld batches=%lld: %s", a.a_u8 ? "u8" : "i8",
+               a.b_u8 ? "u8" : "i8", a.y_u8 ? "u8" : "i8", (long long)a.M, (long long)a.N, (long long)a.K,
+               (long long)(a.nb0 * a.nb1),
+               skinny ? "b streamed on the vector ALU, 16 columns per workgroup"
+               : !vec ? "256x256x128 tiles, 32x32x32 MFMA, register-staged loads"
+               : full ? "256x256x128 tiles, 16x16x64 MFMA, DMA, whole tiles"
+                      : "256x256x128 tiles, 32x32x32 MFMA, DMA, ragged tiles");
+    if (skinny) {
+        if (a.M == 1) return launch_qlinear_skinny<1>(a, s);
+        if (a.M == 2) return launch_qlinear_skinny<2>(a, s);
+        return launch_qlinear_skinny<4>(a, s);
+    }
     if (!vec) return launch_q_types<0>(a, s);
     if (full) {
         // (vec holds K % 256 == 0 when an operand is uint8)

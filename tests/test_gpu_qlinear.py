@@ -291,3 +291,40 @@ def test_uint8_whole_tiles_exact_ties(ta, tb):
     assert np.array_equal(got, ref), np.argwhere(got != ref)[:5]
     want = np.array([int(np.rint((1 if m < 128 else -1) * (m % 8 + 0.5))) + 3 for m in range(M)])
     assert np.array_equal(got[:, 0].astype(int), want)
+
+
+DECODE = [  # (M, K, N): at most 4 rows, one batch -> b streamed on the vector ALU
+    (1, 4096, 4096), (2, 256, 16), (3, 4112, 1024), (4, 8192, 4096), (1, 8192, 11008), (4, 1040, 528),
+]
+
+
+@pytest.mark.parametrize("ta,tb,ty", [(np.int8, np.int8, np.int8), (np.uint8, np.uint8, np.uint8),
+                                      (np.uint8, np.int8, np.int8), (np.int8, np.uint8, np.uint8)])
+@pytest.mark.parametrize("M,K,N", DECODE)
+def test_decode_rows(ta, tb, ty, M, K, N):
+    """Decode-like shapes (1-4 rows, one batch): every output bit-exact, with
+    per-row / per-column parameters, a K tail inside the last 64-row group and
+    a single 16-column group."""
+    rng = np.random.default_rng(M * 7 + K + N + (ta == np.uint8) + 2 * (tb == np.uint8))
+    a, b = rint(rng, (M, K), ta), rint(rng, (K, N), tb)
+    zl = lambda d: (100, 150) if d == np.uint8 else (-16, 16)
+    az, bz = rint(rng, (M, 1), ta, *zl(ta)), rint(rng, (1, N), tb, *zl(tb))
+    asc, bsc = synth.uniform(rng, (M, 1), 0.002, 0.01), synth.uniform(rng, (1, N), 0.002, 0.01)
+    yz = np.array(128 if ty == np.uint8 else -3, ty)
+    got, ref = run(a, asc, az, b, bsc, bz, 0.05, yz)
+    assert got.dtype == ty
+    assert np.array_equal(got, ref), np.argwhere(got != ref)[:5]
+
+
+def test_decode_rows_scalar_params_fp16_and_saturation():
+    """Decode-like rows with per-tensor parameters and fp16 scales, then unit
+    scales and extreme zero points so that most outputs saturate."""
+    rng = np.random.default_rng(4242)
+    M, K, N = 2, 2048, 2048
+    a, b = rint(rng, (M, K), np.int8), rint(rng, (K, N), np.int8)
+    got, ref = run(a, np.float16(0.004), np.array(3, np.int8), b, np.float16(0.006), np.array(-7, np.int8),
+                   np.float16(0.05), np.array(1, np.int8))
+    assert np.array_equal(got, ref)
+    got, ref = run(a, 1.0, np.array(127, np.int8), b, 1.0, np.array(-128, np.int8), 1.0, np.array(0, np.int8))
+    assert np.array_equal(got, ref)
+    assert (np.abs(got.astype(np.int32)) >= 127).mean() > 0.5
